@@ -1,0 +1,195 @@
+/*
+ * megamoe.h - C ABI of libmegamoe.so, an NVFP4 routed-expert ("MegaMoE") layer for gfx950.
+ *
+ * The layer (nvfp4-megamoe-kernel, CURRENT_BUG.md@2e65594, "Architecture: DeepSeek-V4
+ * MegaMoE" and "Test Plan" Phases 1-2) takes top-k routing over many experts, permutes
+ * tokens by expert, quantizes activations to NVFP4, runs the L1 gate+up grouped GEMM,
+ * applies SiLU(gate)*up, requantizes, runs the L2 down grouped GEMM and combines the
+ * expert outputs with the routing weights.  One layer forward is the sequence
+ *
+ *   moe_route_permute -> nvfp4_quantize_act(x) -> moe_grouped_gemm_l1_silu
+ *   -> nvfp4_quantize_act(h, amax from L1) -> moe_grouped_gemm_l2 -> moe_combine
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is a DEVICE pointer owned by the caller.  The library never
+ *   allocates or frees memory and keeps no state between calls; calls are reentrant.
+ * - Every call only enqueues kernels on `stream` (a hipStream_t; NULL = the null stream).
+ *   No call synchronises the device or copies device memory to the host.
+ * - Argument checks run on the host before any HIP call.  Return values:
+ *     MEGAMOE_OK              success (work enqueued)
+ *     MEGAMOE_ERR_NULL        a required pointer is NULL
+ *     MEGAMOE_ERR_SHAPE       a size is out of range (limits stated per function)
+ *     MEGAMOE_ERR_WORKSPACE   workspace_bytes is smaller than the matching *_workspace_bytes()
+ *     MEGAMOE_ERR_LAUNCH      a kernel launch failed (hipGetLastError after the launch)
+ *     MEGAMOE_ERR_DEVICE      the current device is not gfx950
+ * - Data errors on the device are defined away: a top-k id outside
+ *   [expert_begin, expert_begin + num_experts) is "not local" and is dropped.
+ * - Layouts are row-major.  NVFP4 tensors are three parts:
+ *     codes  uint8 [rows, K/2]  two E2M1 codes per byte, the even element in the LOW nibble;
+ *                               E2M1 = sign.exp(2).mantissa(1), magnitudes {0,.5,1,1.5,2,3,4,6};
+ *     scales uint8 [rows, K/16] one OCP E4M3FN block scale per 16 consecutive K elements;
+ *     gs     float             one FP32 global scale per tensor (per expert and matrix for
+ *                               weights); the real value of element i is
+ *                               e2m1(code_i) * e4m3(scale_block(i)) / gs.
+ * - Expert weights: W13 codes [E, 2I, H/2], scales [E, 2I, H/16], gs [E]; rows 0..I-1 are the
+ *   gate projection and rows I..2I-1 the up projection.  W2 codes [E, H, I/2], scales
+ *   [E, H, I/16], gs [E].  bf16 tensors are passed as raw 16-bit storage.
+ */
+#ifndef MEGAMOE_H
+#define MEGAMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MEGAMOE_OK 0
+#define MEGAMOE_ERR_NULL (-1)
+#define MEGAMOE_ERR_SHAPE (-2)
+#define MEGAMOE_ERR_WORKSPACE (-3)
+#define MEGAMOE_ERR_LAUNCH (-4)
+#define MEGAMOE_ERR_DEVICE (-5)
+
+/* Largest number of local experts one call handles. */
+#define MEGAMOE_MAX_EXPERTS 1024
+
+/* ------------------------------------------------------------------------------------------
+ * Host-side size helpers (no HIP calls; usable without a GPU).
+ * ---------------------------------------------------------------------------------------- */
+
+/* Rows of the permuted activation buffers: T*k + E*(P-1), enough for every local assignment
+ * with each expert's rows padded to a multiple of P.  Returns -1 for invalid sizes. */
+int64_t megamoe_row_capacity(int32_t T, int32_t k, int32_t num_experts, int32_t pad_multiple);
+
+/* int32 entries of the `sched` table written by moe_route_permute for num_experts experts. */
+int64_t megamoe_sched_len(int32_t num_experts);
+
+/* Scratch bytes moe_route_permute needs for T tokens, top-k and num_experts experts. */
+size_t megamoe_route_workspace_bytes(int32_t T, int32_t k, int32_t num_experts);
+
+/* Scratch bytes nvfp4_quantize_act needs for a [rows, cols] tensor. */
+size_t megamoe_quant_workspace_bytes(int64_t rows, int64_t cols);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_route_permute - local filter, per-expert counts, offsets, stable permutation, tile table.
+ *
+ * Defined by CURRENT_BUG.md@2e65594, "Test Plan" Phase 1 (the runner receives topk_ids and
+ * variable token counts per expert, padded to 128 in vLLM) and Phase 2 (48-expert EP share of
+ * 384, zero-token experts, expert_offsets and padded_expert_offsets).
+ *
+ * topk_ids        int32 [T, k]  global expert id of each (token, slot).
+ * expert_begin    first global expert held here; local expert e = id - expert_begin.
+ * num_experts     E, local experts (1..MEGAMOE_MAX_EXPERTS).
+ * pad_multiple    P >= 1: each expert's row block is padded to a multiple of P (zero stays 0).
+ * block_m_override 0 = per-expert tile height chosen from the token count (16 for up to 16
+ *                 tokens, larger tiles above); 16, 32, 64, 128 or 256 forces that height for
+ *                 every expert.  The choice changes speed only; results agree to FP32 rounding.
+ * counts          int32 [E]     local assignments per expert.
+ * expert_offsets  int32 [E+1]   exclusive prefix sum of counts.
+ * padded_offsets  int32 [E+1]   exclusive prefix sum of round_up(counts, P).
+ * row_token       int32 [M_cap] token of each permuted row, -1 for padding and unused rows;
+ *                 M_cap = megamoe_row_capacity(T, k, E, P).  Expert e's rows start at
+ *                 padded_offsets[e] and hold its tokens in ascending token order.
+ * token_rows      int32 [T*k]   permuted row of each (token, slot), -1 if not local.
+ * sched           int32 [megamoe_sched_len(E)]  tile table read by the GEMM entry points.
+ * workspace       >= megamoe_route_workspace_bytes(T, k, E) bytes of scratch.
+ * Limits: 0 <= T, 1 <= k <= 64, T*k < 2^31, P >= 1, M_cap < 2^31.
+ * ---------------------------------------------------------------------------------------- */
+int32_t moe_route_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t expert_begin,
+                          int32_t num_experts, int32_t pad_multiple, int32_t block_m_override,
+                          int32_t* counts, int32_t* expert_offsets, int32_t* padded_offsets,
+                          int32_t* row_token, int32_t* token_rows, int32_t* sched,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * nvfp4_quantize_act - NVFP4 quantization with a global scale derived from amax.
+ *
+ * The FP4 quantizer multiplies the input by a global scale before forming E4M3 block scales
+ * (CURRENT_BUG.md@2fc81cc, "Root Cause" and "Key evidence": a global scale taken from a
+ * checkpoint, 1/input_scale = 3977.6, overflows E4M3 on activations with amax 2-8).  Here
+ * gs = fl32(2688 / amax) (2688 = 448 * 6, so no block scale can exceed E4M3's 448; gs = 1
+ * when amax = 0).  Per 16-element block: scale = E4M3 round-to-nearest-even of the exact
+ * value block_amax * gs / 6 (saturating at 448); each element's code is the E2M1 point
+ * nearest to the exact value x * gs / scale, ties to the even code, sign copied from x.
+ * Results are bit-exact with that definition.
+ *
+ * x_bf16       bf16 [rows, cols]; finite values.
+ * rows, cols   rows >= 0, cols > 0 and a multiple of 32.
+ * row_valid    nullable int32 [rows]: rows with row_valid[r] < 0 are excluded from amax and
+ *              get zero codes and scales (pass row_token to quantize permuted rows).
+ * amax_in      nullable float [1]: the amax of the valid rows, when already known (L1 writes
+ *              it for h); NULL = computed here.
+ * codes        uint8 [rows, cols/2];  scales uint8 [rows, cols/16];  global_scale float [1].
+ * workspace    >= megamoe_quant_workspace_bytes(rows, cols) bytes (may be NULL if that is 0).
+ * ---------------------------------------------------------------------------------------- */
+int32_t nvfp4_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, const int32_t* row_valid,
+                           const float* amax_in, uint8_t* codes, uint8_t* scales, float* global_scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_grouped_gemm_l1_silu - L1 gate+up grouped GEMM over experts with SiLU(gate)*up.
+ *
+ * CURRENT_BUG.md@2e65594, "Architecture: DeepSeek-V4 MegaMoE" (persistent grouped GEMM, tile
+ * height 16-192 from the tokens per expert, per-expert shapes) and "Test Plan" Phase 1
+ * (L1 gate+up GEMM, then SiLU).  For each expert e with counts[e] > 0 and each of its rows r
+ * (padded_offsets[e] <= r < padded_offsets[e] + counts[e]):
+ *   acc[n] = sum_k dec(x[row_token[r], k]) * dec(W13[e, n, k]),  n in [0, 2I)
+ *   h[r, i] = bf16( SiLU(acc[i] / (gs_x * gs13[e])) * acc[I+i] / (gs_x * gs13[e]) )
+ * with exact E2M1*E4M3 decode, FP16 MFMA products and FP32 accumulation.  Rows of h that hold
+ * no assignment are not written.  h_amax receives max |h| over the written rows (the call
+ * resets it first).  Experts with no tokens are never read.
+ *
+ * x_codes/x_scales/x_gs   NVFP4 x per token: [T, H/2], [T, H/16], [1].
+ * row_token, padded_offsets, counts, sched   as written by moe_route_permute.
+ * w13_codes/w13_scales/w13_gs   [E, 2I, H/2], [E, 2I, H/16], [E].
+ * E, H, I      E as given to moe_route_permute; H, I multiples of 64 (I >= 64).
+ * M_cap        rows of h: megamoe_row_capacity(T, k, E, P).
+ * h_bf16       bf16 [M_cap, I].   h_amax float [1].
+ * ---------------------------------------------------------------------------------------- */
+int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                 const int32_t* row_token, const int32_t* padded_offsets,
+                                 const int32_t* counts, const int32_t* sched,
+                                 const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
+                                 int32_t E, int32_t H, int32_t I, int64_t M_cap,
+                                 void* h_bf16, float* h_amax, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_grouped_gemm_l2 - L2 down grouped GEMM over experts.
+ *
+ * CURRENT_BUG.md@2e65594, "Test Plan" Phase 1 (L2 GEMM after SiLU) and "What's Been Verified"
+ * (NVFP4 MoE, L1 gate+up and L2 down).  For each expert e with counts[e] > 0 and each row r:
+ *   y[r, n] = bf16( sum_k dec(h[r, k]) * dec(W2[e, n, k]) / (gs_h * gs2[e]) ),  n in [0, H)
+ * Rows of y that hold no assignment are not written.
+ *
+ * h_codes/h_scales/h_gs   NVFP4 h [M_cap, I/2], [M_cap, I/16], [1] (from nvfp4_quantize_act).
+ * padded_offsets, counts, sched   as written by moe_route_permute.
+ * w2_codes/w2_scales/w2_gs   [E, H, I/2], [E, H, I/16], [E].
+ * y_bf16       bf16 [M_cap, H].
+ * ---------------------------------------------------------------------------------------- */
+int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs,
+                            const int32_t* padded_offsets, const int32_t* counts, const int32_t* sched,
+                            const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
+                            int32_t E, int32_t H, int32_t I, int64_t M_cap, void* y_bf16, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_combine - routing-weighted combine of the expert outputs back into token order.
+ *
+ * The routing weight of each (token, expert) is applied exactly once, here:
+ *   out[t, :] = bf16( sum over j = 0..k-1 ascending, token_rows[t*k+j] >= 0, of
+ *                     topk_weights[t, j] * y[token_rows[t*k+j], :] )    (FP32 accumulation)
+ * Tokens with no local assignment get +0.
+ *
+ * y_bf16 [M_cap, H] bf16;  token_rows int32 [T*k];  topk_weights float [T, k];
+ * out_bf16 bf16 [T, H];  T >= 0, 1 <= k <= 64, H a multiple of 8.
+ * ---------------------------------------------------------------------------------------- */
+int32_t moe_combine(const void* y_bf16, const int32_t* token_rows, const float* topk_weights,
+                    int32_t T, int32_t k, int32_t H, void* out_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEGAMOE_H */
