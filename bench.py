@@ -1,0 +1,257 @@
+"""Benchmark of the NVFP4 routed-expert layer on one MI355X.
+
+One step = one layer forward through the C ABI (route/permute, quantize x, L1 gate+up + SiLU,
+quantize h, L2 down, combine) over one batch of synthetic input already resident in HBM.
+
+Headline (``value``): TFLOP/s of the 8192-token prefill with Zipf-skewed routing over 384
+experts (hidden 7168, intermediate 2048, top-6).  Useful FLOPs are 6*H*I per (token, local
+expert) assignment.  The same JSON line carries the decode workload (the 48-expert
+expert-parallel share of 384 experts at T = 1, 4, 8, with 4 rotated weight copies so weights
+come from HBM, not from the 256 MB last-level cache), reported as weight GB/s, where weight
+bytes are the NVFP4 bytes of the experts that received at least one token.
+
+``roofline`` is for the dominant stage (the L1 gate+up grouped GEMM entry point): algorithmic
+FLOPs (prefill, against the 2.5 PFLOP/s dense fp16 MFMA peak) or algorithmic weight bytes
+(decode, against 8 TB/s) per call, divided by that call's average duration measured with HIP
+events on the stream it runs on.  ``cpu_baseline`` times the CPU oracle (float64 NumPy) on a
+bounded sample of the prefill workload: the layer restricted to its most-loaded expert.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer TFLOP/s + weight GB/s (% roofline) at decode and 8192-token prefill"
+PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+STAGES = ("route", "quant_x", "l1", "quant_h", "l2", "combine")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def build_weights(wl, active, copies, dev):
+    """NVFP4 weights for the local experts, quantized on the GPU; experts with no token stay unset."""
+    import torch
+    from nvfp4_block_scaled_top_amd import layer, synth
+
+    W = layer.MoEWeights.empty(wl.num_experts, wl.hidden, wl.intermediate, device=dev)
+    for e in active:
+        w13, w2 = synth.expert_weights(wl, wl.expert_begin + e, device=dev)
+        layer.quantize_expert_into(W, e, w13, w2)
+        del w13, w2
+    torch.cuda.synchronize()
+    return [W] + [W.clone() for _ in range(copies - 1)]
+
+
+def time_workload(wl, T, steps, warmup, copies, use_graph):
+    import torch
+    from nvfp4_block_scaled_top_amd import layer, synth
+
+    dev = "cuda:0"
+    ids, wts = synth.router(wl, T)
+    counts = synth.routing_stats(ids, wl)
+    active = [int(e) for e in np.nonzero(counts)[0]]
+    x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).to(dev)
+    ids_d, wts_d = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
+    Ws = build_weights(wl, active, copies, dev)
+    L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
+                       expert_begin=wl.expert_begin, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        L.forward(x, ids_d, wts_d, Ws[i % copies])
+
+    for i in range(max(warmup, 1)):
+        step(i)
+    torch.cuda.synchronize()
+    graphs = None
+    if use_graph:
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+
+    # Whole-step timing: exactly `steps` steps between two synchronizations.
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        if graphs is not None:
+            graphs[i % copies].replay()
+        else:
+            step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / steps
+
+    # Per-stage durations: a short GPU spin ahead of each stage keeps the launch latency out of
+    # the event pair that brackets it.
+    stage_fns = {
+        "route": lambda i: L.route(ids_d),
+        "quant_x": lambda i: L.quantize_x(x),
+        "l1": lambda i: L.l1(Ws[i % copies]),
+        "quant_h": lambda i: L.quantize_h(),
+        "l2": lambda i: L.l2(Ws[i % copies]),
+        "combine": lambda i: L.combine(wts_d),
+    }
+    reps = max(3, min(steps, 20))
+    stage_ms = {}
+    for name in STAGES:
+        tot = 0.0
+        for i in range(reps):
+            # restore the inputs each stage expects (they are the outputs of the previous stages)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(200_000)
+            a.record(stream)
+            stage_fns[name](i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+        stage_ms[name] = tot / reps
+    assign = int(counts.sum())
+    flops = 6.0 * wl.hidden * wl.intermediate * assign
+    wbytes = len(active) * Ws[0].nbytes_expert()
+    w13_bytes = len(active) * (Ws[0].w13_codes[0].numel() + Ws[0].w13_scales[0].numel() + 4)
+    del Ws, graphs
+    torch.cuda.synchronize()
+    return dict(T=T, ms_per_step=ms_per_step, wall_s=wall, stage_ms=stage_ms, assignments=assign,
+                active_experts=len(active), flops=flops, weight_bytes=wbytes, w13_bytes=w13_bytes,
+                l1_flops=4.0 * wl.hidden * wl.intermediate * assign)
+
+
+def cpu_baseline(wl, T):
+    """The CPU oracle on a bounded sample: the prefill layer restricted to its most-loaded expert."""
+    import torch
+    from nvfp4_block_scaled_top_amd import synth
+    from oracle import nvfp4_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    ids, wts = synth.router(wl, T)
+    counts = synth.routing_stats(ids, wl)
+    e = int(np.argmax(counts))
+    x = O.bf16_from_bits(synth.activations(wl, T))
+    w13, w2 = synth.expert_weights(wl, wl.expert_begin + e, device="cpu")
+    q13 = O.quantize_nvfp4(O.bf16_from_bits(w13.view(torch.int16).numpy().view(np.uint16)))
+    q2 = O.quantize_nvfp4(O.bf16_from_bits(w2.view(torch.int16).numpy().view(np.uint16)))
+    t0 = time.perf_counter()
+    O.moe_layer(x, ids, wts, wl.expert_begin + e, 1, wl.pad_multiple, q13[0][None], q13[1][None],
+                np.array([q13[2]], np.float32), q2[0][None], q2[1][None], np.array([q2[2]], np.float32))
+    dt = time.perf_counter() - t0
+    flops = 6.0 * wl.hidden * wl.intermediate * int(counts[e])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 NumPy oracle, whole layer (route, quantize x, L1+SiLU, requantize, L2, combine) "
+                      f"for T={T} restricted to its most-loaded expert ({int(counts[e])} tokens), {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="prefill only, no CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from nvfp4_block_scaled_top_amd import megamoe, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    megamoe.lib()
+    torch.cuda.set_device(0)
+
+    pre_wl = synth.WORKLOADS[3]
+    T = pre_wl.tokens[0]
+    log(f"[bench] prefill {pre_wl.name} T={T}")
+    pre = time_workload(pre_wl, T, args.steps, args.warmup, copies=1, use_graph=not args.no_graph)
+    tflops = pre["flops"] / (pre["ms_per_step"] * 1e-3) / 1e12
+    l1_tflops = pre["l1_flops"] / (pre["stage_ms"]["l1"] * 1e-3) / 1e12
+    log(f"[bench] prefill {pre['ms_per_step']:.3f} ms/step, {tflops:.1f} TFLOP/s; stages {pre['stage_ms']}")
+
+    decode = {}
+    if not args.quick:
+        dec_wl = synth.WORKLOADS[1]
+        for Td in dec_wl.tokens:
+            log(f"[bench] decode {dec_wl.name} T={Td}")
+            d = time_workload(dec_wl, Td, args.decode_steps, args.warmup, copies=4, use_graph=not args.no_graph)
+            gbs = d["weight_bytes"] / (d["ms_per_step"] * 1e-3) / 1e9
+            l1_gbs = d["w13_bytes"] / (d["stage_ms"]["l1"] * 1e-3) / 1e9
+            decode[f"T{Td}"] = {
+                "ms_per_step": round(d["ms_per_step"], 5), "weight_GBps": round(gbs, 1),
+                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "TFLOPs": round(d["flops"] / (d["ms_per_step"] * 1e-3) / 1e12, 3),
+                "active_experts": d["active_experts"], "assignments": d["assignments"],
+                "weight_bytes": d["weight_bytes"], "stage_ms": {k: round(v, 5) for k, v in d["stage_ms"].items()},
+                "roofline": {"bound": "hbm", "achieved": round(l1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(l1_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                             "kernel": "moe_grouped_gemm_l1_silu"},
+            }
+            log(f"[bench] decode T={Td}: {d['ms_per_step'] * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.quick:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(pre_wl, T)
+        cpu.pop("seconds", None)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{pre_wl.name}: 384 experts, top-6, hidden 7168, intermediate 2048, T={T}, "
+                               "Zipf(1.2) expert bias, NVFP4 weights and activations, seed 0",
+                   "global_batch": T, "experts": 384, "top_k": 6, "hidden": 7168, "intermediate": 2048,
+                   "active_experts": pre["active_experts"], "assignments": pre["assignments"]},
+        "weight_GBps": round(pre["weight_bytes"] / (pre["ms_per_step"] * 1e-3) / 1e9, 1),
+        "mfma_frac": round(tflops / PEAK_FP16_TFLOPS, 4),
+        "stage_ms": {k: round(v, 4) for k, v in pre["stage_ms"].items()},
+        "roofline": {"bound": "mfma", "achieved": round(l1_tflops, 1), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(l1_tflops / PEAK_FP16_TFLOPS, 4), "traffic": None,
+                     "kernel": "moe_grouped_gemm_l1_silu"},
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+// C ABI of libmegamoe.so: host-side argument checks, then kernel launches on the caller's stream.
+// Every check runs before the first HIP call, so invalid arguments are reported without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/megamoe.h"
+#include "internal.h"
+
+using namespace megamoe;
+
+namespace {
+
+// Per-device cache of "is this gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int32_t check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MEGAMOE_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return MEGAMOE_OK;
+    if (c == 2) return MEGAMOE_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MEGAMOE_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? MEGAMOE_OK : MEGAMOE_ERR_DEVICE;
+}
+
+int32_t launch_status(hipError_t e) { return e == hipSuccess ? MEGAMOE_OK : MEGAMOE_ERR_LAUNCH; }
+
+bool gemm_shape_ok(int32_t E, int32_t H, int32_t I, int64_t M_cap) {
+  return E >= 1 && E <= MEGAMOE_MAX_EXPERTS && H >= 128 && I >= 128 && H % 128 == 0 && I % 128 == 0 &&
+         M_cap >= 0 && M_cap < (int64_t)1 << 31;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t megamoe_row_capacity(int32_t T, int32_t k, int32_t num_experts, int32_t pad_multiple) {
+  if (T < 0 || k < 1 || num_experts < 1 || pad_multiple < 1) return -1;
+  return (int64_t)T * k + (int64_t)num_experts * (pad_multiple - 1);
+}
+
+int64_t megamoe_sched_len(int32_t num_experts) {
+  if (num_experts < 1 || num_experts > MEGAMOE_MAX_EXPERTS) return -1;
+  return sched_len(num_experts);
+}
+
+size_t megamoe_route_workspace_bytes(int32_t T, int32_t k, int32_t num_experts) {
+  if (T < 0 || k < 1 || num_experts < 1) return 0;
+  const int64_t n = (int64_t)T * k;
+  const int64_t nchunks = (n + kRouteChunk - 1) / kRouteChunk;
+  return (size_t)(nchunks * num_experts * (int64_t)sizeof(int32_t));
+}
+
+size_t megamoe_quant_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0) return 0;
+  return (size_t)quant_amax_parts(rows, cols) * sizeof(float);
+}
+
+int32_t moe_route_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t expert_begin, int32_t num_experts,
+                          int32_t pad_multiple, int32_t block_m_override, int32_t* counts, int32_t* expert_offsets,
+                          int32_t* padded_offsets, int32_t* row_token, int32_t* token_rows, int32_t* sched,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 0 || k < 1 || k > 64 || num_experts < 1 || num_experts > MEGAMOE_MAX_EXPERTS || pad_multiple < 1 ||
+      expert_begin < 0)
+    return MEGAMOE_ERR_SHAPE;
+  if (block_m_override != 0 && block_m_override != kBlockMSmall && block_m_override != kBlockMLarge)
+    return MEGAMOE_ERR_SHAPE;
+  const int64_t n = (int64_t)T * k;
+  const int64_t M_cap = megamoe_row_capacity(T, k, num_experts, pad_multiple);
+  if (n >= ((int64_t)1 << 31) || M_cap >= ((int64_t)1 << 31)) return MEGAMOE_ERR_SHAPE;
+  if (!counts || !expert_offsets || !padded_offsets || !sched) return MEGAMOE_ERR_NULL;
+  if (M_cap > 0 && !row_token) return MEGAMOE_ERR_NULL;
+  if (n > 0 && (!topk_ids || !token_rows)) return MEGAMOE_ERR_NULL;
+  const size_t need = megamoe_route_workspace_bytes(T, k, num_experts);
+  if (workspace_bytes < need) return MEGAMOE_ERR_WORKSPACE;
+  if (need > 0 && !workspace) return MEGAMOE_ERR_NULL;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  return launch_status(launch_route(topk_ids, T, k, expert_begin, num_experts, pad_multiple, block_m_override, counts,
+                                    expert_offsets, padded_offsets, row_token, M_cap, token_rows, sched,
+                                    static_cast<int32_t*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+int32_t nvfp4_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, const int32_t* row_valid,
+                           const float* amax_in, uint8_t* codes, uint8_t* scales, float* global_scale, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 != 0 || rows > ((int64_t)1 << 40) / cols) return MEGAMOE_ERR_SHAPE;
+  if (!global_scale) return MEGAMOE_ERR_NULL;
+  if (rows > 0 && (!x_bf16 || !codes || !scales)) return MEGAMOE_ERR_NULL;
+  const size_t need = amax_in ? 0 : megamoe_quant_workspace_bytes(rows, cols);
+  if (workspace_bytes < need) return MEGAMOE_ERR_WORKSPACE;
+  if (need > 0 && !workspace) return MEGAMOE_ERR_NULL;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  return launch_status(launch_quant(static_cast<const uint16_t*>(x_bf16), rows, cols, row_valid, amax_in, codes, scales,
+                                    global_scale, static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                 const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
+                                 const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                 const float* w13_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap, void* h_bf16,
+                                 float* h_amax, void* stream) {
+  if (!gemm_shape_ok(E, H, I, M_cap)) return MEGAMOE_ERR_SHAPE;
+  if (!x_codes || !x_scales || !x_gs || !row_token || !padded_offsets || !counts || !sched || !w13_codes ||
+      !w13_scales || !w13_gs || !h_bf16 || !h_amax)
+    return MEGAMOE_ERR_NULL;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  GemmArgs a{x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
+             E, H, I, h_bf16, h_amax};
+  return launch_status(launch_gemm_l1(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs,
+                            const int32_t* padded_offsets, const int32_t* counts, const int32_t* sched,
+                            const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs, int32_t E, int32_t H,
+                            int32_t I, int64_t M_cap, void* y_bf16, void* stream) {
+  if (!gemm_shape_ok(E, H, I, M_cap)) return MEGAMOE_ERR_SHAPE;
+  if (!h_codes || !h_scales || !h_gs || !padded_offsets || !counts || !sched || !w2_codes || !w2_scales || !w2_gs ||
+      !y_bf16)
+    return MEGAMOE_ERR_NULL;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  GemmArgs a{h_codes, h_scales, h_gs, nullptr, padded_offsets, counts, sched, w2_codes, w2_scales, w2_gs,
+             E, I, H, y_bf16, nullptr};
+  return launch_status(launch_gemm_l2(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_combine(const void* y_bf16, const int32_t* token_rows, const float* topk_weights, int32_t T, int32_t k,
+                    int32_t H, void* out_bf16, void* stream) {
+  if (T < 0 || k < 1 || k > 64 || H < 8 || H % 8 != 0) return MEGAMOE_ERR_SHAPE;
+  if (T > 0 && (!y_bf16 || !token_rows || !topk_weights || !out_bf16)) return MEGAMOE_ERR_NULL;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  return launch_status(launch_combine(static_cast<const uint16_t*>(y_bf16), token_rows, topk_weights, T, k, H,
+                                      static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

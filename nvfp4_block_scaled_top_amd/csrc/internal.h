@@ -1,0 +1,71 @@
+// Host-side declarations shared between the C-ABI layer (api.cpp) and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/megamoe.h"
+
+namespace megamoe {
+
+constexpr int kMaxExperts = MEGAMOE_MAX_EXPERTS;
+
+// ---- routing ---------------------------------------------------------------------------------
+constexpr int kRouteChunk = 1024;  // assignments per routing workgroup (one per thread)
+
+// Layout of the int32 tile table written by the routing step and read by the GEMMs:
+//   [0] E  [1] total small-class m-tiles  [2] total large-class m-tiles  [3] 0
+//   [4, 4+E)           block_m of each expert (0 when it has no tokens)
+//   [4+E, 5+2E)        exclusive prefix of small-class m-tiles per expert
+//   [5+2E, 6+3E)       exclusive prefix of large-class m-tiles per expert
+constexpr int kSchedHeader = 4;
+inline int64_t sched_len(int32_t E) { return kSchedHeader + 3 * (int64_t)E + 2; }
+__host__ __device__ inline int sched_block_m(int E) { (void)E; return kSchedHeader; }
+__host__ __device__ inline int sched_pref_small(int E) { return kSchedHeader + E; }
+__host__ __device__ inline int sched_pref_large(int E) { return kSchedHeader + 2 * E + 1; }
+
+// Tile heights.  Small class: one 16-row MFMA block, weights streamed straight to registers with
+// the reduction dimension split across the waves of a workgroup.  Large class: LDS-tiled.
+constexpr int kBlockMSmall = 16;
+constexpr int kBlockMLarge = 128;
+// Experts with at most this many tokens use the small class when block_m is chosen per expert.
+constexpr int kSmallClassMaxTokens = 16;
+
+hipError_t launch_route(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e0, int32_t E, int32_t P,
+                        int32_t block_m_override, int32_t* counts, int32_t* eoff, int32_t* poff,
+                        int32_t* row_token, int64_t M_cap, int32_t* token_rows, int32_t* sched,
+                        int32_t* ws, hipStream_t stream);
+
+// ---- quantizer -------------------------------------------------------------------------------
+int quant_amax_parts(int64_t rows, int64_t cols);
+hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* row_valid,
+                        const float* amax_in, uint8_t* codes, uint8_t* scales, float* gs, float* ws,
+                        hipStream_t stream);
+
+// ---- grouped GEMMs ---------------------------------------------------------------------------
+struct GemmArgs {
+  // A operand: NVFP4 activations.  For L1, rows are gathered through row_token from a [T, K]
+  // tensor; for L2 the permuted row index addresses the [M_cap, K] tensor directly.
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_gs;
+  const int32_t* row_token;  // L1 only (NULL for L2)
+  const int32_t* padded_offsets;
+  const int32_t* counts;
+  const int32_t* sched;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const float* w_gs;
+  int32_t E, K, N;   // N = output columns: I for L1 (weights have 2I rows), H for L2
+  void* out;         // bf16 [M_cap, N]
+  float* amax_out;   // L1: max |h| (uint-ordered atomic max); NULL for L2
+};
+hipError_t launch_gemm_l1(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_l2(const GemmArgs& a, hipStream_t stream);
+
+// ---- combine ---------------------------------------------------------------------------------
+hipError_t launch_combine(const uint16_t* y, const int32_t* token_rows, const float* w, int32_t T,
+                          int32_t k, int32_t H, uint16_t* out, hipStream_t stream);
+
+}  // namespace megamoe

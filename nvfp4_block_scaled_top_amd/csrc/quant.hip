@@ -1,0 +1,178 @@
+// NVFP4 quantization of activations with a global scale derived from amax.
+//
+// The FP4 quantizer multiplies the input by a global scale before it forms the E4M3 block
+// scales; a global scale taken from a checkpoint (1/input_scale = 3977.6) overflows E4M3 for
+// activations with amax 2-8 (nvfp4-megamoe-kernel CURRENT_BUG.md@2fc81cc, "Root Cause" and
+// "Key evidence").  Here gs = fl32(2688 / amax) with 2688 = 448 (E4M3 max) * 6 (E2M1 max), so
+// no block scale can exceed 448.
+//
+// Exactness.  Results are bit-exact with the real-number definition:
+//  * block scale = E4M3 round-to-nearest-even of block_amax * gs / 6.  block_amax * gs is exact
+//    in double (8 + 24 significant bits); the quotient by 6 is rounded once in double, and it
+//    cannot land on or cross an E4M3 rounding midpoint unless the exact value is that midpoint
+//    (a non-zero gap |p - 6*mid| is at least 2^-33 relative, far above double's 2^-53), so
+//    rounding the double to the E4M3 grid with ties-to-even is exact;
+//  * element code = nearest E2M1 point of x * gs / s: compare x * gs with each midpoint m * s
+//    (exact in fp32: <= 7 significant bits).  fmaf(|x|, gs, -m*s) rounds the exact difference
+//    once, which never changes its sign, so each comparison is exact; ties go to the even code.
+//
+// Two kernels: an amax pass writing per-workgroup partial maxima (skipped when the caller passes
+// amax_in), then the quantization pass, whose every workgroup reduces the partials itself.
+#include "device_common.h"
+#include "internal.h"
+
+namespace megamoe {
+
+constexpr int kQuantThreads = 256;
+constexpr int kQuantMaxParts = 1024;
+
+int quant_amax_parts(int64_t rows, int64_t cols) {
+  const int64_t vecs = rows * cols / 8;
+  int64_t b = (vecs + kQuantThreads * 4 - 1) / (kQuantThreads * 4);
+  if (b < 1) b = 1;
+  if (b > kQuantMaxParts) b = kQuantMaxParts;
+  return (int)b;
+}
+
+__device__ __forceinline__ uint32_t bf16_abs_max8(u32x4 v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = v[j] & 0x7FFFu, hi = (v[j] >> 16) & 0x7FFFu;
+    m = m > lo ? m : lo;
+    m = m > hi ? m : hi;
+  }
+  return m;
+}
+
+// Block-level max of a non-negative uint (256 threads).
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+  v = wave_max_u32(v);
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == 0) red[w] = v;
+  __syncthreads();
+  uint32_t r = red[0];
+  for (int j = 1; j < kQuantThreads / kWave; ++j) r = r > red[j] ? r : red[j];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kQuantThreads) void quant_amax_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                   int64_t cols, const int32_t* __restrict__ row_valid,
+                                                                   float* __restrict__ parts) {
+  __shared__ uint32_t red[kQuantThreads / kWave];
+  const int64_t nvec = rows * cols / 8;
+  uint32_t m = 0;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * blockDim.x) {
+    if (row_valid != nullptr && row_valid[(v * 8) / cols] < 0) continue;
+    const u32x4 d = *reinterpret_cast<const u32x4*>(x + v * 8);
+    const uint32_t t = bf16_abs_max8(d);
+    m = m > t ? m : t;
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) parts[blockIdx.x] = bf16_bits_to_f32(m);
+}
+
+// E4M3FN code of the non-negative double q, round to nearest even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_code_rne(double q) {
+  if (q >= 464.0) return 0x7Eu;
+  if (q < 0.015625) return (uint32_t)rint(q * 512.0);  // subnormal grid m * 2^-9 (m = 8 is 2^-6)
+  int ex;
+  (void)frexp(q, &ex);  // q in [2^(ex-1), 2^ex)
+  const int E = ex - 1;
+  double mant = rint(ldexp(q, 3 - E));  // in [8, 16]
+  int Eq = E;
+  if (mant >= 16.0) {
+    mant = 8.0;
+    Eq += 1;
+  }
+  const uint32_t code = ((uint32_t)(Eq + 7) << 3) | ((uint32_t)mant - 8u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
+}
+
+// 4-bit code of one element: sign of x, magnitude = nearest E2M1 index with ties to even.
+__device__ __forceinline__ uint32_t e2m1_code(uint32_t xbits, float gs, const float t[7], bool zero_scale) {
+  const float a = bf16_bits_to_f32(xbits & 0x7FFFu);
+  uint32_t mag = 0;
+  if (!zero_scale) {
+    mag = (fmaf(a, gs, -t[0]) > 0.0f) + (fmaf(a, gs, -t[1]) >= 0.0f) + (fmaf(a, gs, -t[2]) > 0.0f) +
+          (fmaf(a, gs, -t[3]) >= 0.0f) + (fmaf(a, gs, -t[4]) > 0.0f) + (fmaf(a, gs, -t[5]) >= 0.0f) +
+          (fmaf(a, gs, -t[6]) > 0.0f);
+  }
+  return ((xbits >> 12) & 8u) | mag;
+}
+
+__global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                              const int32_t* __restrict__ row_valid,
+                                                              const float* __restrict__ amax_src, int nparts,
+                                                              uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                              float* __restrict__ gs_out) {
+  __shared__ uint32_t red[kQuantThreads / kWave];
+  uint32_t am = 0;
+  for (int j = threadIdx.x; j < nparts; j += blockDim.x) {
+    const uint32_t b = __float_as_uint(amax_src[j]);  // non-negative: uint order is float order
+    am = am > b ? am : b;
+  }
+  am = block_max_u32(am, red);
+  const float amax = __uint_as_float(am);
+  const float gs = amax > 0.0f ? 2688.0f / amax : 1.0f;  // IEEE division (correctly rounded)
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
+
+  const int64_t bpr = cols / 16;
+  const int64_t nblk = rows * bpr;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * blockDim.x) {
+    if (row_valid != nullptr && row_valid[b / bpr] < 0) {
+      *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{0u, 0u};
+      scales[b] = 0;
+      continue;
+    }
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(x + b * 16);
+    const u32x4 v1 = *reinterpret_cast<const u32x4*>(x + b * 16 + 8);
+    uint32_t bmax = bf16_abs_max8(v0);
+    const uint32_t bm1 = bf16_abs_max8(v1);
+    bmax = bmax > bm1 ? bmax : bm1;
+    const double q = ((double)bf16_bits_to_f32(bmax) * (double)gs) / 6.0;
+    const uint32_t sc = e4m3_code_rne(q);
+    const float s = e4m3_value(sc);
+    const float t[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
+    const bool zs = sc == 0;
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = j < 4 ? v0[j] : v1[j - 4];
+      const uint32_t c0 = e2m1_code(w & 0xFFFFu, gs, t, zs);
+      const uint32_t c1 = e2m1_code(w >> 16, gs, t, zs);
+      out[j >> 2] |= (c0 | (c1 << 4)) << (8 * (j & 3));
+    }
+    *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{out[0], out[1]};
+    scales[b] = (uint8_t)sc;
+  }
+}
+
+hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* row_valid,
+                        const float* amax_in, uint8_t* codes, uint8_t* scales, float* gs, float* ws,
+                        hipStream_t stream) {
+  const float* amax_src = amax_in;
+  int nparts = 1;
+  if (amax_in == nullptr) {
+    nparts = quant_amax_parts(rows, cols);
+    hipLaunchKernelGGL(quant_amax_kernel, dim3(nparts), dim3(kQuantThreads), 0, stream, x, rows, cols, row_valid, ws);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    amax_src = ws;
+  }
+  const int64_t nblk = rows * (cols / 16);
+  int64_t grid = (nblk + kQuantThreads - 1) / kQuantThreads;
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(quant_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream, x, rows, cols, row_valid,
+                     amax_src, nparts, codes, scales, gs);
+  return hipGetLastError();
+}
+
+}  // namespace megamoe

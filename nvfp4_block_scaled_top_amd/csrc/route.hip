@@ -1,0 +1,168 @@
+// Routing step: local filter, per-expert counts, offsets, stable permutation and the tile table.
+//
+// The runner receives top-k ids and variable token counts per expert, with each expert's rows
+// padded to 128 (nvfp4-megamoe-kernel CURRENT_BUG.md@2e65594, "Test Plan" Phase 1), and the
+// grouped GEMM needs expert_offsets / padded_expert_offsets and must skip zero-token experts
+// ("Test Plan" Phase 2).  The per-expert tile height follows the tokens per expert, small at
+// decode and large at prefill ("Key References").
+//
+// Three kernels, no atomics on global memory, so the permutation is deterministic:
+//   1. count:   one workgroup per 1024 assignments builds that chunk's expert histogram (LDS
+//               atomics; counts do not depend on order) and resets row_token to -1;
+//   2. scan:    one workgroup turns the per-chunk histograms into per-chunk bases (a column
+//               prefix over chunks), writes counts and both offset arrays, and the tile table;
+//   3. scatter: each chunk ranks its assignments among equal experts with wave ballots (a
+//               lane's rank = earlier lanes with the same expert) plus the counts of earlier
+//               waves, so rows inside an expert follow ascending (token, slot) order.
+#include "device_common.h"
+#include "internal.h"
+
+namespace megamoe {
+
+__global__ __launch_bounds__(kRouteChunk) void route_count_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                                  int32_t e0, int32_t E, int32_t nchunks,
+                                                                  int32_t* __restrict__ ws,
+                                                                  int32_t* __restrict__ row_token, int64_t M_cap) {
+  extern __shared__ int32_t cnt[];  // [E]
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < M_cap;
+       r += (int64_t)gridDim.x * blockDim.x)
+    row_token[r] = -1;
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * kRouteChunk + threadIdx.x;
+  if ((int)blockIdx.x < nchunks && i < n) {
+    const int64_t e = (int64_t)ids[i] - e0;
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if ((int)blockIdx.x < nchunks)
+    for (int e = threadIdx.x; e < E; e += blockDim.x) ws[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Inclusive scan of one int per thread over a 1024-thread block (Hillis-Steele in LDS).
+__device__ __forceinline__ int block_incl_scan(int v, int* buf) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int o = 1; o < (int)blockDim.x; o <<= 1) {
+    const int add = t >= o ? buf[t - o] : 0;
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  const int r = buf[t];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ ws, int32_t nchunks, int32_t E,
+                                                          int32_t P, int32_t bm_override,
+                                                          int32_t* __restrict__ counts, int32_t* __restrict__ eoff,
+                                                          int32_t* __restrict__ poff, int32_t* __restrict__ sched) {
+  __shared__ int buf[1024];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = ws[(int64_t)c * E + e];
+      ws[(int64_t)c * E + e] = total;
+      total += v;
+    }
+    counts[e] = total;
+  }
+  int bm = 0, small_tiles = 0, large_tiles = 0;
+  int padded = 0;
+  if (e < E && total > 0) {
+    const bool small = bm_override ? (bm_override == kBlockMSmall) : (total <= kSmallClassMaxTokens);
+    bm = small ? kBlockMSmall : kBlockMLarge;
+    const int tiles = (total + bm - 1) / bm;
+    if (small) small_tiles = tiles; else large_tiles = tiles;
+    padded = (int)(((int64_t)total + P - 1) / P * P);
+  }
+  const int inc_cnt = block_incl_scan(total, buf);
+  const int inc_pad = block_incl_scan(padded, buf);
+  const int inc_small = block_incl_scan(small_tiles, buf);
+  const int inc_large = block_incl_scan(large_tiles, buf);
+  if (e < E) {
+    eoff[e + 1] = inc_cnt;
+    poff[e + 1] = inc_pad;
+    sched[sched_block_m(E) + e] = bm;
+    sched[sched_pref_small(E) + e + 1] = inc_small;
+    sched[sched_pref_large(E) + e + 1] = inc_large;
+  }
+  if (e == E - 1) {
+    sched[1] = inc_small;
+    sched[2] = inc_large;
+  }
+  if (e == 0) {
+    eoff[0] = 0;
+    poff[0] = 0;
+    sched[0] = E;
+    sched[3] = 0;
+    sched[sched_pref_small(E)] = 0;
+    sched[sched_pref_large(E)] = 0;
+  }
+}
+
+__global__ __launch_bounds__(kRouteChunk) void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                                    int32_t k, int32_t e0, int32_t E,
+                                                                    const int32_t* __restrict__ ws,
+                                                                    const int32_t* __restrict__ poff,
+                                                                    int32_t* __restrict__ row_token,
+                                                                    int32_t* __restrict__ token_rows) {
+  constexpr int kWaves = kRouteChunk / kWave;
+  extern __shared__ int32_t wcnt[];  // [kWaves][E]
+  for (int j = threadIdx.x; j < kWaves * E; j += blockDim.x) wcnt[j] = 0;
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * kRouteChunk + threadIdx.x;
+  int e = E;  // sentinel: not local (or past the end)
+  if (i < n) {
+    const int64_t v = (int64_t)ids[i] - e0;
+    if (v >= 0 && v < E) e = (int)v;
+  }
+  // Lanes holding the same expert: intersect ballots over the bits of e (values 0..E).
+  uint64_t same = __ballot(1);
+  for (int b = 0; (1 << b) <= E; ++b) {
+    const int bit = (e >> b) & 1;
+    const uint64_t m1 = __ballot(bit);
+    same &= bit ? m1 : ~m1;
+  }
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(same & below);
+  if (e < E && rank == 0) wcnt[wave * E + e] = __popcll(same);
+  __syncthreads();
+  if (i < n) {
+    int row = -1;
+    if (e < E) {
+      int base = ws[(int64_t)blockIdx.x * E + e];
+      for (int w = 0; w < wave; ++w) base += wcnt[w * E + e];
+      row = poff[e] + base + rank;
+      row_token[row] = (int32_t)(i / k);
+    }
+    token_rows[i] = row;
+  }
+}
+
+hipError_t launch_route(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e0, int32_t E, int32_t P,
+                        int32_t block_m_override, int32_t* counts, int32_t* eoff, int32_t* poff,
+                        int32_t* row_token, int64_t M_cap, int32_t* token_rows, int32_t* sched,
+                        int32_t* ws, hipStream_t stream) {
+  const int64_t n = (int64_t)T * k;
+  const int32_t nchunks = (int32_t)((n + kRouteChunk - 1) / kRouteChunk);
+  const int grid1 = nchunks > 0 ? nchunks : 1;
+  hipLaunchKernelGGL(route_count_kernel, dim3(grid1), dim3(kRouteChunk), (size_t)E * sizeof(int32_t), stream,
+                     topk_ids, n, e0, E, nchunks, ws, row_token, M_cap);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, ws, nchunks, E, P, block_m_override,
+                     counts, eoff, poff, sched);
+  err = hipGetLastError();
+  if (err != hipSuccess || nchunks == 0) return err;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(kRouteChunk),
+                     (size_t)(kRouteChunk / kWave) * E * sizeof(int32_t), stream, topk_ids, n, k, e0, E, ws, poff,
+                     row_token, token_rows);
+  return hipGetLastError();
+}
+
+}  // namespace megamoe

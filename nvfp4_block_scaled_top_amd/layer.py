@@ -1,0 +1,138 @@
+"""Buffer ownership and call order for one routed-expert layer on the GPU.
+
+PyTorch allocates device memory here; every computation is a call into libmegamoe through
+``megamoe``.  ``MoEWeights`` holds NVFP4 expert weights quantized on the GPU by
+``nvfp4_quantize_act`` (one global scale per expert and matrix), and ``MoELayer`` holds the
+intermediate buffers for a fixed (T, k, E, H, I, P) and runs the six-call forward:
+route/permute, quantize x, L1 gate+up + SiLU, quantize h (amax from L1), L2 down, combine.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import megamoe as mm
+
+
+@dataclasses.dataclass
+class MoEWeights:
+    w13_codes: torch.Tensor   # uint8 [E, 2I, H/2]
+    w13_scales: torch.Tensor  # uint8 [E, 2I, H/16]
+    w13_gs: torch.Tensor      # float32 [E]
+    w2_codes: torch.Tensor    # uint8 [E, H, I/2]
+    w2_scales: torch.Tensor   # uint8 [E, H, I/16]
+    w2_gs: torch.Tensor       # float32 [E]
+
+    @property
+    def num_experts(self) -> int:
+        return self.w13_codes.shape[0]
+
+    @property
+    def hidden(self) -> int:
+        return self.w13_codes.shape[2] * 2
+
+    @property
+    def intermediate(self) -> int:
+        return self.w13_codes.shape[1] // 2
+
+    def nbytes_expert(self) -> int:
+        """NVFP4 bytes of one expert (codes + block scales + the two global scales)."""
+        return sum(t[0].numel() * t.element_size() for t in
+                   (self.w13_codes, self.w13_scales, self.w2_codes, self.w2_scales)) + 8
+
+    @staticmethod
+    def empty(E: int, H: int, I: int, device="cuda") -> "MoEWeights":
+        u8 = dict(dtype=torch.uint8, device=device)
+        return MoEWeights(torch.empty(E, 2 * I, H // 2, **u8), torch.empty(E, 2 * I, H // 16, **u8),
+                          torch.empty(E, dtype=torch.float32, device=device),
+                          torch.empty(E, H, I // 2, **u8), torch.empty(E, H, I // 16, **u8),
+                          torch.empty(E, dtype=torch.float32, device=device))
+
+    def clone(self) -> "MoEWeights":
+        return MoEWeights(*(t.clone() for t in dataclasses.astuple(self)))
+
+
+def quantize_matrix(w_bf16: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, gs: torch.Tensor,
+                    stream=None) -> None:
+    """NVFP4-quantize one bf16 matrix on the GPU (rows = output features, K contiguous)."""
+    ws = torch.empty(mm.megamoe_quant_workspace_bytes(*w_bf16.shape), dtype=torch.uint8, device=w_bf16.device)
+    mm.nvfp4_quantize_act(w_bf16.view(torch.int16), codes, scales, gs, workspace=ws, stream=stream)
+
+
+def quantize_expert_into(weights: MoEWeights, e: int, w13_bf16: torch.Tensor, w2_bf16: torch.Tensor) -> None:
+    quantize_matrix(w13_bf16, weights.w13_codes[e], weights.w13_scales[e], weights.w13_gs[e:e + 1])
+    quantize_matrix(w2_bf16, weights.w2_codes[e], weights.w2_scales[e], weights.w2_gs[e:e + 1])
+
+
+class MoELayer:
+    """Intermediate buffers for T tokens, top-k, E local experts, hidden H, intermediate I, pad P."""
+
+    def __init__(self, T: int, k: int, E: int, H: int, I: int, P: int = 1, expert_begin: int = 0,
+                 block_m_override: int = 0, device="cuda"):
+        self.T, self.k, self.E, self.H, self.I, self.P = T, k, E, H, I, P
+        self.expert_begin, self.block_m_override = expert_begin, block_m_override
+        self.M_cap = mm.megamoe_row_capacity(T, k, E, P)
+        i32 = dict(dtype=torch.int32, device=device)
+        u8 = dict(dtype=torch.uint8, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.counts = torch.empty(E, **i32)
+        self.expert_offsets = torch.empty(E + 1, **i32)
+        self.padded_offsets = torch.empty(E + 1, **i32)
+        self.row_token = torch.empty(max(self.M_cap, 1), **i32)
+        self.token_rows = torch.empty(max(T * k, 1), **i32)
+        self.sched = torch.empty(mm.megamoe_sched_len(E), **i32)
+        self.route_ws = torch.empty(max(mm.megamoe_route_workspace_bytes(T, k, E), 4), **u8)
+        self.x_codes = torch.empty(max(T, 1), H // 2, **u8)
+        self.x_scales = torch.empty(max(T, 1), H // 16, **u8)
+        self.x_gs = torch.empty(1, **f32)
+        self.x_ws = torch.empty(mm.megamoe_quant_workspace_bytes(T, H), **u8)
+        self.h = torch.empty(max(self.M_cap, 1), I, dtype=torch.int16, device=device)
+        self.h_amax = torch.empty(1, **f32)
+        self.h_codes = torch.empty(max(self.M_cap, 1), I // 2, **u8)
+        self.h_scales = torch.empty(max(self.M_cap, 1), I // 16, **u8)
+        self.h_gs = torch.empty(1, **f32)
+        self.y = torch.empty(max(self.M_cap, 1), H, dtype=torch.int16, device=device)
+        self.out = torch.empty(max(T, 1), H, dtype=torch.int16, device=device)
+
+    def _rows(self, t: torch.Tensor, n: int) -> torch.Tensor:
+        return t[:n] if n > 0 else t[:0]
+
+    def route(self, topk_ids: torch.Tensor, stream=None) -> None:
+        mm.moe_route_permute(topk_ids, self.expert_begin, self.E, self.P, self.counts, self.expert_offsets,
+                             self.padded_offsets, self.row_token, self.token_rows, self.sched, self.route_ws,
+                             block_m_override=self.block_m_override, stream=stream)
+
+    def quantize_x(self, x_bf16: torch.Tensor, stream=None) -> None:
+        mm.nvfp4_quantize_act(x_bf16, self._rows(self.x_codes, self.T), self._rows(self.x_scales, self.T),
+                              self.x_gs, workspace=self.x_ws, stream=stream)
+
+    def l1(self, w: MoEWeights, stream=None) -> None:
+        mm.moe_grouped_gemm_l1_silu(self.x_codes, self.x_scales, self.x_gs, self.row_token, self.padded_offsets,
+                                    self.counts, self.sched, w.w13_codes, w.w13_scales, w.w13_gs,
+                                    self._rows(self.h, self.M_cap), self.h_amax, stream=stream)
+
+    def quantize_h(self, stream=None) -> None:
+        mm.nvfp4_quantize_act(self._rows(self.h, self.M_cap), self._rows(self.h_codes, self.M_cap),
+                              self._rows(self.h_scales, self.M_cap), self.h_gs,
+                              row_valid=self._rows(self.row_token, self.M_cap), amax_in=self.h_amax, stream=stream)
+
+    def l2(self, w: MoEWeights, stream=None) -> None:
+        mm.moe_grouped_gemm_l2(self.h_codes, self.h_scales, self.h_gs, self.padded_offsets, self.counts, self.sched,
+                               w.w2_codes, w.w2_scales, w.w2_gs, self._rows(self.y, self.M_cap), stream=stream)
+
+    def combine(self, topk_weights: torch.Tensor, stream=None) -> None:
+        mm.moe_combine(self._rows(self.y, self.M_cap), self._rows(self.token_rows, self.T * self.k), topk_weights,
+                       self._rows(self.out, self.T), stream=stream)
+
+    def forward(self, x_bf16: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, w: MoEWeights,
+                stream=None) -> torch.Tensor:
+        """x_bf16 int16-viewed bf16 [T, H], topk_ids int32 [T, k], topk_weights float32 [T, k]."""
+        self.route(topk_ids, stream)
+        self.quantize_x(x_bf16, stream)
+        self.l1(w, stream)
+        self.quantize_h(stream)
+        self.l2(w, stream)
+        self.combine(topk_weights, stream)
+        return self._rows(self.out, self.T)

@@ -1,0 +1,152 @@
+"""Thin ctypes binding of libmegamoe.so: the C entry points under the same names.
+
+Argument marshalling only: each function takes torch tensors that already live on the GPU,
+passes their device pointers, sizes and the current HIP stream to the C ABI, and raises
+``MegaMoEError`` on a non-zero return code.  Every step of the layer runs in the library's HIP
+kernels; there is no fallback.  If the library has not been built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmegamoe.so")
+_lib = None
+
+ERRORS = {
+    -1: "MEGAMOE_ERR_NULL",
+    -2: "MEGAMOE_ERR_SHAPE",
+    -3: "MEGAMOE_ERR_WORKSPACE",
+    -4: "MEGAMOE_ERR_LAUNCH",
+    -5: "MEGAMOE_ERR_DEVICE",
+}
+
+#: Exported symbols and their C signatures (restype, argtypes), as declared in include/megamoe.h.
+_P = ctypes.c_void_p
+_I32, _I64, _SZ, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+SIGNATURES = {
+    "megamoe_row_capacity": (_I64, [_I32, _I32, _I32, _I32]),
+    "megamoe_sched_len": (_I64, [_I32]),
+    "megamoe_route_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "megamoe_quant_workspace_bytes": (_SZ, [_I64, _I64]),
+    "moe_route_permute": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "nvfp4_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_grouped_gemm_l1_silu": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P]),
+    "moe_grouped_gemm_l2": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P]),
+    "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
+}
+
+
+class MegaMoEError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libmegamoe.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise MegaMoEError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python -m nvfp4_block_scaled_top_amd.build_lib")
+        h = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(name: str, rc: int) -> None:
+    if rc != 0:
+        raise MegaMoEError(f"{name} returned {rc} ({ERRORS.get(rc, 'unknown')})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MegaMoEError("tensors passed to libmegamoe must be on the GPU")
+    if not t.is_contiguous():
+        raise MegaMoEError("tensors passed to libmegamoe must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+# ---- size helpers ------------------------------------------------------------------------------
+
+def megamoe_row_capacity(T: int, k: int, num_experts: int, pad_multiple: int) -> int:
+    return int(lib().megamoe_row_capacity(T, k, num_experts, pad_multiple))
+
+
+def megamoe_sched_len(num_experts: int) -> int:
+    return int(lib().megamoe_sched_len(num_experts))
+
+
+def megamoe_route_workspace_bytes(T: int, k: int, num_experts: int) -> int:
+    return int(lib().megamoe_route_workspace_bytes(T, k, num_experts))
+
+
+def megamoe_quant_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().megamoe_quant_workspace_bytes(rows, cols))
+
+
+# ---- entry points --------------------------------------------------------------------------------
+
+def moe_route_permute(topk_ids, expert_begin, num_experts, pad_multiple, counts, expert_offsets, padded_offsets,
+                      row_token, token_rows, sched, workspace, block_m_override=0, stream=None):
+    T, k = topk_ids.shape
+    _check("moe_route_permute", lib().moe_route_permute(
+        _ptr(topk_ids), T, k, expert_begin, num_experts, pad_multiple, block_m_override, _ptr(counts),
+        _ptr(expert_offsets), _ptr(padded_offsets), _ptr(row_token), _ptr(token_rows), _ptr(sched),
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def nvfp4_quantize_act(x_bf16, codes, scales, global_scale, workspace=None, row_valid=None, amax_in=None,
+                       stream=None):
+    rows, cols = x_bf16.shape
+    _check("nvfp4_quantize_act", lib().nvfp4_quantize_act(
+        _ptr(x_bf16), rows, cols, _ptr(row_valid), _ptr(amax_in), _ptr(codes), _ptr(scales), _ptr(global_scale),
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_grouped_gemm_l1_silu(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes,
+                             w13_scales, w13_gs, h_bf16, h_amax, stream=None):
+    E, I2, Hh = w13_codes.shape
+    M_cap = h_bf16.shape[0]
+    _check("moe_grouped_gemm_l1_silu", lib().moe_grouped_gemm_l1_silu(
+        _ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts), _ptr(sched),
+        _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), E, 2 * Hh, I2 // 2, M_cap, _ptr(h_bf16), _ptr(h_amax),
+        _stream(stream)))
+
+
+def moe_grouped_gemm_l2(h_codes, h_scales, h_gs, padded_offsets, counts, sched, w2_codes, w2_scales, w2_gs, y_bf16,
+                        stream=None):
+    E, H, Ih = w2_codes.shape
+    M_cap = y_bf16.shape[0]
+    _check("moe_grouped_gemm_l2", lib().moe_grouped_gemm_l2(
+        _ptr(h_codes), _ptr(h_scales), _ptr(h_gs), _ptr(padded_offsets), _ptr(counts), _ptr(sched), _ptr(w2_codes),
+        _ptr(w2_scales), _ptr(w2_gs), E, H, 2 * Ih, M_cap, _ptr(y_bf16), _stream(stream)))
+
+
+def moe_combine(y_bf16, token_rows, topk_weights, out_bf16, stream=None):
+    T, k = topk_weights.shape
+    H = out_bf16.shape[1]
+    _check("moe_combine", lib().moe_combine(
+        _ptr(y_bf16), _ptr(token_rows), _ptr(topk_weights), T, k, H, _ptr(out_bf16), _stream(stream)))

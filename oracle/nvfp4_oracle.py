@@ -102,7 +102,8 @@ def bf16_bits(v) -> np.ndarray:
 def bf16_from_bits(bits) -> np.ndarray:
     """float64 values of uint16 bf16 bit patterns."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
-    return b.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # NaN patterns stay NaN
+        return b.view(np.float32).astype(np.float64)
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every symbol include/megamoe.h declares, and rejects bad
+arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_block_scaled_top_amd import megamoe as mm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "megamoe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:int32_t|int64_t|size_t)\s+(\w+)\s*\(", src, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mm.library_path()):
+        from nvfp4_block_scaled_top_amd import build_lib
+        build_lib.build()
+    return mm.lib()
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(mm.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_error_codes_match_header():
+    src = open(HEADER).read()
+    for code, name in mm.ERRORS.items():
+        assert re.search(rf"#define {name} \({code}\)", src), name
+
+
+def test_size_helpers(lib):
+    assert mm.megamoe_row_capacity(8192, 6, 384, 1) == 49152
+    assert mm.megamoe_row_capacity(512, 6, 384, 128) == 3072 + 384 * 127
+    assert mm.megamoe_row_capacity(-1, 6, 384, 1) == -1
+    assert mm.megamoe_sched_len(48) == 6 + 3 * 48
+    assert mm.megamoe_sched_len(0) == -1
+    assert mm.megamoe_route_workspace_bytes(8, 6, 48) == 48 * 4
+    assert mm.megamoe_route_workspace_bytes(16384, 6, 384) == 96 * 384 * 4
+    assert mm.megamoe_quant_workspace_bytes(16, 256) == 4
+    assert mm.megamoe_quant_workspace_bytes(16384, 7168) == 1024 * 4
+
+
+def _c(v):
+    return ctypes.c_void_p(v)
+
+
+FAKE = 0x1000  # never dereferenced: every call below must fail its host-side checks
+
+
+def test_route_rejects_bad_args(lib):
+    f = lib.moe_route_permute
+    ok = [FAKE] * 6
+    assert f(FAKE, 4, 0, 0, 48, 1, 0, *ok, FAKE, 4096, None) == -2            # k < 1
+    assert f(FAKE, 4, 6, 0, 0, 1, 0, *ok, FAKE, 4096, None) == -2             # E < 1
+    assert f(FAKE, 4, 6, 0, 2000, 1, 0, *ok, FAKE, 1 << 20, None) == -2       # E too large
+    assert f(FAKE, 4, 6, 0, 48, 0, 0, *ok, FAKE, 4096, None) == -2            # P < 1
+    assert f(FAKE, 4, 6, 0, 48, 1, 48, *ok, FAKE, 4096, None) == -2           # unsupported block_m
+    assert f(FAKE, -1, 6, 0, 48, 1, 0, *ok, FAKE, 4096, None) == -2           # T < 0
+    assert f(None, 4, 6, 0, 48, 1, 0, *ok, FAKE, 4096, None) == -1            # ids NULL
+    assert f(FAKE, 4, 6, 0, 48, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == -1  # sched NULL
+    assert f(FAKE, 4, 6, 0, 48, 1, 0, *ok, FAKE, 4, None) == -3               # workspace too small
+
+
+def test_quant_rejects_bad_args(lib):
+    f = lib.nvfp4_quantize_act
+    assert f(FAKE, 4, 48, None, None, FAKE, FAKE, FAKE, FAKE, 64, None) == -2   # cols % 32
+    assert f(FAKE, 4, 0, None, None, FAKE, FAKE, FAKE, FAKE, 64, None) == -2    # cols 0
+    assert f(FAKE, -2, 64, None, None, FAKE, FAKE, FAKE, FAKE, 64, None) == -2  # rows < 0
+    assert f(None, 4, 64, None, None, FAKE, FAKE, FAKE, FAKE, 64, None) == -1
+    assert f(FAKE, 4, 64, None, None, FAKE, FAKE, None, FAKE, 64, None) == -1
+    assert f(FAKE, 4, 64, None, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -3
+    assert f(FAKE, 4, 64, None, None, FAKE, FAKE, FAKE, None, 64, None) == -1   # workspace NULL
+
+
+def test_gemm_rejects_bad_args(lib):
+    l1, l2 = lib.moe_grouped_gemm_l1_silu, lib.moe_grouped_gemm_l2
+    p10 = [FAKE] * 10
+    assert l1(*p10, 8, 200, 128, 64, FAKE, FAKE, None) == -2      # H not a multiple of 128
+    assert l1(*p10, 8, 256, 96, 64, FAKE, FAKE, None) == -2       # I not a multiple of 128
+    assert l1(*p10, 0, 256, 128, 64, FAKE, FAKE, None) == -2      # E < 1
+    assert l1(*p10, 8, 256, 128, -1, FAKE, FAKE, None) == -2      # M_cap < 0
+    assert l1(*p10, 8, 256, 128, 64, FAKE, None, None) == -1      # h_amax NULL
+    assert l1(None, *p10[1:], 8, 256, 128, 64, FAKE, FAKE, None) == -1
+    p9 = [FAKE] * 9
+    assert l2(*p9, 8, 256, 100, 64, FAKE, None) == -2
+    assert l2(*p9, 8, 256, 128, 64, None, None) == -1
+
+
+def test_combine_rejects_bad_args(lib):
+    f = lib.moe_combine
+    assert f(FAKE, FAKE, FAKE, 4, 0, 256, FAKE, None) == -2
+    assert f(FAKE, FAKE, FAKE, 4, 6, 12, FAKE, None) == -2
+    assert f(None, FAKE, FAKE, 4, 6, 256, FAKE, None) == -1
