@@ -56,6 +56,9 @@ extern "C" {
 /* Largest number of local experts one call handles. */
 #define MEGAMOE_MAX_EXPERTS 1024
 
+/* Slots of the per-workgroup h amax written by moe_grouped_gemm_l1_silu (every slot, every call). */
+#define MEGAMOE_L1_AMAX_PARTS 1280
+
 /* ------------------------------------------------------------------------------------------
  * Host-side size helpers (no HIP calls; usable without a GPU).
  * ---------------------------------------------------------------------------------------- */
@@ -85,8 +88,8 @@ size_t megamoe_quant_workspace_bytes(int64_t rows, int64_t cols);
  * num_experts     E, local experts (1..MEGAMOE_MAX_EXPERTS).
  * pad_multiple    P >= 1: each expert's row block is padded to a multiple of P (zero stays 0).
  * block_m_override 0 = per-expert tile height chosen from the token count (16 for up to 16
- *                 tokens, larger tiles above); 16, 32, 64, 128 or 256 forces that height for
- *                 every expert.  The choice changes speed only; results agree to FP32 rounding.
+ *                 tokens, 256 above); 16 or 256 forces that height for every expert.  The
+ *                 choice changes speed only; results agree to FP32 summation order.
  * counts          int32 [E]     local assignments per expert.
  * expert_offsets  int32 [E+1]   exclusive prefix sum of counts.
  * padded_offsets  int32 [E+1]   exclusive prefix sum of round_up(counts, P).
@@ -120,13 +123,16 @@ int32_t moe_route_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t
  * rows, cols   rows >= 0, cols > 0 and a multiple of 32.
  * row_valid    nullable int32 [rows]: rows with row_valid[r] < 0 are excluded from amax and
  *              get zero codes and scales (pass row_token to quantize permuted rows).
- * amax_in      nullable float [1]: the amax of the valid rows, when already known (L1 writes
- *              it for h); NULL = computed here.
+ * amax_in      nullable float [amax_in_count]: partial maxima whose max is the amax of the valid
+ *              rows, when already known (moe_grouped_gemm_l1_silu writes MEGAMOE_L1_AMAX_PARTS of
+ *              them for h); NULL = computed here.
+ * amax_in_count number of floats at amax_in (1..65536; ignored when amax_in is NULL).
  * codes        uint8 [rows, cols/2];  scales uint8 [rows, cols/16];  global_scale float [1].
  * workspace    >= megamoe_quant_workspace_bytes(rows, cols) bytes (may be NULL if that is 0).
  * ---------------------------------------------------------------------------------------- */
 int32_t nvfp4_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, const int32_t* row_valid,
-                           const float* amax_in, uint8_t* codes, uint8_t* scales, float* global_scale,
+                           const float* amax_in, int32_t amax_in_count, uint8_t* codes, uint8_t* scales,
+                           float* global_scale,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
@@ -139,22 +145,24 @@ int32_t nvfp4_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, const
  *   acc[n] = sum_k dec(x[row_token[r], k]) * dec(W13[e, n, k]),  n in [0, 2I)
  *   h[r, i] = bf16( SiLU(acc[i] / (gs_x * gs13[e])) * acc[I+i] / (gs_x * gs13[e]) )
  * with exact E2M1*E4M3 decode, FP16 MFMA products and FP32 accumulation.  Rows of h that hold
- * no assignment are not written.  h_amax receives max |h| over the written rows (the call
- * resets it first).  Experts with no tokens are never read.
+ * no assignment are not written.  Every workgroup writes the max |h| of the rows it wrote (0 if
+ * none) into its own slot of h_amax_parts, and every slot is written on every call, so the max
+ * over the MEGAMOE_L1_AMAX_PARTS slots is max |h| over the valid rows (no reset, no atomics).
+ * Experts with no tokens are never read.
  *
  * x_codes/x_scales/x_gs   NVFP4 x per token: [T, H/2], [T, H/16], [1].
  * row_token, padded_offsets, counts, sched   as written by moe_route_permute.
  * w13_codes/w13_scales/w13_gs   [E, 2I, H/2], [E, 2I, H/16], [E].
- * E, H, I      E as given to moe_route_permute; H, I multiples of 64 (I >= 64).
+ * E, H, I      E as given to moe_route_permute; H a multiple of 256, I a multiple of 128.
  * M_cap        rows of h: megamoe_row_capacity(T, k, E, P).
- * h_bf16       bf16 [M_cap, I].   h_amax float [1].
+ * h_bf16       bf16 [M_cap, I].   h_amax_parts float [MEGAMOE_L1_AMAX_PARTS].
  * ---------------------------------------------------------------------------------------- */
 int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
                                  const int32_t* row_token, const int32_t* padded_offsets,
                                  const int32_t* counts, const int32_t* sched,
                                  const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
                                  int32_t E, int32_t H, int32_t I, int64_t M_cap,
-                                 void* h_bf16, float* h_amax, void* stream);
+                                 void* h_bf16, float* h_amax_parts, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * moe_grouped_gemm_l2 - L2 down grouped GEMM over experts.

@@ -34,7 +34,7 @@ int32_t check_device() {
 int32_t launch_status(hipError_t e) { return e == hipSuccess ? MEGAMOE_OK : MEGAMOE_ERR_LAUNCH; }
 
 bool gemm_shape_ok(int32_t E, int32_t H, int32_t I, int64_t M_cap) {
-  return E >= 1 && E <= MEGAMOE_MAX_EXPERTS && H >= 128 && I >= 128 && H % 128 == 0 && I % 128 == 0 &&
+  return E >= 1 && E <= MEGAMOE_MAX_EXPERTS && H >= 256 && I >= 128 && H % 256 == 0 && I % 128 == 0 &&
          M_cap >= 0 && M_cap < (int64_t)1 << 31;
 }
 
@@ -90,9 +90,10 @@ int32_t moe_route_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t
 }
 
 int32_t nvfp4_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, const int32_t* row_valid,
-                           const float* amax_in, uint8_t* codes, uint8_t* scales, float* global_scale, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           const float* amax_in, int32_t amax_in_count, uint8_t* codes, uint8_t* scales,
+                           float* global_scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 0 || cols <= 0 || cols % 32 != 0 || rows > ((int64_t)1 << 40) / cols) return MEGAMOE_ERR_SHAPE;
+  if (amax_in && (amax_in_count < 1 || amax_in_count > 65536)) return MEGAMOE_ERR_SHAPE;
   if (!global_scale) return MEGAMOE_ERR_NULL;
   if (rows > 0 && (!x_bf16 || !codes || !scales)) return MEGAMOE_ERR_NULL;
   const size_t need = amax_in ? 0 : megamoe_quant_workspace_bytes(rows, cols);
@@ -100,7 +101,7 @@ int32_t nvfp4_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, const
   if (need > 0 && !workspace) return MEGAMOE_ERR_NULL;
   const int32_t dev = check_device();
   if (dev != MEGAMOE_OK) return dev;
-  return launch_status(launch_quant(static_cast<const uint16_t*>(x_bf16), rows, cols, row_valid, amax_in, codes, scales,
+  return launch_status(launch_quant(static_cast<const uint16_t*>(x_bf16), rows, cols, row_valid, amax_in, amax_in_count, codes, scales,
                                     global_scale, static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
@@ -108,15 +109,15 @@ int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales
                                  const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
                                  const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
                                  const float* w13_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap, void* h_bf16,
-                                 float* h_amax, void* stream) {
+                                 float* h_amax_parts, void* stream) {
   if (!gemm_shape_ok(E, H, I, M_cap)) return MEGAMOE_ERR_SHAPE;
   if (!x_codes || !x_scales || !x_gs || !row_token || !padded_offsets || !counts || !sched || !w13_codes ||
-      !w13_scales || !w13_gs || !h_bf16 || !h_amax)
+      !w13_scales || !w13_gs || !h_bf16 || !h_amax_parts)
     return MEGAMOE_ERR_NULL;
   const int32_t dev = check_device();
   if (dev != MEGAMOE_OK) return dev;
   GemmArgs a{x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
-             E, H, I, h_bf16, h_amax};
+             E, H, I, h_bf16, h_amax_parts};
   return launch_status(launch_gemm_l1(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -16,8 +16,8 @@
 //    from HBM straight into registers, 16 B per lane per 128-element chunk of the reduction
 //    dimension; the reduction dimension is split over the 4 waves of a workgroup and the partial
 //    sums are added in a fixed order through LDS (deterministic);
-//  * large (128x128 tiles): both operands are decoded into fp16 tiles in LDS (double-buffered,
-//    register-prefetched), and each wave computes a 64x64 block with 16 MFMAs per 32-K step.
+//  * large (256x256 tiles): raw NVFP4 staged in a 3-slot LDS ring and decoded per wave; each
+//    wave computes a 128x128 block with 64 MFMAs per 32-K step (details below).
 // Tiles are ordered expert-major, then m-tile, then n-tile (n fastest), and workgroup ids are
 // remapped so that the workgroups on one XCD take consecutive tiles (the same A rows stay in that
 // XCD's L2).
@@ -36,6 +36,10 @@ constexpr int kXcds = 8;
 
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // XCD-aware persistent tile loop.  Workgroups are dispatched round-robin over the 8 XCDs, so
@@ -80,7 +84,10 @@ __device__ __forceinline__ TileInfo decode_tile(const int* s_pref, int E, int nt
   return ti;
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// SiLU in fp32 with the hardware exp2 and reciprocal (a few ulp); h is rounded to bf16 right after.
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+}
 
 // ============================================================================================
 // Small class: 16 rows x 32 weight rows per tile, K split over 4 waves.
@@ -88,6 +95,9 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)
 // ============================================================================================
 constexpr int kSmallBn = 32;
 constexpr int kChunk = 128;
+constexpr int kLargeGrid = 256;   // large class: one workgroup per CU (LDS ~139 KB)
+constexpr int kSmallGrid = MEGAMOE_L1_AMAX_PARTS - kLargeGrid;
+static_assert(kSmallGrid % kXcds == 0 && kSmallGrid > 0, "grid split");
 
 template <bool kL1>
 __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs p) {
@@ -206,145 +216,321 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs p) {
     __syncthreads();
   }
   if (kL1) {
+    // only wave 0 wrote h; its max is the workgroup's
     amax_bits = wave_max_u32(amax_bits);
-    if (threadIdx.x == 0 && amax_bits != 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax_out), amax_bits << 16);
+    if (threadIdx.x == 0) p.amax_out[kLargeGrid + blockIdx.x] = bf16_bits_to_f32(amax_bits);
   }
 }
 
 // ============================================================================================
-// Large class: 128x128 tiles, K step 64, LDS-staged fp16 operands.
-// L1: B tile rows 0..63 = gate rows nt*64.., rows 64..127 = up rows I + nt*64.. -> 64 h columns.
-// L2: B tile rows = weight rows nt*128..+128 -> 128 y columns.
+// Large class: 256x256 tiles, stages of raw NVFP4 streamed straight into an LDS ring.
+//
+// Global -> LDS: gfx950's global_load_lds_dwordx4 writes each lane's 16 bytes into LDS without a
+// register round trip (lane i of an instruction lands at base + 16*i).  Stage ks+kLAhead is
+// requested while stage ks is computed; a stage is consumed after an explicit s_waitcnt vmcnt
+// (this wave's loads) and one s_barrier (everyone's).  The slot being refilled was last read two
+// stages earlier, so that single barrier per stage orders both directions.  (__syncthreads()
+// would also wait for every load still in flight.)  Measured on the 8192-token prefill, 128-K
+// stages with 4 slots were faster than 64-K stages with 8 slots and six stages in flight.
+//
+// LDS holds raw codes and scales (0.5625 B/element) and each wave decodes the fragments it needs
+// right before its MFMAs.  Decoding into fp16 tiles in LDS instead would move ~3.5x more LDS
+// bytes per MFMA; per-wave decoding costs 4 VALU instructions per 32-cycle
+// v_mfma_f32_32x32x16_f16, which the VALU issues while the matrix core runs (the 32x32x16 shape
+// sustains ~97% of the fp16 peak on gfx950, the 16x16x32 shape only ~55%).
+//
+// Stage layout (per operand): codes row-major, kLRowBytes per tile row R, with the 16-byte chunk
+// c (elements 32c..32c+31 of the stage) stored in slot c ^ swizzle(R) so that the 16-byte
+// fragment reads of 8 consecutive rows hit distinct banks; a DMA instruction covers 1024 / 
+// kLRowBytes rows with kLChunks lanes per row (row-contiguous global bytes).  Scales: the stage's
+// block scales of row R for lane half h at h * (kLBm * kLScaleRow / 2) + R * kLScaleRow / 2.
+// Lane (p = lane % 32, h = lane / 32) of a 32-row fragment owns elements [h * kLKs/2, +kLKs/2) of
+// its row and feeds [h * kLKs/2 + 8s, +8) to MFMA step s as the MFMA's k = 8h..8h+7.  A and B use
+// the same map, so each dot product runs over every element once.
+//
+// Waves are 2x2, each 128x128 of the tile (4 x 4 MFMA blocks of 32x32, 256 fp32 accumulators).
+// L1: tile weight rows 0..127 are gate rows nt*128.., 128..255 the matching up rows, so a wave
+// holds gate and up of the same 64 h columns and applies SiLU(gate)*up in registers.
+// L2: tile weight rows are output rows nt*256..+256.
+// The epilogue stages the bf16 tile in LDS and writes it with 16-byte row-contiguous stores.
 // ============================================================================================
-constexpr int kLBm = kBlockMLarge, kLBn = 128, kLKt = 64, kLLd = kLKt + 8;  // LDS row pitch (fp16)
+constexpr int kLBm = kBlockMLarge, kLBn = 256;
+constexpr int kLKs = 128, kLSlots = 4, kLAhead = 2;               // stage depth, ring slots, prefetch
+constexpr int kLRowBytes = kLKs / 2;                             // code bytes of one row per stage
+constexpr int kLChunks = kLRowBytes / 16;                        // 16-byte chunks per row (2 or 4)
+constexpr int kLSwzShift = kLChunks == 2 ? 2 : 1;                // row bits that pick the swizzle
+constexpr int kLScaleRow = kLKs / 16;                            // scale bytes of one row per stage
+constexpr int kLSteps = kLKs / 16;                               // 32x32x16 MFMA steps per stage
+constexpr int kLCodeBytes = kLBm * kLRowBytes;
+constexpr int kLScaleBytes = kLBm * kLScaleRow;
+constexpr int kLOpBytes = kLCodeBytes + kLScaleBytes;            // one operand, one stage
+constexpr int kLStageBytes = 2 * kLOpBytes;
+constexpr int kLLdsBytes = kLSlots * kLStageBytes;
+constexpr int kLCodeDma = 64 * kLRowBytes / 1024;                // per wave and operand
+constexpr int kLScaleDma = kLScaleRow / 4;                       // 4-byte DMA per row and half
+constexpr int kLDmaPerWave = 2 * (kLCodeDma + kLScaleDma);
+constexpr int kLOutPitchL1 = 128 * 2 + 16, kLOutPitchL2 = 256 * 2 + 16;  // bf16 staging pitches
+static_assert(kLKs == 64 || kLKs == 128, "stage depth");
+static_assert(kLBm == 256 && kLBn == 256, "large tiles are 256x256");
+static_assert(kLAhead <= kLSlots - 2, "refilled slot must have been read two stages earlier");
+static_assert(kLBm * kLOutPitchL2 <= kLLdsBytes && kLBm * kLOutPitchL1 <= kLLdsBytes, "staging fits");
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Direct global -> LDS loads.  Issued through inline assembly so that the compiler does not track
+// them as LDS writes (it would otherwise wait for every outstanding load before any LDS read it
+// cannot prove disjoint, draining the prefetch each stage).  Their ordering is explicit instead:
+// wait_vmcnt() for this wave's loads, then s_barrier for everyone's.  The compiler's own vmcnt
+// waits stay correct because loads retire in order.  Nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is written only here (checked in the ISA)
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform; must live in an SGPR for M0
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t* src, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding: vmcnt bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most `stages_after` (<= kLAhead) later stages' loads are outstanding for this wave.
+template <int K = kLAhead>
+__device__ __forceinline__ void wait_stage(int stages_after) {
+  if constexpr (K == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (stages_after >= K) wait_vmcnt<K * kLDmaPerWave>();
+    else wait_stage<K - 1>(stages_after);
+  }
+}
 
 template <bool kL1>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_large_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][kLBm * kLLd];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kLBn * kLLd];
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLLdsBytes];
   __shared__ int s_pref[kMaxExperts + 1];
+  __shared__ uint32_t s_amax[kGemmThreads / kWave];
   const int E = p.E;
   for (int j = threadIdx.x; j <= E; j += blockDim.x) s_pref[j] = p.sched[sched_pref_large(E) + j];
   __syncthreads();
-  const int ntn = kL1 ? p.N / 64 : p.N / kLBn;
+  const int ntn = kL1 ? p.N / 128 : p.N / kLBn;
   const int total = s_pref[E] * ntn;
   const int K = p.K, Kh = K / 2, Ks = K / 16;
   const int Nw = kL1 ? 2 * p.N : p.N;
-  const int nk = K / kLKt;
+  const int nks = K / kLKs;
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int wm = wave >> 1, wn = wave & 1;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int ld_row = tid >> 1, ld_half = tid & 1;  // global->LDS: 128 rows x 2 halves of 32 K
+  const int p32 = lane & 31, h2 = lane >> 5;
   const float gs_a = *p.a_gs;
   uint32_t amax_bits = 0;
-  // LDS row of B fragment f for this wave.
-  int brow[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) brow[f] = kL1 ? (f < 2 ? wn * 32 + 16 * f : 64 + wn * 32 + 16 * (f - 2)) : wn * 64 + 16 * f;
+
+  // first tile weight row of this wave's 32-column fragment f
+  auto brow_of = [&](int f) {
+    return kL1 ? (f < 2 ? wn * 64 + 32 * f : 128 + wn * 64 + 32 * (f - 2)) : wn * 128 + 32 * f;
+  };
 
   const XcdTiles tl(total);
   for (int t = tl.t; t < tl.end; t += tl.stride) {
     const TileInfo ti = decode_tile(s_pref, E, ntn, t, kLBm, p.padded_offsets, p.counts);
-    // This thread's A and B source rows for the global->LDS copy.
-    const bool a_ok = ld_row < ti.rows_left;
-    int64_t a_row = ti.row0 + ld_row;
-    if (kL1) a_row = a_ok ? p.row_token[a_row] : 0;
-    const uint8_t* __restrict__ a_c = p.a_codes + a_row * Kh + ld_half * 16;
-    const uint8_t* __restrict__ a_s = p.a_scales + a_row * Ks + ld_half * 2;
-    int64_t b_row;
-    if (kL1) b_row = (int64_t)ti.e * Nw + (ld_row < 64 ? ti.nt * 64 + ld_row : p.N + ti.nt * 64 + ld_row - 64);
-    else b_row = (int64_t)ti.e * Nw + ti.nt * kLBn + ld_row;
-    const uint8_t* __restrict__ b_c = p.w_codes + b_row * Kh + ld_half * 16;
-    const uint8_t* __restrict__ b_s = p.w_scales + b_row * Ks + ld_half * 2;
+    // ---- DMA sources of this lane --------------------------------------------------------------
+    // codes: instruction j covers tile rows 64*wave + j*rows_per + lane/kLChunks; lane%kLChunks
+    // picks the LDS slot and the global chunk (lane%kLChunks) ^ swizzle(row) goes there; scales:
+    // tile row 64*wave + lane.
+    auto a_row_of = [&](int R) -> int64_t {
+      const int Rv = R < ti.rows_left ? R : 0;  // rows past the expert read row 0; never stored
+      const int64_t r = ti.row0 + Rv;
+      return kL1 ? (int64_t)p.row_token[r] : r;
+    };
+    auto b_row_of = [&](int R) -> int64_t {
+      if (kL1) return (int64_t)ti.e * Nw + (R < 128 ? ti.nt * 128 + R : p.N + ti.nt * 128 + R - 128);
+      return (int64_t)ti.e * Nw + ti.nt * kLBn + R;
+    };
+    constexpr int rows_per = 1024 / kLRowBytes;
+    const uint8_t* a_code_src[kLCodeDma];
+    const uint8_t* b_code_src[kLCodeDma];
+#pragma unroll
+    for (int j = 0; j < kLCodeDma; ++j) {
+      const int R = 64 * wave + rows_per * j + lane / kLChunks;
+      const int chunk = (lane % kLChunks) ^ ((R >> kLSwzShift) & (kLChunks - 1));
+      a_code_src[j] = p.a_codes + a_row_of(R) * Kh + 16 * chunk;
+      b_code_src[j] = p.w_codes + b_row_of(R) * Kh + 16 * chunk;
+    }
+    const uint8_t* a_scale_src = p.a_scales + a_row_of(64 * wave + lane) * Ks;
+    const uint8_t* b_scale_src = p.w_scales + b_row_of(64 * wave + lane) * Ks;
 
-    f32x4 acc[4][4];
+    f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int f = 0; f < 4; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.f;
 
-    u32x4 ac = {0u, 0u, 0u, 0u}, bc = {0u, 0u, 0u, 0u};
-    uint32_t as = 0, bs = 0;
-    auto load = [&](int kt) {
-      const int64_t off = (int64_t)kt * (kLKt / 2), soff = (int64_t)kt * (kLKt / 16);
-      if (a_ok) {
-        ac = *reinterpret_cast<const u32x4*>(a_c + off);
-        as = *reinterpret_cast<const uint16_t*>(a_s + soff);
-      }
-      bc = *reinterpret_cast<const u32x4*>(b_c + off);
-      bs = *reinterpret_cast<const uint16_t*>(b_s + soff);
-    };
-    auto store = [&](int buf) {
-      const f16x2 sa = e4m3x2_to_f16(as, false), sb = e4m3x2_to_f16(bs, false);
-      _Float16* ad = &As[buf][ld_row * kLLd + ld_half * 32];
-      _Float16* bd = &Bs[buf][ld_row * kLLd + ld_half * 32];
+    // kLDmaPerWave DMA instructions per wave: this wave's 64 rows of both operands for stage ks.
+    auto issue_stage = [&](int ks, int slot) {
+      const uint32_t lb = lds_addr(smem + slot * kLStageBytes);
+      const int64_t off = (int64_t)ks * kLRowBytes, soff = (int64_t)ks * kLScaleRow;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<f16x8*>(ad + 8 * j) = decode8(ac[j], j < 2 ? bcast_lo(sa) : bcast_hi(sa));
-        *reinterpret_cast<f16x8*>(bd + 8 * j) = decode8(bc[j], j < 2 ? bcast_lo(sb) : bcast_hi(sb));
+      for (int j = 0; j < kLCodeDma; ++j) {
+        dma16(a_code_src[j] + off, lb + (64 * wave + rows_per * j) * kLRowBytes);
+        dma16(b_code_src[j] + off, lb + kLOpBytes + (64 * wave + rows_per * j) * kLRowBytes);
+      }
+#pragma unroll
+      for (int hh = 0; hh < kLScaleDma; ++hh) {
+        const int so = kLCodeBytes + hh * (kLBm * 4) + 64 * wave * 4;
+        dma4(a_scale_src + soff + 4 * hh, lb + so);
+        dma4(b_scale_src + soff + 4 * hh, lb + kLOpBytes + so);
       }
     };
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) load(kt + 1);
+    auto compute_stage = [&](int slot) {
+      const uint8_t* base = smem + slot * kLStageBytes;
+      const uint8_t* a_codes = base;
+      const uint8_t* a_scales = base + kLCodeBytes;
+      const uint8_t* b_codes = base + kLOpBytes;
+      const uint8_t* b_scales = b_codes + kLCodeBytes;
+      constexpr int CPL = kLChunks / 2;  // chunks per lane half
+      // rows 32i + p and brow_of(f) + p share (row >> shift) with p: offsets are multiples of 32
+      const int swz = (p32 >> kLSwzShift) & (kLChunks - 1);
+      // scale bytes of this lane half: 2 (64-K stages) or 4 (128-K stages) per row
+      auto scale_word = [&](const uint8_t* sp, int row) -> uint32_t {
+        if (kLScaleRow == 8) return *reinterpret_cast<const uint32_t*>(sp + h2 * (kLBm * 4) + row * 4);
+        return *reinterpret_cast<const uint16_t*>(sp + row * 4 + 2 * h2);
+      };
+      u32x4 araw[4][CPL], braw[4][CPL];
+      uint32_t asw[4], bsw[4];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        f16x8 a[4], b[4];
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + 32 * i + p32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a[i] = *reinterpret_cast<const f16x8*>(&As[buf][(wm * 64 + 16 * i + r16) * kLLd + s * 32 + 8 * g]);
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-          b[f] = *reinterpret_cast<const f16x8*>(&Bs[buf][(brow[f] + r16) * kLLd + s * 32 + 8 * g]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int f = 0; f < 4; ++f) acc[i][f] = mfma16(a[i], b[f], acc[i][f]);
+        for (int j = 0; j < CPL; ++j)
+          araw[i][j] = *reinterpret_cast<const u32x4*>(a_codes + row * kLRowBytes + 16 * ((CPL * h2 + j) ^ swz));
+        asw[i] = scale_word(a_scales, row);
       }
-      if (kt + 1 < nk) store(buf ^ 1);
-      __syncthreads();
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int row = brow_of(f) + p32;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+          braw[f][j] = *reinterpret_cast<const u32x4*>(b_codes + row * kLRowBytes + 16 * ((CPL * h2 + j) ^ swz));
+        bsw[f] = scale_word(b_scales, row);
+      }
+      // fp16 scale pairs: pair q covers steps 4q..4q+3 (blocks 2q, 2q+1 of this lane half)
+      f16x2 asc[4][CPL], bsc[4][CPL];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        asc[i][0] = e4m3x2_to_f16(asw[i], false);
+        bsc[i][0] = e4m3x2_to_f16(bsw[i], false);
+        if (CPL == 2) {
+          asc[i][CPL - 1] = e4m3x2_to_f16(asw[i], true);
+          bsc[i][CPL - 1] = e4m3x2_to_f16(bsw[i], true);
+        }
+      }
+      auto sc = [](const f16x2 (&pr)[CPL], int step) {
+        const f16x2 v = pr[step >> 2];
+        return (step & 2) ? bcast_hi(v) : bcast_lo(v);
+      };
+      auto word = [](const u32x4 (&r)[CPL], int step) { return r[step >> 2][step & 3]; };
+      // Software pipeline: B fragments of step s+1 are decoded between the MFMAs of step s.
+      f16x8 b[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) b[f] = decode8(word(braw[f], 0), sc(bsc[f], 0));
+#pragma unroll
+      for (int st = 0; st < kLSteps; ++st) {
+        f16x8 bn[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f16x8 a = decode8(word(araw[i], st), sc(asc[i], st));
+          if (st + 1 < kLSteps) bn[i] = decode8(word(braw[i], st + 1), sc(bsc[i], st + 1));
+#pragma unroll
+          for (int f = 0; f < 4; ++f) acc[i][f] = mfma32(a, b[f], acc[i][f]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
+          }
+        }
+        if (st + 1 < kLSteps) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) b[f] = bn[f];
+        }
+      }
+    };
+
+    for (int ks = 0; ks < kLAhead && ks < nks; ++ks) issue_stage(ks, ks);
+    for (int ks = 0; ks < nks; ++ks) {
+      // Request stage ks+kLAhead into the slot last read by stage ks-2 (every wave has passed the
+      // barrier of stage ks-1 since), then wait until this wave's stage-ks loads have landed.
+      if (ks + kLAhead < nks) issue_stage(ks + kLAhead, (ks + kLAhead) % kLSlots);
+      const int after = nks - 1 - ks;
+      wait_stage(after < kLAhead ? after : kLAhead);
+      __builtin_amdgcn_s_barrier();  // everyone's stage-ks loads have landed
+      compute_stage(ks % kLSlots);
     }
+    __syncthreads();  // all waves are done reading the ring before it is reused for staging
 
+    // ---- epilogue: scale, (SiLU*up), bf16, stage in LDS, coalesced stores ----------------------
+    // accumulator r of block (i, f) is row 32i + 8(r/4) + 4h + r%4, column 32f + p of the wave tile
     const float inv = (float)(1.0 / ((double)gs_a * (double)p.w_gs[ti.e]));
-    uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
+    constexpr int pitch = kL1 ? kLOutPitchL1 : kLOutPitchL2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = wm * 64 + 16 * i + 4 * g + q;
-        if (r < ti.rows_left) {
-          const int64_t orow = (int64_t)(ti.row0 + r) * p.N;
-          if (kL1) {
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        const bool ok = row < ti.rows_left;
+        if (kL1) {
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-              const float gt = acc[i][f][q] * inv, up = acc[i][f + 2][q] * inv;
-              const uint32_t hb = f32_to_bf16_bits(silu_f32(gt) * up);
-              out[orow + ti.nt * 64 + wn * 32 + 16 * f + r16] = (uint16_t)hb;
-              const uint32_t mag = hb & 0x7FFFu;
-              amax_bits = amax_bits > mag ? amax_bits : mag;
-            }
-          } else {
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-              out[orow + ti.nt * kLBn + wn * 64 + 16 * f + r16] = (uint16_t)f32_to_bf16_bits(acc[i][f][q] * inv);
+          for (int f = 0; f < 2; ++f) {
+            const float gt = acc[i][f][r] * inv, up = acc[i][f + 2][r] * inv;
+            const uint32_t hb = f32_to_bf16_bits(silu_f32(gt) * up);
+            *reinterpret_cast<uint16_t*>(smem + row * pitch + 2 * (wn * 64 + 32 * f + p32)) = (uint16_t)hb;
+            const uint32_t mag = ok ? (hb & 0x7FFFu) : 0u;
+            amax_bits = amax_bits > mag ? amax_bits : mag;
           }
+        } else {
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+            *reinterpret_cast<uint16_t*>(smem + row * pitch + 2 * (wn * 128 + 32 * f + p32)) =
+                (uint16_t)f32_to_bf16_bits(acc[i][f][r] * inv);
         }
       }
     }
+    __syncthreads();
+    {
+      constexpr int cols = kL1 ? 128 : 256;
+      constexpr int chunks = cols * 2 / 16;  // 16-byte chunks per row
+      const int nrows = ti.rows_left < kLBm ? ti.rows_left : kLBm;
+      uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
+      const int col0 = ti.nt * cols;
+      for (int idx = tid; idx < nrows * chunks; idx += kGemmThreads) {
+        const int r = idx / chunks, c = idx - r * chunks;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * pitch + 16 * c);
+        *reinterpret_cast<u32x4*>(out + (int64_t)(ti.row0 + r) * p.N + col0 + 8 * c) = v;
+      }
+    }
+    __syncthreads();  // staging reads done before the next tile's DMA refills the ring
   }
   if (kL1) {
     amax_bits = wave_max_u32(amax_bits);
-    if (lane == 0 && amax_bits != 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax_out), amax_bits << 16);
+    if (lane == 0) s_amax[wave] = amax_bits;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m = s_amax[0];
+      for (int w = 1; w < kGemmThreads / kWave; ++w) m = m > s_amax[w] ? m : s_amax[w];
+      p.amax_out[blockIdx.x] = bf16_bits_to_f32(m);
+    }
   }
 }
-
-__global__ void zero_f32_kernel(float* p) { *p = 0.0f; }
-
-constexpr int kSmallGrid = 1024;  // persistent grids (multiples of kXcds)
-constexpr int kLargeGrid = 512;
 
 template <bool kL1>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
@@ -355,12 +541,7 @@ static hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_l1(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, stream, a.amax_out);
-  const hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  return launch_gemm<true>(a, stream);
-}
+hipError_t launch_gemm_l1(const GemmArgs& a, hipStream_t stream) { return launch_gemm<true>(a, stream); }
 
 hipError_t launch_gemm_l2(const GemmArgs& a, hipStream_t stream) { return launch_gemm<false>(a, stream); }
 

@@ -28,7 +28,7 @@ __host__ __device__ inline int sched_pref_large(int E) { return kSchedHeader + 2
 // Tile heights.  Small class: one 16-row MFMA block, weights streamed straight to registers with
 // the reduction dimension split across the waves of a workgroup.  Large class: LDS-tiled.
 constexpr int kBlockMSmall = 16;
-constexpr int kBlockMLarge = 128;
+constexpr int kBlockMLarge = 256;
 // Experts with at most this many tokens use the small class when block_m is chosen per expert.
 constexpr int kSmallClassMaxTokens = 16;
 
@@ -40,7 +40,7 @@ hipError_t launch_route(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e
 // ---- quantizer -------------------------------------------------------------------------------
 int quant_amax_parts(int64_t rows, int64_t cols);
 hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* row_valid,
-                        const float* amax_in, uint8_t* codes, uint8_t* scales, float* gs, float* ws,
+                        const float* amax_in, int32_t amax_in_count, uint8_t* codes, uint8_t* scales, float* gs, float* ws,
                         hipStream_t stream);
 
 // ---- grouped GEMMs ---------------------------------------------------------------------------
@@ -59,7 +59,7 @@ struct GemmArgs {
   const float* w_gs;
   int32_t E, K, N;   // N = output columns: I for L1 (weights have 2I rows), H for L2
   void* out;         // bf16 [M_cap, N]
-  float* amax_out;   // L1: max |h| (uint-ordered atomic max); NULL for L2
+  float* amax_out;   // L1: per-workgroup max |h| slots [MEGAMOE_L1_AMAX_PARTS]; NULL for L2
 };
 hipError_t launch_gemm_l1(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_l2(const GemmArgs& a, hipStream_t stream);

@@ -17,7 +17,8 @@
 //    once, which never changes its sign, so each comparison is exact; ties go to the even code.
 //
 // Two kernels: an amax pass writing per-workgroup partial maxima (skipped when the caller passes
-// amax_in), then the quantization pass, whose every workgroup reduces the partials itself.
+// its own partial maxima in amax_in), then the quantization pass, whose every workgroup reduces
+// the partials itself (no atomics, nothing to reset between calls).
 #include "device_common.h"
 #include "internal.h"
 
@@ -155,10 +156,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint16_t* __
 }
 
 hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* row_valid,
-                        const float* amax_in, uint8_t* codes, uint8_t* scales, float* gs, float* ws,
-                        hipStream_t stream) {
+                        const float* amax_in, int32_t amax_in_count, uint8_t* codes, uint8_t* scales, float* gs,
+                        float* ws, hipStream_t stream) {
   const float* amax_src = amax_in;
-  int nparts = 1;
+  int nparts = amax_in_count;
   if (amax_in == nullptr) {
     nparts = quant_amax_parts(rows, cols);
     hipLaunchKernelGGL(quant_amax_kernel, dim3(nparts), dim3(kQuantThreads), 0, stream, x, rows, cols, row_valid, ws);
@@ -168,7 +169,7 @@ hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int
   }
   const int64_t nblk = rows * (cols / 16);
   int64_t grid = (nblk + kQuantThreads - 1) / kQuantThreads;
-  if (grid > 8192) grid = 8192;
+  if (grid > 2048) grid = 2048;  // grid-stride beyond: every workgroup re-reduces the partial maxima
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(quant_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream, x, rows, cols, row_valid,
                      amax_src, nparts, codes, scales, gs);

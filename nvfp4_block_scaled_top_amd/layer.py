@@ -89,7 +89,7 @@ class MoELayer:
         self.x_gs = torch.empty(1, **f32)
         self.x_ws = torch.empty(mm.megamoe_quant_workspace_bytes(T, H), **u8)
         self.h = torch.empty(max(self.M_cap, 1), I, dtype=torch.int16, device=device)
-        self.h_amax = torch.empty(1, **f32)
+        self.h_amax = torch.empty(mm.L1_AMAX_PARTS, **f32)  # per-workgroup partial maxima from L1
         self.h_codes = torch.empty(max(self.M_cap, 1), I // 2, **u8)
         self.h_scales = torch.empty(max(self.M_cap, 1), I // 16, **u8)
         self.h_gs = torch.empty(1, **f32)

@@ -16,6 +16,9 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmegamoe.so")
 _lib = None
 
+#: Slots of per-workgroup h amax written by moe_grouped_gemm_l1_silu (MEGAMOE_L1_AMAX_PARTS).
+L1_AMAX_PARTS = 1280
+
 ERRORS = {
     -1: "MEGAMOE_ERR_NULL",
     -2: "MEGAMOE_ERR_SHAPE",
@@ -33,7 +36,7 @@ SIGNATURES = {
     "megamoe_route_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "megamoe_quant_workspace_bytes": (_SZ, [_I64, _I64]),
     "moe_route_permute": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "nvfp4_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "nvfp4_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_l1_silu": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P]),
     "moe_grouped_gemm_l2": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
@@ -121,18 +124,21 @@ def moe_route_permute(topk_ids, expert_begin, num_experts, pad_multiple, counts,
 def nvfp4_quantize_act(x_bf16, codes, scales, global_scale, workspace=None, row_valid=None, amax_in=None,
                        stream=None):
     rows, cols = x_bf16.shape
+    n_amax = 0 if amax_in is None else amax_in.numel()
     _check("nvfp4_quantize_act", lib().nvfp4_quantize_act(
-        _ptr(x_bf16), rows, cols, _ptr(row_valid), _ptr(amax_in), _ptr(codes), _ptr(scales), _ptr(global_scale),
+        _ptr(x_bf16), rows, cols, _ptr(row_valid), _ptr(amax_in), n_amax, _ptr(codes), _ptr(scales), _ptr(global_scale),
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def moe_grouped_gemm_l1_silu(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes,
-                             w13_scales, w13_gs, h_bf16, h_amax, stream=None):
+                             w13_scales, w13_gs, h_bf16, h_amax_parts, stream=None):
     E, I2, Hh = w13_codes.shape
     M_cap = h_bf16.shape[0]
+    if h_amax_parts.numel() < L1_AMAX_PARTS:
+        raise MegaMoEError(f"h_amax_parts needs {L1_AMAX_PARTS} floats")
     _check("moe_grouped_gemm_l1_silu", lib().moe_grouped_gemm_l1_silu(
         _ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts), _ptr(sched),
-        _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), E, 2 * Hh, I2 // 2, M_cap, _ptr(h_bf16), _ptr(h_amax),
+        _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), E, 2 * Hh, I2 // 2, M_cap, _ptr(h_bf16), _ptr(h_amax_parts),
         _stream(stream)))
 
 

@@ -33,6 +33,11 @@ def test_header_symbols_exported(lib):
         assert hasattr(lib, n)
 
 
+def test_constants_match_header():
+    src = open(HEADER).read()
+    assert re.search(rf"#define MEGAMOE_L1_AMAX_PARTS {mm.L1_AMAX_PARTS}\b", src)
+
+
 def test_error_codes_match_header():
     src = open(HEADER).read()
     for code, name in mm.ERRORS.items():
@@ -74,19 +79,20 @@ def test_route_rejects_bad_args(lib):
 
 def test_quant_rejects_bad_args(lib):
     f = lib.nvfp4_quantize_act
-    assert f(FAKE, 4, 48, None, None, FAKE, FAKE, FAKE, FAKE, 64, None) == -2   # cols % 32
-    assert f(FAKE, 4, 0, None, None, FAKE, FAKE, FAKE, FAKE, 64, None) == -2    # cols 0
-    assert f(FAKE, -2, 64, None, None, FAKE, FAKE, FAKE, FAKE, 64, None) == -2  # rows < 0
-    assert f(None, 4, 64, None, None, FAKE, FAKE, FAKE, FAKE, 64, None) == -1
-    assert f(FAKE, 4, 64, None, None, FAKE, FAKE, None, FAKE, 64, None) == -1
-    assert f(FAKE, 4, 64, None, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -3
-    assert f(FAKE, 4, 64, None, None, FAKE, FAKE, FAKE, None, 64, None) == -1   # workspace NULL
+    assert f(FAKE, 4, 48, None, None, 0, FAKE, FAKE, FAKE, FAKE, 64, None) == -2   # cols % 32
+    assert f(FAKE, 4, 0, None, None, 0, FAKE, FAKE, FAKE, FAKE, 64, None) == -2    # cols 0
+    assert f(FAKE, -2, 64, None, None, 0, FAKE, FAKE, FAKE, FAKE, 64, None) == -2  # rows < 0
+    assert f(FAKE, 4, 64, None, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 64, None) == -2   # amax_in_count 0
+    assert f(None, 4, 64, None, None, 0, FAKE, FAKE, FAKE, FAKE, 64, None) == -1
+    assert f(FAKE, 4, 64, None, None, 0, FAKE, FAKE, None, FAKE, 64, None) == -1
+    assert f(FAKE, 4, 64, None, None, 0, FAKE, FAKE, FAKE, FAKE, 0, None) == -3
+    assert f(FAKE, 4, 64, None, None, 0, FAKE, FAKE, FAKE, None, 64, None) == -1   # workspace NULL
 
 
 def test_gemm_rejects_bad_args(lib):
     l1, l2 = lib.moe_grouped_gemm_l1_silu, lib.moe_grouped_gemm_l2
     p10 = [FAKE] * 10
-    assert l1(*p10, 8, 200, 128, 64, FAKE, FAKE, None) == -2      # H not a multiple of 128
+    assert l1(*p10, 8, 384, 128, 64, FAKE, FAKE, None) == -2      # H not a multiple of 256
     assert l1(*p10, 8, 256, 96, 64, FAKE, FAKE, None) == -2       # I not a multiple of 128
     assert l1(*p10, 0, 256, 128, 64, FAKE, FAKE, None) == -2      # E < 1
     assert l1(*p10, 8, 256, 128, -1, FAKE, FAKE, None) == -2      # M_cap < 0
@@ -94,6 +100,7 @@ def test_gemm_rejects_bad_args(lib):
     assert l1(None, *p10[1:], 8, 256, 128, 64, FAKE, FAKE, None) == -1
     p9 = [FAKE] * 9
     assert l2(*p9, 8, 256, 100, 64, FAKE, None) == -2
+    assert l2(*p9, 8, 128, 128, 64, FAKE, None) == -2
     assert l2(*p9, 8, 256, 128, 64, None, None) == -1
 
 

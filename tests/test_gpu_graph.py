@@ -1,0 +1,37 @@
+"""HIP-graph capture of one layer forward: every replay equals the eager result bit for bit,
+with eager work and synchronizations between replays (the benchmark replays captured steps)."""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_block_scaled_top_amd import layer, synth
+
+from gpu_util import DEV, make_setup, np_i32
+
+pytestmark = pytest.mark.gpu
+
+MID = synth.Workload("mid_zipf_e24", 32, 4, 512, 256, (300,), 0, 24, 1, zipf=True)
+
+
+@pytest.mark.parametrize("wl,T", [(MID, 300), (synth.WORKLOADS[1], 8)], ids=["mid", "decode_t8"])
+def test_graph_replays_match_eager(wl, T):
+    s = make_setup(wl, T)
+    x, ids, wts = s.dev_inputs()
+    L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
+                       expert_begin=wl.expert_begin, device=DEV)
+    L.forward(x, ids, wts, s.gpu_w)
+    torch.cuda.synchronize()
+    eager = np_i32(L.out[:T].view(torch.int16)).copy()
+    eager_h = np_i32(L.h[:L.M_cap].view(torch.int16)).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.forward(x, ids, wts, s.gpu_w)
+    for r in range(4):
+        L.out.fill_(0x7FC0)   # eager work between replays: poison outputs
+        L.h_amax.fill_(123.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np_i32(L.out[:T].view(torch.int16)), eager), r
+        valid = np_i32(L.row_token[:L.M_cap]) >= 0
+        assert np.array_equal(np_i32(L.h[:L.M_cap].view(torch.int16))[valid], eager_h[valid]), r

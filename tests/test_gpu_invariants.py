@@ -66,7 +66,7 @@ def test_deterministic_across_runs():
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-@pytest.mark.parametrize("bm", [16, 128])
+@pytest.mark.parametrize("bm", [16, 256])
 def test_block_m_override_changes_speed_only(bm):
     s = mid()
     auto = run_gpu(s)

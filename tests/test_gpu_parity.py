@@ -52,7 +52,7 @@ def check_tables(L, ref):
     counts = ref["counts"]
     assert np.all((bm == 0) == (counts == 0))
     small = np.where(bm == 16, (counts + 15) // 16, 0)
-    large = np.where(bm == 128, (counts + 127) // 128, 0)
+    large = np.where(bm == 256, (counts + 255) // 256, 0)
     assert np.array_equal(sched[4 + E:5 + 2 * E], np.concatenate([[0], np.cumsum(small)]))
     assert np.array_equal(sched[5 + 2 * E:6 + 3 * E], np.concatenate([[0], np.cumsum(large)]))
     assert sched[1] == small.sum() and sched[2] == large.sum()
@@ -85,7 +85,7 @@ def test_layer_end_to_end_and_stages(wl, T):
     h = bf16_t2np(L.h[:L.M_cap])
     err_h = rel_frob(h[valid], ref["h"][valid])
     # the L1 amax is the max over the rows the kernel wrote
-    assert L.h_amax.item() == np.abs(h[valid]).max()
+    assert L.h_amax.max().item() == np.abs(h[valid]).max()
     log(f"[l1] rel_frob={err_h:.2e}")
     assert err_h <= STAGE_TOL
     # end to end
