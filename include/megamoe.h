@@ -155,6 +155,11 @@ int32_t nvfp4_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, const
  * w13_codes/w13_scales/w13_gs   [E, 2I, H/2], [E, 2I, H/16], [E].
  * E, H, I      E as given to moe_route_permute; H a multiple of 256, I a multiple of 128.
  * M_cap        rows of h: megamoe_row_capacity(T, k, E, P).
+ * block_m_override  the value given to moe_route_permute (0, 16 or 256).
+ * max_rows_per_expert  a bound on counts[e] known to the caller, or 0 if none.  T is always one
+ *              (a token picks each expert at most once).  With block_m_override 0 and a bound of
+ *              at most 16, every expert uses 16-row tiles and the 256-row tile kernel is not
+ *              launched (one launch fewer at decode).  A wrong bound gives wrong results.
  * h_bf16       bf16 [M_cap, I].   h_amax_parts float [MEGAMOE_L1_AMAX_PARTS].
  * ---------------------------------------------------------------------------------------- */
 int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
@@ -162,6 +167,7 @@ int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales
                                  const int32_t* counts, const int32_t* sched,
                                  const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
                                  int32_t E, int32_t H, int32_t I, int64_t M_cap,
+                                 int32_t block_m_override, int32_t max_rows_per_expert,
                                  void* h_bf16, float* h_amax_parts, void* stream);
 
 /* ------------------------------------------------------------------------------------------
@@ -175,12 +181,14 @@ int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales
  * h_codes/h_scales/h_gs   NVFP4 h [M_cap, I/2], [M_cap, I/16], [1] (from nvfp4_quantize_act).
  * padded_offsets, counts, sched   as written by moe_route_permute.
  * w2_codes/w2_scales/w2_gs   [E, H, I/2], [E, H, I/16], [E].
+ * block_m_override, max_rows_per_expert   as for moe_grouped_gemm_l1_silu.
  * y_bf16       bf16 [M_cap, H].
  * ---------------------------------------------------------------------------------------- */
 int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs,
                             const int32_t* padded_offsets, const int32_t* counts, const int32_t* sched,
                             const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
-                            int32_t E, int32_t H, int32_t I, int64_t M_cap, void* y_bf16, void* stream);
+                            int32_t E, int32_t H, int32_t I, int64_t M_cap, int32_t block_m_override,
+                            int32_t max_rows_per_expert, void* y_bf16, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * moe_combine - routing-weighted combine of the expert outputs back into token order.

@@ -33,6 +33,17 @@ int32_t check_device() {
 
 int32_t launch_status(hipError_t e) { return e == hipSuccess ? MEGAMOE_OK : MEGAMOE_ERR_LAUNCH; }
 
+// Tile classes a GEMM call may contain: route assigns 16-row tiles to experts with at most
+// kSmallClassMaxTokens tokens unless block_m_override forces one height for all.
+bool classes_of(int32_t block_m_override, int32_t max_rows_per_expert, GemmClasses* c) {
+  if (block_m_override != 0 && block_m_override != kBlockMSmall && block_m_override != kBlockMLarge) return false;
+  if (max_rows_per_expert < 0) return false;
+  if (block_m_override == kBlockMSmall) *c = {true, false};
+  else if (block_m_override == kBlockMLarge) *c = {false, true};
+  else *c = {true, !(max_rows_per_expert > 0 && max_rows_per_expert <= kSmallClassMaxTokens)};
+  return true;
+}
+
 bool gemm_shape_ok(int32_t E, int32_t H, int32_t I, int64_t M_cap) {
   return E >= 1 && E <= MEGAMOE_MAX_EXPERTS && H >= 256 && I >= 128 && H % 256 == 0 && I % 128 == 0 &&
          M_cap >= 0 && M_cap < (int64_t)1 << 31;
@@ -108,32 +119,38 @@ int32_t nvfp4_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, const
 int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
                                  const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
                                  const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
-                                 const float* w13_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap, void* h_bf16,
+                                 const float* w13_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap,
+                                 int32_t block_m_override, int32_t max_rows_per_expert, void* h_bf16,
                                  float* h_amax_parts, void* stream) {
-  if (!gemm_shape_ok(E, H, I, M_cap)) return MEGAMOE_ERR_SHAPE;
+  GemmClasses cls;
+  if (!gemm_shape_ok(E, H, I, M_cap) || !classes_of(block_m_override, max_rows_per_expert, &cls))
+    return MEGAMOE_ERR_SHAPE;
   if (!x_codes || !x_scales || !x_gs || !row_token || !padded_offsets || !counts || !sched || !w13_codes ||
       !w13_scales || !w13_gs || !h_bf16 || !h_amax_parts)
     return MEGAMOE_ERR_NULL;
   const int32_t dev = check_device();
   if (dev != MEGAMOE_OK) return dev;
   GemmArgs a{x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
-             E, H, I, h_bf16, h_amax_parts};
-  return launch_status(launch_gemm_l1(a, static_cast<hipStream_t>(stream)));
+             E, H, I, h_bf16, h_amax_parts, 0};
+  return launch_status(launch_gemm_l1(a, cls, static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs,
                             const int32_t* padded_offsets, const int32_t* counts, const int32_t* sched,
                             const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs, int32_t E, int32_t H,
-                            int32_t I, int64_t M_cap, void* y_bf16, void* stream) {
-  if (!gemm_shape_ok(E, H, I, M_cap)) return MEGAMOE_ERR_SHAPE;
+                            int32_t I, int64_t M_cap, int32_t block_m_override, int32_t max_rows_per_expert,
+                            void* y_bf16, void* stream) {
+  GemmClasses cls;
+  if (!gemm_shape_ok(E, H, I, M_cap) || !classes_of(block_m_override, max_rows_per_expert, &cls))
+    return MEGAMOE_ERR_SHAPE;
   if (!h_codes || !h_scales || !h_gs || !padded_offsets || !counts || !sched || !w2_codes || !w2_scales || !w2_gs ||
       !y_bf16)
     return MEGAMOE_ERR_NULL;
   const int32_t dev = check_device();
   if (dev != MEGAMOE_OK) return dev;
   GemmArgs a{h_codes, h_scales, h_gs, nullptr, padded_offsets, counts, sched, w2_codes, w2_scales, w2_gs,
-             E, I, H, y_bf16, nullptr};
-  return launch_status(launch_gemm_l2(a, static_cast<hipStream_t>(stream)));
+             E, I, H, y_bf16, nullptr, 0};
+  return launch_status(launch_gemm_l2(a, cls, static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_combine(const void* y_bf16, const int32_t* token_rows, const float* topk_weights, int32_t T, int32_t k,

@@ -90,24 +90,40 @@ __device__ __forceinline__ float silu_f32(float g) {
 }
 
 // ============================================================================================
-// Small class: 16 rows x 32 weight rows per tile, K split over 4 waves.
-// L1: weight rows {nt*16 + r (gate), I + nt*16 + r (up)} -> 16 h columns.  L2: rows nt*32 + r.
+// Small class: 16 token rows x 16 weight rows per tile (one MFMA column block), K split over the 4
+// waves of a workgroup.  L1: MFMA columns 0-7 are gate rows nt*8.., columns 8-15 the matching up
+// rows I + nt*8.., paired after the reduction with a lane shuffle -> 8 h columns.  L2: weight rows
+// nt*16..+16 -> 16 y columns.  Small tiles give many tiles per expert, so the persistent grid
+// stays balanced when only a few experts are active.
+//
+// Weight streaming: at decode an expert holds 1-2 tokens, so each weight byte feeds one 16-row
+// MFMA block and the kernel is bound by HBM.  Each wave walks its quarter of K in 128-element
+// chunks with a 4-deep register ring (loads for chunks c+1..c+4 in flight while chunk c is
+// decoded and multiplied); the partial sums of the 4 waves are added in a fixed order through
+// LDS (deterministic).
 // ============================================================================================
-constexpr int kSmallBn = 32;
 constexpr int kChunk = 128;
-constexpr int kLargeGrid = 256;   // large class: one workgroup per CU (LDS ~139 KB)
-constexpr int kSmallGrid = MEGAMOE_L1_AMAX_PARTS - kLargeGrid;
-static_assert(kSmallGrid % kXcds == 0 && kSmallGrid > 0, "grid split");
+constexpr int kSmallDepth = 4;
+constexpr int kSmallWavesPerSimd = 4;
+constexpr int kLargeGrid = 256;   // large class: one workgroup per CU (LDS ~148 KB)
+constexpr int kSmallGrid = MEGAMOE_L1_AMAX_PARTS - kLargeGrid;   // small class: resident workgroups
+static_assert(kSmallGrid == 256 * kSmallWavesPerSimd, "small grid = workgroups resident at once");
+static_assert(kSmallGrid % kXcds == 0, "grid split");
+
+struct SmallChunk {
+  u32x4 a, b;
+  uint32_t as, bs;
+};
 
 template <bool kL1>
-__global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kGemmThreads, kSmallWavesPerSimd) void gemm_small_kernel(GemmArgs p) {
   __shared__ int s_pref[kMaxExperts + 1];
-  __shared__ f32x4 s_red[4][2][kWave];
+  __shared__ f32x4 s_red[4][kWave];
   const int E = p.E;
   const int32_t* __restrict__ sched = p.sched;
   for (int j = threadIdx.x; j <= E; j += blockDim.x) s_pref[j] = sched[sched_pref_small(E) + j];
   __syncthreads();
-  const int ntn = kL1 ? p.N / 16 : p.N / kSmallBn;
+  const int ntn = kL1 ? p.N / 8 : p.N / 16;
   const int total = s_pref[E] * ntn;
   const int K = p.K, Kh = K / 2, Ks = K / 16;
   const int Nw = kL1 ? 2 * p.N : p.N;  // weight rows per expert
@@ -126,90 +142,73 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs p) {
     if (kL1) a_row = a_ok ? p.row_token[a_row] : 0;
     const uint8_t* __restrict__ a_c = p.a_codes + a_row * Kh + g * 16;
     const uint8_t* __restrict__ a_s = p.a_scales + a_row * Ks + g * 2;
-    int64_t b_row0, b_row1;
-    if (kL1) {
-      b_row0 = (int64_t)ti.e * Nw + ti.nt * 16 + r16;
-      b_row1 = b_row0 + p.N;
-    } else {
-      b_row0 = (int64_t)ti.e * Nw + ti.nt * kSmallBn + r16;
-      b_row1 = b_row0 + 16;
-    }
-    const uint8_t* __restrict__ b0_c = p.w_codes + b_row0 * Kh + g * 16;
-    const uint8_t* __restrict__ b1_c = p.w_codes + b_row1 * Kh + g * 16;
-    const uint8_t* __restrict__ b0_s = p.w_scales + b_row0 * Ks + g * 2;
-    const uint8_t* __restrict__ b1_s = p.w_scales + b_row1 * Ks + g * 2;
+    int64_t b_row;
+    if (kL1) b_row = (int64_t)ti.e * Nw + (r16 < 8 ? ti.nt * 8 + r16 : p.N + ti.nt * 8 + r16 - 8);
+    else b_row = (int64_t)ti.e * Nw + ti.nt * 16 + r16;
+    const uint8_t* __restrict__ b_c = p.w_codes + b_row * Kh + g * 16;
+    const uint8_t* __restrict__ b_s = p.w_scales + b_row * Ks + g * 2;
 
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    // Register double-buffering of the next chunk's raw codes and scales.
-    u32x4 ac = {0u, 0u, 0u, 0u}, bc0 = {0u, 0u, 0u, 0u}, bc1 = {0u, 0u, 0u, 0u};
-    uint32_t as = 0, bs0 = 0, bs1 = 0;
-    if (c_begin < c_end) {
-      const int64_t off = (int64_t)c_begin * (kChunk / 2);
-      const int64_t soff = (int64_t)c_begin * (kChunk / 16);
+    auto load = [&](int c, SmallChunk& d) {
+      const int64_t off = (int64_t)c * (kChunk / 2), soff = (int64_t)c * (kChunk / 16);
       if (a_ok) {
-        ac = *reinterpret_cast<const u32x4*>(a_c + off);
-        as = *reinterpret_cast<const uint16_t*>(a_s + soff);
+        d.a = *reinterpret_cast<const u32x4*>(a_c + off);
+        d.as = *reinterpret_cast<const uint16_t*>(a_s + soff);
+      } else {
+        d.a = u32x4{0u, 0u, 0u, 0u};
+        d.as = 0u;
       }
-      bc0 = *reinterpret_cast<const u32x4*>(b0_c + off);
-      bc1 = *reinterpret_cast<const u32x4*>(b1_c + off);
-      bs0 = *reinterpret_cast<const uint16_t*>(b0_s + soff);
-      bs1 = *reinterpret_cast<const uint16_t*>(b1_s + soff);
-    }
-    for (int c = c_begin; c < c_end; ++c) {
-      const u32x4 cac = ac, cb0 = bc0, cb1 = bc1;
-      const uint32_t cas = as, cbs0 = bs0, cbs1 = bs1;
-      if (c + 1 < c_end) {
-        const int64_t off = (int64_t)(c + 1) * (kChunk / 2);
-        const int64_t soff = (int64_t)(c + 1) * (kChunk / 16);
-        if (a_ok) {
-          ac = *reinterpret_cast<const u32x4*>(a_c + off);
-          as = *reinterpret_cast<const uint16_t*>(a_s + soff);
-        }
-        bc0 = *reinterpret_cast<const u32x4*>(b0_c + off);
-        bc1 = *reinterpret_cast<const u32x4*>(b1_c + off);
-        bs0 = *reinterpret_cast<const uint16_t*>(b0_s + soff);
-        bs1 = *reinterpret_cast<const uint16_t*>(b1_s + soff);
-      }
-      const f16x2 sa = e4m3x2_to_f16(cas, false);
-      const f16x2 sb0 = e4m3x2_to_f16(cbs0, false);
-      const f16x2 sb1 = e4m3x2_to_f16(cbs1, false);
+      d.b = *reinterpret_cast<const u32x4*>(b_c + off);
+      d.bs = *reinterpret_cast<const uint16_t*>(b_s + soff);
+    };
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const SmallChunk& d) {
+      const f16x2 sa = e4m3x2_to_f16(d.as, false);
+      const f16x2 sb = e4m3x2_to_f16(d.bs, false);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f16x8 a = decode8(cac[j], j < 2 ? bcast_lo(sa) : bcast_hi(sa));
-        const f16x8 w0 = decode8(cb0[j], j < 2 ? bcast_lo(sb0) : bcast_hi(sb0));
-        const f16x8 w1 = decode8(cb1[j], j < 2 ? bcast_lo(sb1) : bcast_hi(sb1));
-        acc0 = mfma16(a, w0, acc0);
-        acc1 = mfma16(a, w1, acc1);
+        const f16x8 a = decode8(d.a[j], j < 2 ? bcast_lo(sa) : bcast_hi(sa));
+        const f16x8 w = decode8(d.b[j], j < 2 ? bcast_lo(sb) : bcast_hi(sb));
+        acc = mfma16(a, w, acc);
+      }
+    };
+    // 4-deep register ring over this wave's chunks; slot k always holds chunks c with
+    // (c - c_begin) % 4 == k, so every slot has fixed registers after unrolling.
+    SmallChunk ring[kSmallDepth];
+#pragma unroll
+    for (int k = 0; k < kSmallDepth; ++k)
+      if (c_begin + k < c_end) load(c_begin + k, ring[k]);
+    for (int c = c_begin; c < c_end; c += kSmallDepth) {
+#pragma unroll
+      for (int k = 0; k < kSmallDepth; ++k) {
+        if (c + k < c_end) {
+          compute(ring[k]);
+          if (c + k + kSmallDepth < c_end) load(c + k + kSmallDepth, ring[k]);
+        }
       }
     }
     // Fixed-order reduction of the 4 K-partials.
-    s_red[wave][0][lane] = acc0;
-    s_red[wave][1][lane] = acc1;
+    s_red[wave][lane] = acc;
     __syncthreads();
     if (wave == 0) {
-      f32x4 r0 = s_red[0][0][lane], r1 = s_red[0][1][lane];
+      f32x4 r = s_red[0][lane];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        r0 += s_red[w][0][lane];
-        r1 += s_red[w][1][lane];
-      }
+      for (int w = 1; w < 4; ++w) r += s_red[w][lane];
       const float inv = (float)(1.0 / ((double)gs_a * (double)p.w_gs[ti.e]));
       uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = 4 * g + q;
-        if (r < ti.rows_left) {
-          const int64_t orow = (int64_t)(ti.row0 + r) * p.N;
-          if (kL1) {
-            const float gt = r0[q] * inv, up = r1[q] * inv;
+        const int row = 4 * g + q;
+        if (kL1) {
+          const float up_raw = __shfl(r[q], lane + 8, kWave);  // column c+8 holds the up row of c
+          if (r16 < 8 && row < ti.rows_left) {
+            const float gt = r[q] * inv, up = up_raw * inv;
             const uint32_t hb = f32_to_bf16_bits(silu_f32(gt) * up);
-            out[orow + ti.nt * 16 + r16] = (uint16_t)hb;
+            out[(int64_t)(ti.row0 + row) * p.N + ti.nt * 8 + r16] = (uint16_t)hb;
             const uint32_t mag = hb & 0x7FFFu;
             amax_bits = amax_bits > mag ? amax_bits : mag;
-          } else {
-            out[orow + ti.nt * kSmallBn + r16] = (uint16_t)f32_to_bf16_bits(r0[q] * inv);
-            out[orow + ti.nt * kSmallBn + 16 + r16] = (uint16_t)f32_to_bf16_bits(r1[q] * inv);
           }
+        } else if (row < ti.rows_left) {
+          out[(int64_t)(ti.row0 + row) * p.N + ti.nt * 16 + r16] = (uint16_t)f32_to_bf16_bits(r[q] * inv);
         }
       }
     }
@@ -219,6 +218,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs p) {
     // only wave 0 wrote h; its max is the workgroup's
     amax_bits = wave_max_u32(amax_bits);
     if (threadIdx.x == 0) p.amax_out[kLargeGrid + blockIdx.x] = bf16_bits_to_f32(amax_bits);
+    if (p.clear_other && threadIdx.x == 0 && (int)blockIdx.x < kLargeGrid) p.amax_out[blockIdx.x] = 0.0f;
   }
 }
 
@@ -528,21 +528,31 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
       uint32_t m = s_amax[0];
       for (int w = 1; w < kGemmThreads / kWave; ++w) m = m > s_amax[w] ? m : s_amax[w];
       p.amax_out[blockIdx.x] = bf16_bits_to_f32(m);
+      if (p.clear_other)
+        for (int j = (int)blockIdx.x; j < kSmallGrid; j += kLargeGrid) p.amax_out[kLargeGrid + j] = 0.0f;
     }
   }
 }
 
+// Launch the tile classes the call may contain.  When only one class runs, its kernel also
+// zeroes the other class's amax slots (clear_other), so every slot is written on every call.
 template <bool kL1>
-static hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(gemm_large_kernel<kL1>, dim3(kLargeGrid), dim3(kGemmThreads), 0, stream, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gemm_small_kernel<kL1>, dim3(kSmallGrid), dim3(kGemmThreads), 0, stream, a);
-  return hipGetLastError();
+static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
+  a.clear_other = !(c.large && c.small);
+  if (c.large) {
+    hipLaunchKernelGGL(gemm_large_kernel<kL1>, dim3(kLargeGrid), dim3(kGemmThreads), 0, stream, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (c.small) {
+    hipLaunchKernelGGL(gemm_small_kernel<kL1>, dim3(kSmallGrid), dim3(kGemmThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
-hipError_t launch_gemm_l1(const GemmArgs& a, hipStream_t stream) { return launch_gemm<true>(a, stream); }
+hipError_t launch_gemm_l1(const GemmArgs& a, GemmClasses c, hipStream_t stream) { return launch_gemm<true>(a, c, stream); }
 
-hipError_t launch_gemm_l2(const GemmArgs& a, hipStream_t stream) { return launch_gemm<false>(a, stream); }
+hipError_t launch_gemm_l2(const GemmArgs& a, GemmClasses c, hipStream_t stream) { return launch_gemm<false>(a, c, stream); }
 
 }  // namespace megamoe

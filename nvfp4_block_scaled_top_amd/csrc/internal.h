@@ -60,9 +60,14 @@ struct GemmArgs {
   int32_t E, K, N;   // N = output columns: I for L1 (weights have 2I rows), H for L2
   void* out;         // bf16 [M_cap, N]
   float* amax_out;   // L1: per-workgroup max |h| slots [MEGAMOE_L1_AMAX_PARTS]; NULL for L2
+  int clear_other;   // L1: the other tile class is not launched; this kernel zeroes its slots
 };
-hipError_t launch_gemm_l1(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_gemm_l2(const GemmArgs& a, hipStream_t stream);
+// Which tile classes a call may contain, from the routing override and the caller's row bound.
+struct GemmClasses {
+  bool small, large;
+};
+hipError_t launch_gemm_l1(const GemmArgs& a, GemmClasses c, hipStream_t stream);
+hipError_t launch_gemm_l2(const GemmArgs& a, GemmClasses c, hipStream_t stream);
 
 // ---- combine ---------------------------------------------------------------------------------
 hipError_t launch_combine(const uint16_t* y, const int32_t* token_rows, const float* w, int32_t T,

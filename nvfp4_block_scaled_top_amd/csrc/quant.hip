@@ -18,7 +18,8 @@
 //
 // Two kernels: an amax pass writing per-workgroup partial maxima (skipped when the caller passes
 // its own partial maxima in amax_in), then the quantization pass, whose every workgroup reduces
-// the partials itself (no atomics, nothing to reset between calls).
+// the partials itself (no atomics, nothing to reset between calls).  Tensors of up to 2^18
+// elements (decode activations) are done by one workgroup in one launch.
 #include "device_common.h"
 #include "internal.h"
 
@@ -108,6 +109,35 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t xbits, float gs, const fl
   return ((xbits >> 12) & 8u) | mag;
 }
 
+// Quantize one 16-element block b of the tensor (row-major blocks) with global scale gs.
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int64_t b, float gs,
+                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const u32x4 v0 = *reinterpret_cast<const u32x4*>(x + b * 16);
+  const u32x4 v1 = *reinterpret_cast<const u32x4*>(x + b * 16 + 8);
+  uint32_t bmax = bf16_abs_max8(v0);
+  const uint32_t bm1 = bf16_abs_max8(v1);
+  bmax = bmax > bm1 ? bmax : bm1;
+  const double q = ((double)bf16_bits_to_f32(bmax) * (double)gs) / 6.0;
+  const uint32_t sc = e4m3_code_rne(q);
+  const float s = e4m3_value(sc);
+  const float t[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
+  const bool zs = sc == 0;
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w = j < 4 ? v0[j] : v1[j - 4];
+    const uint32_t c0 = e2m1_code(w & 0xFFFFu, gs, t, zs);
+    const uint32_t c1 = e2m1_code(w >> 16, gs, t, zs);
+    out[j >> 2] |= (c0 | (c1 << 4)) << (8 * (j & 3));
+  }
+  *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{out[0], out[1]};
+  scales[b] = (uint8_t)sc;
+}
+
+__device__ __forceinline__ float global_scale_of(float amax) {
+  return amax > 0.0f ? 2688.0f / amax : 1.0f;  // IEEE division (correctly rounded)
+}
+
 __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                               const int32_t* __restrict__ row_valid,
                                                               const float* __restrict__ amax_src, int nparts,
@@ -120,8 +150,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint16_t* __
     am = am > b ? am : b;
   }
   am = block_max_u32(am, red);
-  const float amax = __uint_as_float(am);
-  const float gs = amax > 0.0f ? 2688.0f / amax : 1.0f;  // IEEE division (correctly rounded)
+  const float gs = global_scale_of(__uint_as_float(am));
   if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
 
   const int64_t bpr = cols / 16;
@@ -132,26 +161,38 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint16_t* __
       scales[b] = 0;
       continue;
     }
-    const u32x4 v0 = *reinterpret_cast<const u32x4*>(x + b * 16);
-    const u32x4 v1 = *reinterpret_cast<const u32x4*>(x + b * 16 + 8);
-    uint32_t bmax = bf16_abs_max8(v0);
-    const uint32_t bm1 = bf16_abs_max8(v1);
-    bmax = bmax > bm1 ? bmax : bm1;
-    const double q = ((double)bf16_bits_to_f32(bmax) * (double)gs) / 6.0;
-    const uint32_t sc = e4m3_code_rne(q);
-    const float s = e4m3_value(sc);
-    const float t[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
-    const bool zs = sc == 0;
-    uint32_t out[2] = {0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w = j < 4 ? v0[j] : v1[j - 4];
-      const uint32_t c0 = e2m1_code(w & 0xFFFFu, gs, t, zs);
-      const uint32_t c1 = e2m1_code(w >> 16, gs, t, zs);
-      out[j >> 2] |= (c0 | (c1 << 4)) << (8 * (j & 3));
+    quant_block(x, b, gs, codes, scales);
+  }
+}
+
+// Small tensors (decode activations): amax and quantization in one workgroup, one launch.
+constexpr int64_t kQuantSmallElems = 1 << 18;
+
+__global__ __launch_bounds__(kQuantThreads) void quant_small_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                    int64_t cols, const int32_t* __restrict__ row_valid,
+                                                                    uint8_t* __restrict__ codes,
+                                                                    uint8_t* __restrict__ scales,
+                                                                    float* __restrict__ gs_out) {
+  __shared__ uint32_t red[kQuantThreads / kWave];
+  const int64_t nvec = rows * cols / 8;
+  uint32_t m = 0;
+  for (int64_t v = threadIdx.x; v < nvec; v += blockDim.x) {
+    if (row_valid != nullptr && row_valid[(v * 8) / cols] < 0) continue;
+    const uint32_t t = bf16_abs_max8(*reinterpret_cast<const u32x4*>(x + v * 8));
+    m = m > t ? m : t;
+  }
+  m = block_max_u32(m, red);
+  const float gs = global_scale_of(bf16_bits_to_f32(m));
+  if (threadIdx.x == 0) *gs_out = gs;
+  const int64_t bpr = cols / 16;
+  const int64_t nblk = rows * bpr;
+  for (int64_t b = threadIdx.x; b < nblk; b += blockDim.x) {
+    if (row_valid != nullptr && row_valid[b / bpr] < 0) {
+      *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{0u, 0u};
+      scales[b] = 0;
+      continue;
     }
-    *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{out[0], out[1]};
-    scales[b] = (uint8_t)sc;
+    quant_block(x, b, gs, codes, scales);
   }
 }
 
@@ -160,6 +201,11 @@ hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int
                         float* ws, hipStream_t stream) {
   const float* amax_src = amax_in;
   int nparts = amax_in_count;
+  if (amax_in == nullptr && rows * cols <= kQuantSmallElems) {
+    hipLaunchKernelGGL(quant_small_kernel, dim3(1), dim3(kQuantThreads), 0, stream, x, rows, cols, row_valid, codes,
+                       scales, gs);
+    return hipGetLastError();
+  }
   if (amax_in == nullptr) {
     nparts = quant_amax_parts(rows, cols);
     hipLaunchKernelGGL(quant_amax_kernel, dim3(nparts), dim3(kQuantThreads), 0, stream, x, rows, cols, row_valid, ws);

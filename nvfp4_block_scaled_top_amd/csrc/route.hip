@@ -6,7 +6,8 @@
 // ("Test Plan" Phase 2).  The per-expert tile height follows the tokens per expert, small at
 // decode and large at prefill ("Key References").
 //
-// Three kernels, no atomics on global memory, so the permutation is deterministic:
+// Up to 1024 assignments (decode) one workgroup does everything (route_small_kernel).  Above
+// that, three kernels, no atomics on global memory, so the permutation is deterministic:
 //   1. count:   one workgroup per 1024 assignments builds that chunk's expert histogram (LDS
 //               atomics; counts do not depend on order) and resets row_token to -1;
 //   2. scan:    one workgroup turns the per-chunk histograms into per-chunk bases (a column
@@ -55,21 +56,14 @@ __device__ __forceinline__ int block_incl_scan(int v, int* buf) {
   return r;
 }
 
-__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ ws, int32_t nchunks, int32_t E,
-                                                          int32_t P, int32_t bm_override,
-                                                          int32_t* __restrict__ counts, int32_t* __restrict__ eoff,
-                                                          int32_t* __restrict__ poff, int32_t* __restrict__ sched) {
-  __shared__ int buf[1024];
+// Given each expert's total (thread e holds expert e's count; threads >= E hold 0), write counts,
+// both offset arrays and the tile table.  Called by all 1024 threads of the block.
+// If s_poff is given, padded_offsets[0..E) are also left there (LDS) for the caller.
+__device__ void finish_tables(int total, int32_t E, int32_t P, int32_t bm_override, int* buf,
+                              int32_t* __restrict__ counts, int32_t* __restrict__ eoff,
+                              int32_t* __restrict__ poff, int32_t* __restrict__ sched, int* s_poff) {
   const int e = threadIdx.x;
-  int total = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = ws[(int64_t)c * E + e];
-      ws[(int64_t)c * E + e] = total;
-      total += v;
-    }
-    counts[e] = total;
-  }
+  if (e < E) counts[e] = total;
   int bm = 0, small_tiles = 0, large_tiles = 0;
   int padded = 0;
   if (e < E && total > 0) {
@@ -83,6 +77,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
   const int inc_pad = block_incl_scan(padded, buf);
   const int inc_small = block_incl_scan(small_tiles, buf);
   const int inc_large = block_incl_scan(large_tiles, buf);
+  if (s_poff != nullptr && e < E) s_poff[e] = inc_pad - padded;
   if (e < E) {
     eoff[e + 1] = inc_cnt;
     poff[e + 1] = inc_pad;
@@ -104,6 +99,38 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
   }
 }
 
+__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ ws, int32_t nchunks, int32_t E,
+                                                          int32_t P, int32_t bm_override,
+                                                          int32_t* __restrict__ counts, int32_t* __restrict__ eoff,
+                                                          int32_t* __restrict__ poff, int32_t* __restrict__ sched) {
+  __shared__ int buf[1024];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = ws[(int64_t)c * E + e];
+      ws[(int64_t)c * E + e] = total;
+      total += v;
+    }
+  }
+  finish_tables(total, E, P, bm_override, buf, counts, eoff, poff, sched, nullptr);
+}
+
+// Rank of this lane's expert among the lanes of its wave holding the same expert (values 0..E;
+// E is the "not local" sentinel), and the number of such lanes.
+__device__ __forceinline__ void wave_rank(int e, int E, int& rank, int& count) {
+  uint64_t same = __ballot(1);
+  for (int b = 0; (1 << b) <= E; ++b) {
+    const int bit = (e >> b) & 1;
+    const uint64_t m1 = __ballot(bit);
+    same &= bit ? m1 : ~m1;
+  }
+  const int lane = lane_id();
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  rank = __popcll(same & below);
+  count = __popcll(same);
+}
+
 __global__ __launch_bounds__(kRouteChunk) void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t n,
                                                                     int32_t k, int32_t e0, int32_t E,
                                                                     const int32_t* __restrict__ ws,
@@ -120,17 +147,10 @@ __global__ __launch_bounds__(kRouteChunk) void route_scatter_kernel(const int32_
     const int64_t v = (int64_t)ids[i] - e0;
     if (v >= 0 && v < E) e = (int)v;
   }
-  // Lanes holding the same expert: intersect ballots over the bits of e (values 0..E).
-  uint64_t same = __ballot(1);
-  for (int b = 0; (1 << b) <= E; ++b) {
-    const int bit = (e >> b) & 1;
-    const uint64_t m1 = __ballot(bit);
-    same &= bit ? m1 : ~m1;
-  }
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  const int rank = __popcll(same & below);
-  if (e < E && rank == 0) wcnt[wave * E + e] = __popcll(same);
+  int rank, cnt;
+  wave_rank(e, E, rank, cnt);
+  const int wave = threadIdx.x / kWave;
+  if (e < E && rank == 0) wcnt[wave * E + e] = cnt;
   __syncthreads();
   if (i < n) {
     int row = -1;
@@ -144,24 +164,71 @@ __global__ __launch_bounds__(kRouteChunk) void route_scatter_kernel(const int32_
   }
 }
 
+// Whole routing step in one workgroup when T*k <= kRouteChunk (decode): count, scan and scatter
+// with barriers in between instead of three launches.
+__global__ __launch_bounds__(kRouteChunk) void route_small_kernel(const int32_t* __restrict__ ids, int32_t n, int32_t k,
+                                                                  int32_t e0, int32_t E, int32_t P, int32_t bm_override,
+                                                                  int32_t* __restrict__ counts, int32_t* __restrict__ eoff,
+                                                                  int32_t* __restrict__ poff, int32_t* __restrict__ row_token,
+                                                                  int64_t M_cap, int32_t* __restrict__ token_rows,
+                                                                  int32_t* __restrict__ sched) {
+  constexpr int kWaves = kRouteChunk / kWave;
+  extern __shared__ int32_t wcnt[];  // [kWaves][E]
+  __shared__ int buf[kRouteChunk];
+  __shared__ int s_poff[kMaxExperts];
+  for (int j = threadIdx.x; j < kWaves * E; j += blockDim.x) wcnt[j] = 0;
+  for (int64_t r = threadIdx.x; r < M_cap; r += blockDim.x) row_token[r] = -1;
+  __syncthreads();
+  const int i = threadIdx.x;
+  int e = E;
+  if (i < n) {
+    const int64_t v = (int64_t)ids[i] - e0;
+    if (v >= 0 && v < E) e = (int)v;
+  }
+  int rank, cnt;
+  wave_rank(e, E, rank, cnt);
+  const int wave = threadIdx.x / kWave;
+  if (e < E && rank == 0) wcnt[wave * E + e] = cnt;
+  __syncthreads();
+  int total = 0;
+  if ((int)threadIdx.x < E)
+    for (int w = 0; w < kWaves; ++w) total += wcnt[w * E + threadIdx.x];
+  finish_tables(total, E, P, bm_override, buf, counts, eoff, poff, sched, s_poff);
+  __syncthreads();  // s_poff and the -1 fill of row_token are complete
+  if (i < n) {
+    int row = -1;
+    if (e < E) {
+      int base = 0;
+      for (int w = 0; w < wave; ++w) base += wcnt[w * E + e];
+      row = s_poff[e] + base + rank;
+      row_token[row] = i / k;
+    }
+    token_rows[i] = row;
+  }
+}
+
 hipError_t launch_route(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e0, int32_t E, int32_t P,
                         int32_t block_m_override, int32_t* counts, int32_t* eoff, int32_t* poff,
                         int32_t* row_token, int64_t M_cap, int32_t* token_rows, int32_t* sched,
                         int32_t* ws, hipStream_t stream) {
   const int64_t n = (int64_t)T * k;
+  const size_t wcnt_bytes = (size_t)(kRouteChunk / kWave) * E * sizeof(int32_t);
+  if (n <= kRouteChunk) {
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kRouteChunk), wcnt_bytes, stream, topk_ids, (int32_t)n, k, e0,
+                       E, P, block_m_override, counts, eoff, poff, row_token, M_cap, token_rows, sched);
+    return hipGetLastError();
+  }
   const int32_t nchunks = (int32_t)((n + kRouteChunk - 1) / kRouteChunk);
-  const int grid1 = nchunks > 0 ? nchunks : 1;
-  hipLaunchKernelGGL(route_count_kernel, dim3(grid1), dim3(kRouteChunk), (size_t)E * sizeof(int32_t), stream,
+  hipLaunchKernelGGL(route_count_kernel, dim3(nchunks), dim3(kRouteChunk), (size_t)E * sizeof(int32_t), stream,
                      topk_ids, n, e0, E, nchunks, ws, row_token, M_cap);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, ws, nchunks, E, P, block_m_override,
                      counts, eoff, poff, sched);
   err = hipGetLastError();
-  if (err != hipSuccess || nchunks == 0) return err;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(kRouteChunk),
-                     (size_t)(kRouteChunk / kWave) * E * sizeof(int32_t), stream, topk_ids, n, k, e0, E, ws, poff,
-                     row_token, token_rows);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(kRouteChunk), wcnt_bytes, stream, topk_ids, n, k, e0, E,
+                     ws, poff, row_token, token_rows);
   return hipGetLastError();
 }
 

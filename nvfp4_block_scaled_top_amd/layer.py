@@ -111,7 +111,8 @@ class MoELayer:
     def l1(self, w: MoEWeights, stream=None) -> None:
         mm.moe_grouped_gemm_l1_silu(self.x_codes, self.x_scales, self.x_gs, self.row_token, self.padded_offsets,
                                     self.counts, self.sched, w.w13_codes, w.w13_scales, w.w13_gs,
-                                    self._rows(self.h, self.M_cap), self.h_amax, stream=stream)
+                                    self._rows(self.h, self.M_cap), self.h_amax, self.block_m_override,
+                                    self.T, stream=stream)
 
     def quantize_h(self, stream=None) -> None:
         mm.nvfp4_quantize_act(self._rows(self.h, self.M_cap), self._rows(self.h_codes, self.M_cap),
@@ -120,7 +121,8 @@ class MoELayer:
 
     def l2(self, w: MoEWeights, stream=None) -> None:
         mm.moe_grouped_gemm_l2(self.h_codes, self.h_scales, self.h_gs, self.padded_offsets, self.counts, self.sched,
-                               w.w2_codes, w.w2_scales, w.w2_gs, self._rows(self.y, self.M_cap), stream=stream)
+                               w.w2_codes, w.w2_scales, w.w2_gs, self._rows(self.y, self.M_cap),
+                               self.block_m_override, self.T, stream=stream)
 
     def combine(self, topk_weights: torch.Tensor, stream=None) -> None:
         mm.moe_combine(self._rows(self.y, self.M_cap), self._rows(self.token_rows, self.T * self.k), topk_weights,

@@ -37,8 +37,9 @@ SIGNATURES = {
     "megamoe_quant_workspace_bytes": (_SZ, [_I64, _I64]),
     "moe_route_permute": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
-    "moe_grouped_gemm_l1_silu": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P]),
-    "moe_grouped_gemm_l2": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P]),
+    "moe_grouped_gemm_l1_silu": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
+                                        _P, _P, _P]),
+    "moe_grouped_gemm_l2": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
 }
 
@@ -131,24 +132,26 @@ def nvfp4_quantize_act(x_bf16, codes, scales, global_scale, workspace=None, row_
 
 
 def moe_grouped_gemm_l1_silu(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes,
-                             w13_scales, w13_gs, h_bf16, h_amax_parts, stream=None):
+                             w13_scales, w13_gs, h_bf16, h_amax_parts, block_m_override=0, max_rows_per_expert=0,
+                             stream=None):
     E, I2, Hh = w13_codes.shape
     M_cap = h_bf16.shape[0]
     if h_amax_parts.numel() < L1_AMAX_PARTS:
         raise MegaMoEError(f"h_amax_parts needs {L1_AMAX_PARTS} floats")
     _check("moe_grouped_gemm_l1_silu", lib().moe_grouped_gemm_l1_silu(
         _ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts), _ptr(sched),
-        _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), E, 2 * Hh, I2 // 2, M_cap, _ptr(h_bf16), _ptr(h_amax_parts),
-        _stream(stream)))
+        _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), E, 2 * Hh, I2 // 2, M_cap, block_m_override,
+        max_rows_per_expert, _ptr(h_bf16), _ptr(h_amax_parts), _stream(stream)))
 
 
 def moe_grouped_gemm_l2(h_codes, h_scales, h_gs, padded_offsets, counts, sched, w2_codes, w2_scales, w2_gs, y_bf16,
-                        stream=None):
+                        block_m_override=0, max_rows_per_expert=0, stream=None):
     E, H, Ih = w2_codes.shape
     M_cap = y_bf16.shape[0]
     _check("moe_grouped_gemm_l2", lib().moe_grouped_gemm_l2(
         _ptr(h_codes), _ptr(h_scales), _ptr(h_gs), _ptr(padded_offsets), _ptr(counts), _ptr(sched), _ptr(w2_codes),
-        _ptr(w2_scales), _ptr(w2_gs), E, H, 2 * Ih, M_cap, _ptr(y_bf16), _stream(stream)))
+        _ptr(w2_scales), _ptr(w2_gs), E, H, 2 * Ih, M_cap, block_m_override, max_rows_per_expert, _ptr(y_bf16),
+        _stream(stream)))
 
 
 def moe_combine(y_bf16, token_rows, topk_weights, out_bf16, stream=None):

@@ -92,16 +92,19 @@ def test_quant_rejects_bad_args(lib):
 def test_gemm_rejects_bad_args(lib):
     l1, l2 = lib.moe_grouped_gemm_l1_silu, lib.moe_grouped_gemm_l2
     p10 = [FAKE] * 10
-    assert l1(*p10, 8, 384, 128, 64, FAKE, FAKE, None) == -2      # H not a multiple of 256
-    assert l1(*p10, 8, 256, 96, 64, FAKE, FAKE, None) == -2       # I not a multiple of 128
-    assert l1(*p10, 0, 256, 128, 64, FAKE, FAKE, None) == -2      # E < 1
-    assert l1(*p10, 8, 256, 128, -1, FAKE, FAKE, None) == -2      # M_cap < 0
-    assert l1(*p10, 8, 256, 128, 64, FAKE, None, None) == -1      # h_amax NULL
-    assert l1(None, *p10[1:], 8, 256, 128, 64, FAKE, FAKE, None) == -1
+    assert l1(*p10, 8, 384, 128, 64, 0, 0, FAKE, FAKE, None) == -2      # H not a multiple of 256
+    assert l1(*p10, 8, 256, 96, 64, 0, 0, FAKE, FAKE, None) == -2       # I not a multiple of 128
+    assert l1(*p10, 0, 256, 128, 64, 0, 0, FAKE, FAKE, None) == -2      # E < 1
+    assert l1(*p10, 8, 256, 128, -1, 0, 0, FAKE, FAKE, None) == -2      # M_cap < 0
+    assert l1(*p10, 8, 256, 128, 64, 48, 0, FAKE, FAKE, None) == -2     # unsupported block_m
+    assert l1(*p10, 8, 256, 128, 64, 0, -1, FAKE, FAKE, None) == -2     # negative row bound
+    assert l1(*p10, 8, 256, 128, 64, 0, 0, FAKE, None, None) == -1      # h_amax NULL
+    assert l1(None, *p10[1:], 8, 256, 128, 64, 0, 0, FAKE, FAKE, None) == -1
     p9 = [FAKE] * 9
-    assert l2(*p9, 8, 256, 100, 64, FAKE, None) == -2
-    assert l2(*p9, 8, 128, 128, 64, FAKE, None) == -2
-    assert l2(*p9, 8, 256, 128, 64, None, None) == -1
+    assert l2(*p9, 8, 256, 100, 64, 0, 0, FAKE, None) == -2
+    assert l2(*p9, 8, 128, 128, 64, 0, 0, FAKE, None) == -2
+    assert l2(*p9, 8, 256, 128, 64, 32, 0, FAKE, None) == -2
+    assert l2(*p9, 8, 256, 128, 64, 0, 0, None, None) == -1
 
 
 def test_combine_rejects_bad_args(lib):

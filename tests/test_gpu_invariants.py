@@ -92,3 +92,26 @@ def test_nonlocal_tokens_plus_zero_and_finite():
     if none.any():
         assert np.all(o[none] == 0)
     assert np.isfinite(bf16_t2np(L.out[:L.T])).all()
+
+
+@pytest.mark.parametrize("wl,T", [(synth.WORKLOADS[1], 8), (MID, 300)], ids=["decode_t8", "mid"])
+def test_row_bound_hint_does_not_change_results(wl, T):
+    """The GEMMs' max_rows_per_expert hint (T here, 0 = unknown) only selects which kernels launch."""
+    import torch as _t
+    from nvfp4_block_scaled_top_amd import megamoe as mm
+
+    s = mid() if wl is MID else make_setup(wl, T)
+    L = run_gpu(s)  # the layer passes max_rows_per_expert = T
+    h_hint = np_i32(L.h[:L.M_cap].view(_t.int16)).copy()
+    amax_hint = L.h_amax.max().item()
+    y_hint = np_i32(L.y[:L.M_cap].view(_t.int16)).copy()
+    valid = np_i32(L.row_token[:L.M_cap]) >= 0
+    w = s.gpu_w
+    mm.moe_grouped_gemm_l1_silu(L.x_codes, L.x_scales, L.x_gs, L.row_token, L.padded_offsets, L.counts, L.sched,
+                                w.w13_codes, w.w13_scales, w.w13_gs, L.h[:L.M_cap], L.h_amax, 0, 0)
+    mm.moe_grouped_gemm_l2(L.h_codes, L.h_scales, L.h_gs, L.padded_offsets, L.counts, L.sched, w.w2_codes,
+                           w.w2_scales, w.w2_gs, L.y[:L.M_cap], 0, 0)
+    _t.cuda.synchronize()
+    assert np.array_equal(np_i32(L.h[:L.M_cap].view(_t.int16))[valid], h_hint[valid])
+    assert np.array_equal(np_i32(L.y[:L.M_cap].view(_t.int16))[valid], y_hint[valid])
+    assert L.h_amax.max().item() == amax_hint

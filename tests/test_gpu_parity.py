@@ -118,7 +118,7 @@ def test_stage_inputs_from_oracle(wl, T):
     # S5: L2 on the oracle's quantized h
     y = torch.empty(M, wl.hidden, dtype=torch.int16, device=DEV)
     mm.moe_grouped_gemm_l2(codes, scales, gs, L.padded_offsets, L.counts, L.sched, s.gpu_w.w2_codes,
-                           s.gpu_w.w2_scales, s.gpu_w.w2_gs, y)
+                           s.gpu_w.w2_scales, s.gpu_w.w2_gs, y, max_rows_per_expert=T)
     torch.cuda.synchronize()
     err_y = rel_frob(bf16_t2np(y)[valid], ref["y"][valid])
     log(f"[l2] rel_frob={err_y:.2e}")
