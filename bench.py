@@ -169,6 +169,109 @@ def cpu_baseline(wl, T):
             "seconds": dt}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_l1_entry.txt")
+GEMM_SRC = os.path.join(ROOT, "nvfp4_block_scaled_top_amd", "csrc", "gemm.hip")
+COPY_BYTES = 1 << 30  # the calibration kernel reads and writes this many bytes
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_pass(which: str) -> None:
+    """Launch sequence for the HBM-traffic counters (run under rocprofv3 --pmc FETCH_SIZE or
+    WRITE_SIZE): a plain elementwise copy of COPY_BYTES (torch.neg on float32, the calibration
+    kernel), then two untimed forwards of the workload without graphs."""
+    import torch
+    from nvfp4_block_scaled_top_amd import layer, synth
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    wl = synth.WORKLOADS[3] if which == "prefill" else synth.WORKLOADS[1]
+    T = wl.tokens[0] if which == "prefill" else 8
+    ids, wts = synth.router(wl, T)
+    counts = synth.routing_stats(ids, wl)
+    active = [int(e) for e in np.nonzero(counts)[0]]
+    W = build_weights(wl, active, 1, "cuda")[0]
+    L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
+                       expert_begin=wl.expert_begin)
+    x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).cuda()
+    idd, wtd = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
+    for _ in range(2):
+        L.forward(x, idd, wtd, W)
+    torch.cuda.synchronize()
+    log(f"[traffic-pass] {which} T={T} done")
+
+
+def _counter_medians(path: str, counter: str) -> dict:
+    """Median per-dispatch value of `counter` for each kernel name in a rocprofv3 counter CSV."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            vals.setdefault(name, []).append(float(r["Counter_Value"]))
+    return {k: sorted(v)[len(v) // 2] for k, v in vals.items()}
+
+
+def summarize_traffic(paths: list) -> None:
+    """paths: FETCH_SIZE and WRITE_SIZE counter CSVs for prefill, then the same for decode.
+    Writes TRAFFIC_FILE: HBM bytes per call of moe_grouped_gemm_l1_silu, counter values scaled by
+    what the same counters read for the copy kernel of known size."""
+    out = ["# HBM traffic of moe_grouped_gemm_l1_silu per call (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)",
+           "# Commands, from /tmp with TMPDIR=/tmp, for W in prefill decode and C in FETCH_SIZE WRITE_SIZE:",
+           "#   rocprofv3 --pmc C -f csv -d <out>/pmc_C_W -o p -- python3 bench.py --traffic-pass W",
+           "# then: python3 bench.py --summarize-traffic <prefill FETCH csv> <prefill WRITE csv> "
+           "<decode FETCH csv> <decode WRITE csv>",
+           "# Counter KiB per dispatch (median over dispatches) x factor = bytes, where factor = bytes the",
+           "# copy kernel (torch.neg on 1 GiB of float32) reads or writes / what the counter reads for it.",
+           f"gemm_source_sha256_16: {gemm_source_hash()}"]
+    for which, fpath, wpath in (("prefill", paths[0], paths[1]), ("decode_t8", paths[2], paths[3])):
+        fetch = _counter_medians(fpath, "FETCH_SIZE")
+        write = _counter_medians(wpath, "WRITE_SIZE")
+        copy_k = [k for k in fetch if "neg" in k.lower() or "AUnaryFunctor" in k or "unary" in k.lower()]
+        ck = copy_k[0]
+        f_factor = COPY_BYTES / (fetch[ck] * 1024.0)
+        w_factor = COPY_BYTES / (write[ck] * 1024.0)
+        l1 = [k for k in fetch if "gemm_large_kernel<true" in k or "gemm_small_kernel<true" in k]
+        fb = sum(fetch[k] for k in l1) * 1024.0 * f_factor
+        wb = sum(write.get(k, 0.0) for k in l1) * 1024.0 * w_factor
+        out.append(f"{which}_copy_kernel: {ck}")
+        out.append(f"{which}_copy_fetch_kib: {fetch[ck]:.0f}  (factor {f_factor:.4f})")
+        out.append(f"{which}_copy_write_kib: {write[ck]:.0f}  (factor {w_factor:.4f})")
+        for k in l1:
+            out.append(f"{which}_kernel: {k} fetch_kib {fetch[k]:.0f} write_kib {write.get(k, 0.0):.0f}")
+        out.append(f"{which}_traffic_bytes: {fb + wb:.0f}")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def recorded_traffic(which: str):
+    """Bytes per L1 call recorded in TRAFFIC_FILE, or None if absent or taken on other kernel code."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("gemm_source_sha256_16") != gemm_source_hash():
+            return None
+        return float(kv[f"{which}_traffic_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,7 +281,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--quick", action="store_true", help="prefill only, no CPU baseline")
+    ap.add_argument("--traffic-pass", choices=("prefill", "decode"),
+                    help="launch sequence for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (no timing)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar="CSV",
+                    help="prefill FETCH_SIZE, prefill WRITE_SIZE, decode FETCH_SIZE, decode WRITE_SIZE counter CSVs")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
@@ -190,6 +300,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     megamoe.lib()
     torch.cuda.set_device(0)
+    if args.traffic_pass:
+        traffic_pass(args.traffic_pass)
+        return
 
     pre_wl = synth.WORKLOADS[3]
     T = pre_wl.tokens[0]
@@ -213,7 +326,8 @@ def main():
                 "active_experts": d["active_experts"], "assignments": d["assignments"],
                 "weight_bytes": d["weight_bytes"], "stage_ms": {k: round(v, 5) for k, v in d["stage_ms"].items()},
                 "roofline": {"bound": "hbm", "achieved": round(l1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": round(l1_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                             "frac": round(l1_gbs / PEAK_HBM_GBS, 4),
+                             "traffic": recorded_traffic("decode_t8") if Td == 8 else None,
                              "kernel": "moe_grouped_gemm_l1_silu"},
             }
             log(f"[bench] decode T={Td}: {d['ms_per_step'] * 1e3:.1f} us/step, {gbs:.0f} GB/s")
@@ -245,7 +359,7 @@ def main():
         "mfma_frac": round(tflops / PEAK_FP16_TFLOPS, 4),
         "stage_ms": {k: round(v, 4) for k, v in pre["stage_ms"].items()},
         "roofline": {"bound": "mfma", "achieved": round(l1_tflops, 1), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(l1_tflops / PEAK_FP16_TFLOPS, 4), "traffic": None,
+                     "frac": round(l1_tflops / PEAK_FP16_TFLOPS, 4), "traffic": recorded_traffic("prefill"),
                      "kernel": "moe_grouped_gemm_l1_silu"},
         "decode": decode,
         "cpu_baseline": cpu,

@@ -8,24 +8,24 @@
 // expert's base pointers.
 //
 // Arithmetic.  Both operands are NVFP4 and are decoded exactly to fp16 (e2m1 * e4m3 is always a
-// normal fp16 number), multiplied on the fp16 MFMA (v_mfma_f32_16x16x32_f16) and accumulated in
+// normal fp16 number), multiplied on the fp16 MFMA (16x16x32 in the small class, 32x32x16 in the
+// large class) and accumulated in
 // fp32; the product of the two global scales is divided out in the epilogue.
 //
-// Two tile classes, both persistent over a tile list taken from the routing step's table:
-//  * small (16-row tiles, used for experts with few tokens, e.g. decode): weights are streamed
-//    from HBM straight into registers, 16 B per lane per 128-element chunk of the reduction
-//    dimension; the reduction dimension is split over the 4 waves of a workgroup and the partial
-//    sums are added in a fixed order through LDS (deterministic);
-//  * large (256x256 tiles): raw NVFP4 staged in a 3-slot LDS ring and decoded per wave; each
-//    wave computes a 128x128 block with 64 MFMAs per 32-K step (details below).
-// Tiles are ordered expert-major, then m-tile, then n-tile (n fastest), and workgroup ids are
-// remapped so that the workgroups on one XCD take consecutive tiles (the same A rows stay in that
-// XCD's L2).
+// Two tile classes, both persistent over a work list taken from the routing step's table:
+//  * small (m-tiles of 16 token rows, for experts with few tokens, e.g. decode): weights are
+//    streamed from HBM straight into registers; every workgroup takes an equal share of the
+//    output columns, its 4 waves split K and add their partial sums in a fixed order through LDS
+//    (deterministic);
+//  * large (256x256 tiles): raw NVFP4 staged in an LDS ring and decoded per wave; each wave
+//    computes a 128x128 block with 64 MFMAs per 32-K step (details below).
+// Workgroup ids are remapped so that the workgroups on one XCD take neighbouring work (the same A
+// rows stay in that XCD's L2).
 //
-// Reduction-order permutation.  In the small class, lane l of a fragment holds 8 consecutive
-// elements at k = chunk + 32*(l/16) + 8*j for MFMA step j = 0..3 (instead of the MFMA's natural
-// 8*(l/16) within each 32-K step).  A and B use the same permutation, so each dot product is
-// unchanged; it lets a lane read 16 contiguous bytes of codes per chunk.
+// Reduction-order permutation.  In the small class, lane l of a fragment holds CH/8 consecutive
+// code bytes of its row (elements chunk + (CH/4)*(l/16) ..) and feeds element group st of them to
+// MFMA step st (instead of the MFMA's natural 8*(l/16) within each 32-K step).  A and B use the
+// same permutation, so each dot product is unchanged; it lets a lane read contiguous bytes.
 #include "device_common.h"
 #include "internal.h"
 
@@ -90,135 +90,347 @@ __device__ __forceinline__ float silu_f32(float g) {
 }
 
 // ============================================================================================
-// Small class: 16 token rows x 16 weight rows per tile (one MFMA column block), K split over the 4
-// waves of a workgroup.  L1: MFMA columns 0-7 are gate rows nt*8.., columns 8-15 the matching up
-// rows I + nt*8.., paired after the reduction with a lane shuffle -> 8 h columns.  L2: weight rows
-// nt*16..+16 -> 16 y columns.  Small tiles give many tiles per expert, so the persistent grid
-// stays balanced when only a few experts are active.
-//
-// Weight streaming: at decode an expert holds 1-2 tokens, so each weight byte feeds one 16-row
-// MFMA block and the kernel is bound by HBM.  Each wave walks its quarter of K in 128-element
-// chunks with a 4-deep register ring (loads for chunks c+1..c+4 in flight while chunk c is
-// decoded and multiplied); the partial sums of the 4 waves are added in a fixed order through
-// LDS (deterministic).
+// Small class (m-tiles of 16 token rows; experts with few tokens, e.g. decode).  Each weight byte
+// feeds one 16-row MFMA block, so the kernel streams weights, and decoding NVFP4 to fp16 costs
+// about 2 VALU instructions per weight byte and lane -- the VALU, not HBM, is what runs out
+// first.  The design keeps the VALU work per weight byte low and every workgroup equally busy:
+//  * work unit = one output column of one m-tile (L1: an h column, i.e. a gate row and its up
+//    row; L2: a y column, i.e. a weight row).  The units of all small m-tiles are laid end to end
+//    and each workgroup takes an equal contiguous range (workgroups on one XCD get neighbouring
+//    ranges, so the A rows of an m-tile stay in that XCD's L2);
+//  * a workgroup walks its range in groups of up to kSNb 16-column MFMA blocks (one m-tile per
+//    group).  Its 4 waves split the reduction dimension K in four and stream the same groups:
+//    one decoded A fragment feeds kSNb MFMAs;
+//  * weights come straight into registers, 16 B per lane per 128-element chunk, through a
+//    kSDepth-deep ring that runs on across group boundaries;
+//  * at the end of a group each wave leaves its kSNb partial blocks in LDS (double-buffered by
+//    group parity) and, after one LDS-only barrier (the weight loads stay in flight), wave w adds
+//    the 4 partials of blocks j = w mod 4 in wave order (deterministic) and stores them.
+// Lanes whose row lies outside the group or m-tile load a valid row of the same tile instead; the
+// MFMA outputs they feed are never stored.
+// L1 block j of a group: MFMA columns 0-7 are gate rows of h columns j0+8j.., columns 8-15 the
+// matching up rows, paired after the reduction with a lane shuffle.  L2 block j: weight rows
+// j0+16j..+16.
 // ============================================================================================
-constexpr int kChunk = 128;
-constexpr int kSmallDepth = 4;
-constexpr int kSmallWavesPerSimd = 4;
-constexpr int kLargeGrid = 256;   // large class: one workgroup per CU (LDS ~148 KB)
-constexpr int kSmallGrid = MEGAMOE_L1_AMAX_PARTS - kLargeGrid;   // small class: resident workgroups
-static_assert(kSmallGrid == 256 * kSmallWavesPerSimd, "small grid = workgroups resident at once");
+#ifndef MEGAMOE_SMALL_NB
+#define MEGAMOE_SMALL_NB 2
+#endif
+#ifndef MEGAMOE_SMALL_DEPTH
+#define MEGAMOE_SMALL_DEPTH 2
+#endif
+#ifndef MEGAMOE_SMALL_OCC
+#define MEGAMOE_SMALL_OCC 2
+#endif
+constexpr int kSNb = MEGAMOE_SMALL_NB;        // MFMA column blocks per group (share A)
+constexpr int kSDepth = MEGAMOE_SMALL_DEPTH;  // ring slots (chunks in flight per wave)
+constexpr int kSOcc = MEGAMOE_SMALL_OCC;      // workgroups (of 4 waves) per CU
+constexpr int kSWaves = kGemmThreads / kWave; // K split
+constexpr int kLargeGrid = 256;               // large class: one workgroup per CU (LDS ~148 KB)
+constexpr int kSmallGrid = 256 * kSOcc;       // small class: resident workgroups
+constexpr int kAmaxSmallSlots = MEGAMOE_L1_AMAX_PARTS - kLargeGrid;  // slots [kLargeGrid, PARTS)
+static_assert(kSmallGrid <= kAmaxSmallSlots, "one amax slot per small workgroup");
 static_assert(kSmallGrid % kXcds == 0, "grid split");
 
-struct SmallChunk {
-  u32x4 a, b;
-  uint32_t as, bs;
+template <bool kL1>
+constexpr int small_group_units() { return kL1 ? 8 * kSNb : 16 * kSNb; }
+
+struct SmallGroup {
+  int e;          // expert
+  int row0;       // first padded row of the m-tile
+  int rows_left;  // token rows of the m-tile (>= 1)
+  int j0;         // first unit of the group (L1: h column, L2: output column)
+  int n;          // units in the group
 };
 
-template <bool kL1>
-__global__ __launch_bounds__(kGemmThreads, kSmallWavesPerSimd) void gemm_small_kernel(GemmArgs p) {
+// One chunk of the reduction dimension for one lane: CH/8 code bytes (CH/32 MFMA steps) and
+// CH/64 scale bytes of its A row and of each of its kSNb weight rows.
+template <int CH>
+struct SmallSlot {
+  static constexpr int kQ = CH / 128;  // u32x4 words per lane and row (1 or 2)
+  u32x4 a[kQ];
+  uint32_t as;
+  u32x4 b[kSNb][kQ];
+  uint32_t bs[kSNb];
+};
+
+// Wave-uniform read through the scalar data cache (the index must be wave-uniform).  Scalar
+// loads are counted by lgkmcnt, so waiting for one does not wait for the vector loads of the
+// weight stream (vmcnt counts vector memory operations in issue order).
+template <typename T>
+__device__ __forceinline__ T sload(const T* p, int i) {
+  i = __builtin_amdgcn_readfirstlane(i);
+  return ((const __attribute__((address_space(4))) T*)(uintptr_t)p)[i];
+}
+
+// Workgroup barrier that orders LDS only: vector memory loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// CH (128 or 256) is the chunk of K a wave step covers: a lane loads CH/8 contiguous code bytes
+// (CH/32 MFMA steps) and CH/64 scale bytes per row.  256 halves the scale loads per weight byte
+// (one u32 instead of one u16 per 128 elements); 128 serves K that is an odd multiple of 128.
+template <bool kL1, int CH>
+__global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArgs p) {
+  using Slot = SmallSlot<CH>;
+  constexpr int kQ = Slot::kQ;
+  constexpr int kLaneBytes = CH / 8, kLaneScales = CH / 64;
+  // Per-expert tables in LDS: reading them inside the loop must not wait on the weight stream.
   __shared__ int s_pref[kMaxExperts + 1];
-  __shared__ f32x4 s_red[4][kWave];
+  __shared__ int s_poff[kMaxExperts];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ float s_wgs[kMaxExperts];
+  __shared__ f32x4 s_red[2][kSWaves][kSNb][kWave];
+  __shared__ uint32_t s_amax[kSWaves];
   const int E = p.E;
   const int32_t* __restrict__ sched = p.sched;
-  for (int j = threadIdx.x; j <= E; j += blockDim.x) s_pref[j] = sched[sched_pref_small(E) + j];
+  for (int j = threadIdx.x; j <= E; j += blockDim.x) {
+    s_pref[j] = sched[sched_pref_small(E) + j];
+    if (j < E) {
+      s_poff[j] = p.padded_offsets[j];
+      s_cnt[j] = p.counts[j];
+      s_wgs[j] = p.w_gs[j];
+    }
+  }
   __syncthreads();
-  const int ntn = kL1 ? p.N / 8 : p.N / 16;
-  const int total = s_pref[E] * ntn;
+  const int NU = p.N;  // units per m-tile: L1 h columns (I), L2 output columns (H)
+  constexpr int GU = small_group_units<kL1>();
+  const int64_t U = (int64_t)s_pref[E] * NU;
   const int K = p.K, Kh = K / 2, Ks = K / 16;
   const int Nw = kL1 ? 2 * p.N : p.N;  // weight rows per expert
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int r16 = lane & 15, g = lane >> 4;
-  const int nc = K / kChunk;
-  const int c_begin = wave * nc / 4, c_end = (wave + 1) * nc / 4;
+  const int nch = K / CH;
+  const int ks = nch < kSWaves ? nch : kSWaves;  // waves sharing K (all 4 unless K < 512)
+  const int c0 = wave < ks ? wave * nch / ks : 0, c1 = wave < ks ? (wave + 1) * nch / ks : 0;
   const float gs_a = *p.a_gs;
   uint32_t amax_bits = 0;
 
-  const XcdTiles tl(total);
-  for (int t = tl.t; t < tl.end; t += tl.stride) {
-    const TileInfo ti = decode_tile(s_pref, E, ntn, t, kBlockMSmall, p.padded_offsets, p.counts);
-    const bool a_ok = r16 < ti.rows_left;
-    int64_t a_row = ti.row0 + r16;
-    if (kL1) a_row = a_ok ? p.row_token[a_row] : 0;
-    const uint8_t* __restrict__ a_c = p.a_codes + a_row * Kh + g * 16;
-    const uint8_t* __restrict__ a_s = p.a_scales + a_row * Ks + g * 2;
-    int64_t b_row;
-    if (kL1) b_row = (int64_t)ti.e * Nw + (r16 < 8 ? ti.nt * 8 + r16 : p.N + ti.nt * 8 + r16 - 8);
-    else b_row = (int64_t)ti.e * Nw + ti.nt * 16 + r16;
-    const uint8_t* __restrict__ b_c = p.w_codes + b_row * Kh + g * 16;
-    const uint8_t* __restrict__ b_s = p.w_scales + b_row * Ks + g * 2;
+  // This workgroup's unit range; workgroup b runs on XCD b % 8.
+  const int G = gridDim.x, b = blockIdx.x;
+  const int64_t lb = (int64_t)(b % kXcds) * (G / kXcds) + b / kXcds;
+  const int64_t u_begin = lb * U / G, u_end = (lb + 1) * U / G;
 
-    auto load = [&](int c, SmallChunk& d) {
-      const int64_t off = (int64_t)c * (kChunk / 2), soff = (int64_t)c * (kChunk / 16);
-      if (a_ok) {
-        d.a = *reinterpret_cast<const u32x4*>(a_c + off);
-        d.as = *reinterpret_cast<const uint16_t*>(a_s + soff);
+  // Number of groups in [u_begin, u_end): groups never cross an m-tile.
+  int64_t ngroups = 0;
+  if (u_begin < u_end) {
+    const int64_t ma = u_begin / NU, mb = (u_end - 1) / NU;
+    if (ma == mb) {
+      ngroups = (u_end - u_begin + GU - 1) / GU;
+    } else {
+      ngroups = ((ma + 1) * NU - u_begin + GU - 1) / GU + (mb - ma - 1) * ((NU + GU - 1) / GU) +
+                (u_end - mb * NU + GU - 1) / GU;
+    }
+  }
+
+  auto group_at = [&](int64_t u) {
+    SmallGroup q;
+    const int mtg = (int)(u / NU);
+    q.e = find_expert(s_pref, E, 1, mtg);
+    const int mt = mtg - s_pref[q.e];
+    q.row0 = s_poff[q.e] + mt * kBlockMSmall;
+    q.rows_left = s_cnt[q.e] - mt * kBlockMSmall;
+    q.j0 = (int)(u - (int64_t)mtg * NU);
+    int64_t n = u_end - u;
+    if (n > NU - q.j0) n = NU - q.j0;
+    if (n > GU) n = GU;
+    q.n = (int)n;
+    return q;
+  };
+
+  if (c1 == c0) {
+    // K has fewer than 4 chunks and this wave has none: it only keeps the barrier count.
+    for (int64_t q = 0; q < ngroups; ++q) lds_barrier();
+  } else {
+    // ---- loader cursor: group being loaded, this lane's row pointers, next chunk --------------
+    // Past the last step the loader keeps re-reading its last group's first chunk (valid memory,
+    // never consumed), so every step issues the same loads.
+    int64_t lu = u_begin;
+    int lc = c0, ln = 0;
+    const uint8_t* la_c = p.a_codes;
+    const uint8_t* la_s = p.a_scales;
+    const uint8_t* lb_c[kSNb];
+    const uint8_t* lb_s[kSNb];
+#pragma unroll
+    for (int j = 0; j < kSNb; ++j) {
+      lb_c[j] = p.w_codes;
+      lb_s[j] = p.w_scales;
+    }
+    auto loader_enter = [&](int64_t u) {
+      const SmallGroup q = group_at(u);
+      int64_t arow;
+      if (kL1) {
+        int tok = sload(p.row_token, q.row0);
+        for (int i = 1; i < kBlockMSmall; ++i) {
+          if (i < q.rows_left) {
+            const int t = sload(p.row_token, q.row0 + i);
+            tok = r16 == i ? t : tok;
+          }
+        }
+        arow = tok;
       } else {
-        d.a = u32x4{0u, 0u, 0u, 0u};
-        d.as = 0u;
+        arow = q.row0 + (r16 < q.rows_left ? r16 : 0);
       }
-      d.b = *reinterpret_cast<const u32x4*>(b_c + off);
-      d.bs = *reinterpret_cast<const uint16_t*>(b_s + soff);
-    };
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](const SmallChunk& d) {
-      const f16x2 sa = e4m3x2_to_f16(d.as, false);
-      const f16x2 sb = e4m3x2_to_f16(d.bs, false);
+      la_c = p.a_codes + arow * Kh + g * kLaneBytes;
+      la_s = p.a_scales + arow * Ks + g * kLaneScales;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f16x8 a = decode8(d.a[j], j < 2 ? bcast_lo(sa) : bcast_hi(sa));
-        const f16x8 w = decode8(d.b[j], j < 2 ? bcast_lo(sb) : bcast_hi(sb));
-        acc = mfma16(a, w, acc);
+      for (int j = 0; j < kSNb; ++j) {
+        int64_t brow;
+        if (kL1) {
+          const int hc = 8 * j + (r16 & 7);
+          const int col = q.j0 + (hc < q.n ? hc : 0);
+          brow = (int64_t)q.e * Nw + (r16 < 8 ? col : p.N + col);
+        } else {
+          const int rc = 16 * j + r16;
+          brow = (int64_t)q.e * Nw + q.j0 + (rc < q.n ? rc : 0);
+        }
+        lb_c[j] = p.w_codes + brow * Kh + g * kLaneBytes;
+        lb_s[j] = p.w_scales + brow * Ks + g * kLaneScales;
       }
+      ln = q.n;
     };
-    // 4-deep register ring over this wave's chunks; slot k always holds chunks c with
-    // (c - c_begin) % 4 == k, so every slot has fixed registers after unrolling.
-    SmallChunk ring[kSmallDepth];
+    if (u_begin < u_end) loader_enter(u_begin);
+    auto load_scale = [](const uint8_t* q) -> uint32_t {
+      if (kLaneScales == 4) return *reinterpret_cast<const uint32_t*>(q);
+      return *reinterpret_cast<const uint16_t*>(q);
+    };
+    auto load = [&](Slot& d) {
+      const int64_t off = (int64_t)lc * (CH / 2), soff = (int64_t)lc * (CH / 16);
 #pragma unroll
-    for (int k = 0; k < kSmallDepth; ++k)
-      if (c_begin + k < c_end) load(c_begin + k, ring[k]);
-    for (int c = c_begin; c < c_end; c += kSmallDepth) {
+      for (int q = 0; q < kQ; ++q) d.a[q] = *reinterpret_cast<const u32x4*>(la_c + off + 16 * q);
+      d.as = load_scale(la_s + soff);
 #pragma unroll
-      for (int k = 0; k < kSmallDepth; ++k) {
-        if (c + k < c_end) {
-          compute(ring[k]);
-          if (c + k + kSmallDepth < c_end) load(c + k + kSmallDepth, ring[k]);
+      for (int j = 0; j < kSNb; ++j) {
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) d.b[j][q] = *reinterpret_cast<const u32x4*>(lb_c[j] + off + 16 * q);
+        d.bs[j] = load_scale(lb_s[j] + soff);
+      }
+      if (++lc == c1) {
+        lc = c0;
+        if (lu + ln < u_end) {
+          lu += ln;
+          loader_enter(lu);
         }
       }
-    }
-    // Fixed-order reduction of the 4 K-partials.
-    s_red[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-      f32x4 r = s_red[0][lane];
+    };
+
+    // ---- compute cursor ---------------------------------------------------------------------------
+    int64_t cu = u_begin;
+    int cc = c0, parity = 0;
+    SmallGroup cg{0, 0, 1, 0, 0};
+    if (cu < u_end) cg = group_at(cu);
+    f32x4 acc[kSNb];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) r += s_red[w][lane];
-      const float inv = (float)(1.0 / ((double)gs_a * (double)p.w_gs[ti.e]));
+    for (int j = 0; j < kSNb; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // MFMA step st takes the lane's code word st (8 elements, scale block st / 2).
+    auto compute = [&](const Slot& d) {
+      f16x2 sa[kQ];
+      f16x2 sb[kSNb][kQ];
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        sa[q] = e4m3x2_to_f16(d.as, q == 1);
+#pragma unroll
+        for (int j = 0; j < kSNb; ++j) sb[j][q] = e4m3x2_to_f16(d.bs[j], q == 1);
+      }
+#pragma unroll
+      for (int st = 0; st < CH / 32; ++st) {
+        const int q = st / 4, w4 = st % 4;
+        const f16x8 a = decode8(d.a[q][w4], w4 < 2 ? bcast_lo(sa[q]) : bcast_hi(sa[q]));
+#pragma unroll
+        for (int j = 0; j < kSNb; ++j) {
+          const f16x8 w = decode8(d.b[j][q][w4], w4 < 2 ? bcast_lo(sb[j][q]) : bcast_hi(sb[j][q]));
+          acc[j] = mfma16(a, w, acc[j]);
+        }
+      }
+    };
+
+    // End of a group: publish the partial blocks, then wave w finishes blocks j = w (mod ks).
+    auto group_end = [&]() {
+#pragma unroll
+      for (int j = 0; j < kSNb; ++j) {
+        s_red[parity][wave][j][lane] = acc[j];
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      lds_barrier();
+      const float inv = (float)(1.0 / ((double)gs_a * (double)s_wgs[cg.e]));
       uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = 4 * g + q;
-        if (kL1) {
-          const float up_raw = __shfl(r[q], lane + 8, kWave);  // column c+8 holds the up row of c
-          if (r16 < 8 && row < ti.rows_left) {
-            const float gt = r[q] * inv, up = up_raw * inv;
-            const uint32_t hb = f32_to_bf16_bits(silu_f32(gt) * up);
-            out[(int64_t)(ti.row0 + row) * p.N + ti.nt * 8 + r16] = (uint16_t)hb;
-            const uint32_t mag = hb & 0x7FFFu;
-            amax_bits = amax_bits > mag ? amax_bits : mag;
+      for (int j = 0; j < kSNb; ++j) {
+        if (j % ks != wave) continue;
+        f32x4 r = s_red[parity][0][j][lane];
+        for (int w = 1; w < ks; ++w) r += s_red[parity][w][j][lane];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 4 * g + q;
+          if (kL1) {
+            const float up_raw = __shfl(r[q], lane + 8, kWave);  // column c+8 holds the up row of c
+            const int hc = 8 * j + r16;
+            if (r16 < 8 && hc < cg.n && row < cg.rows_left) {
+              const float gt = r[q] * inv, up = up_raw * inv;
+              const uint32_t hb = f32_to_bf16_bits(silu_f32(gt) * up);
+              out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + hc] = (uint16_t)hb;
+              const uint32_t mag = hb & 0x7FFFu;
+              amax_bits = amax_bits > mag ? amax_bits : mag;
+            }
+          } else {
+            const int rc = 16 * j + r16;
+            if (rc < cg.n && row < cg.rows_left)
+              out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + rc] = (uint16_t)f32_to_bf16_bits(r[q] * inv);
           }
-        } else if (row < ti.rows_left) {
-          out[(int64_t)(ti.row0 + row) * p.N + ti.nt * 16 + r16] = (uint16_t)f32_to_bf16_bits(r[q] * inv);
         }
       }
+      parity ^= 1;
+    };
+    auto step_done = [&]() {
+      if (++cc == c1) {
+        group_end();
+        cc = c0;
+        cu += cg.n;
+        if (cu < u_end) cg = group_at(cu);
+      }
+    };
+
+    // Steady state: step s computes ring slot s % kSDepth and refills it with step s + kSDepth.
+    // Loads are unconditional in the prologue and the main loop (so the compiler's in-order vmcnt
+    // waits keep kSDepth - 1 steps in flight); only the last < 2 kSDepth steps are predicated.
+    const int64_t S = ngroups * (c1 - c0);
+    Slot ring[kSDepth];
+#pragma unroll
+    for (int k = 0; k < kSDepth; ++k) load(ring[k]);
+    int64_t s0 = 0;
+    for (; s0 + 2 * kSDepth <= S; s0 += kSDepth) {
+#pragma unroll
+      for (int k = 0; k < kSDepth; ++k) {
+        compute(ring[k]);
+        load(ring[k]);
+        step_done();
+      }
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2 * kSDepth - 1; ++i) {
+      if (s0 + i < S) {
+        compute(ring[i % kSDepth]);
+        if (s0 + i + kSDepth < S) load(ring[i % kSDepth]);
+        step_done();
+      }
+    }
   }
+
   if (kL1) {
-    // only wave 0 wrote h; its max is the workgroup's
     amax_bits = wave_max_u32(amax_bits);
-    if (threadIdx.x == 0) p.amax_out[kLargeGrid + blockIdx.x] = bf16_bits_to_f32(amax_bits);
-    if (p.clear_other && threadIdx.x == 0 && (int)blockIdx.x < kLargeGrid) p.amax_out[blockIdx.x] = 0.0f;
+    if (lane == 0) s_amax[wave] = amax_bits;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t m = s_amax[0];
+      for (int w = 1; w < kSWaves; ++w) m = m > s_amax[w] ? m : s_amax[w];
+      p.amax_out[kLargeGrid + b] = bf16_bits_to_f32(m);
+      for (int j = b + G; j < kAmaxSmallSlots; j += G) p.amax_out[kLargeGrid + j] = 0.0f;
+      if (p.clear_other)
+        for (int j = b; j < kLargeGrid; j += G) p.amax_out[j] = 0.0f;
+    }
   }
 }
 
@@ -529,7 +741,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
       for (int w = 1; w < kGemmThreads / kWave; ++w) m = m > s_amax[w] ? m : s_amax[w];
       p.amax_out[blockIdx.x] = bf16_bits_to_f32(m);
       if (p.clear_other)
-        for (int j = (int)blockIdx.x; j < kSmallGrid; j += kLargeGrid) p.amax_out[kLargeGrid + j] = 0.0f;
+        for (int j = (int)blockIdx.x; j < kAmaxSmallSlots; j += kLargeGrid) p.amax_out[kLargeGrid + j] = 0.0f;
     }
   }
 }
@@ -545,7 +757,10 @@ static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
     if (err != hipSuccess) return err;
   }
   if (c.small) {
-    hipLaunchKernelGGL(gemm_small_kernel<kL1>, dim3(kSmallGrid), dim3(kGemmThreads), 0, stream, a);
+    if (a.K % 256 == 0)
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256>), dim3(kSmallGrid), dim3(kGemmThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 128>), dim3(kSmallGrid), dim3(kGemmThreads), 0, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;

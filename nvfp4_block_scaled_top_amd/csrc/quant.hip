@@ -18,8 +18,8 @@
 //
 // Two kernels: an amax pass writing per-workgroup partial maxima (skipped when the caller passes
 // its own partial maxima in amax_in), then the quantization pass, whose every workgroup reduces
-// the partials itself (no atomics, nothing to reset between calls).  Tensors of up to 2^18
-// elements (decode activations) are done by one workgroup in one launch.
+// the partials itself (no atomics, nothing to reset between calls).  Tensors of up to 2^16
+// elements (decode activations) take a single launch (quant_small_kernel).
 #include "device_common.h"
 #include "internal.h"
 
@@ -165,35 +165,52 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint16_t* __
   }
 }
 
-// Small tensors (decode activations): amax and quantization in one workgroup, one launch.
-constexpr int64_t kQuantSmallElems = 1 << 18;
+// Small tensors (decode activations, up to 2^16 elements): one launch of ceil(blocks / 1024)
+// workgroups of 1024 threads.  Every workgroup reduces the amax of the whole tensor itself (at most
+// 8 loads of 16 bytes per thread, all in flight, from L2 after the first workgroup), so no
+// workgroup waits for another; then each thread quantizes one 16-element block.
+constexpr int kQuantSmallThreads = 1024;
+constexpr int kQuantSmallLoads = 8;
+constexpr int64_t kQuantSmallElems = (int64_t)kQuantSmallThreads * kQuantSmallLoads * 8;
 
-__global__ __launch_bounds__(kQuantThreads) void quant_small_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                                    int64_t cols, const int32_t* __restrict__ row_valid,
-                                                                    uint8_t* __restrict__ codes,
-                                                                    uint8_t* __restrict__ scales,
-                                                                    float* __restrict__ gs_out) {
-  __shared__ uint32_t red[kQuantThreads / kWave];
-  const int64_t nvec = rows * cols / 8;
+__global__ __launch_bounds__(kQuantSmallThreads) void quant_small_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                         int64_t cols,
+                                                                         const int32_t* __restrict__ row_valid,
+                                                                         uint8_t* __restrict__ codes,
+                                                                         uint8_t* __restrict__ scales,
+                                                                         float* __restrict__ gs_out) {
+  __shared__ uint32_t red[kQuantSmallThreads / kWave];
+  const int nvec = (int)(rows * cols / 8);
+  u32x4 d[kQuantSmallLoads];
+#pragma unroll
+  for (int j = 0; j < kQuantSmallLoads; ++j) {
+    const int v = (int)threadIdx.x + j * kQuantSmallThreads;
+    d[j] = u32x4{0u, 0u, 0u, 0u};
+    if (v < nvec && (row_valid == nullptr || row_valid[((int64_t)v * 8) / cols] >= 0))
+      d[j] = *reinterpret_cast<const u32x4*>(x + (int64_t)v * 8);
+  }
   uint32_t m = 0;
-  for (int64_t v = threadIdx.x; v < nvec; v += blockDim.x) {
-    if (row_valid != nullptr && row_valid[(v * 8) / cols] < 0) continue;
-    const uint32_t t = bf16_abs_max8(*reinterpret_cast<const u32x4*>(x + v * 8));
+#pragma unroll
+  for (int j = 0; j < kQuantSmallLoads; ++j) {
+    const uint32_t t = bf16_abs_max8(d[j]);
     m = m > t ? m : t;
   }
-  m = block_max_u32(m, red);
+  m = wave_max_u32(m);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  m = red[0];
+  for (int j = 1; j < kQuantSmallThreads / kWave; ++j) m = m > red[j] ? m : red[j];
   const float gs = global_scale_of(bf16_bits_to_f32(m));
-  if (threadIdx.x == 0) *gs_out = gs;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
   const int64_t bpr = cols / 16;
-  const int64_t nblk = rows * bpr;
-  for (int64_t b = threadIdx.x; b < nblk; b += blockDim.x) {
-    if (row_valid != nullptr && row_valid[b / bpr] < 0) {
-      *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{0u, 0u};
-      scales[b] = 0;
-      continue;
-    }
-    quant_block(x, b, gs, codes, scales);
+  const int64_t b = (int64_t)blockIdx.x * kQuantSmallThreads + threadIdx.x;
+  if (b >= rows * bpr) return;
+  if (row_valid != nullptr && row_valid[b / bpr] < 0) {
+    *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{0u, 0u};
+    scales[b] = 0;
+    return;
   }
+  quant_block(x, b, gs, codes, scales);
 }
 
 hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* row_valid,
@@ -202,8 +219,10 @@ hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int
   const float* amax_src = amax_in;
   int nparts = amax_in_count;
   if (amax_in == nullptr && rows * cols <= kQuantSmallElems) {
-    hipLaunchKernelGGL(quant_small_kernel, dim3(1), dim3(kQuantThreads), 0, stream, x, rows, cols, row_valid, codes,
-                       scales, gs);
+    const int64_t nblk = rows * (cols / 16);
+    const int grid = (int)((nblk + kQuantSmallThreads - 1) / kQuantSmallThreads);
+    hipLaunchKernelGGL(quant_small_kernel, dim3(grid > 0 ? grid : 1), dim3(kQuantSmallThreads), 0, stream, x, rows,
+                       cols, row_valid, codes, scales, gs);
     return hipGetLastError();
   }
   if (amax_in == nullptr) {

@@ -40,26 +40,35 @@ __global__ __launch_bounds__(kRouteChunk) void route_count_kernel(const int32_t*
     for (int e = threadIdx.x; e < E; e += blockDim.x) ws[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// Inclusive scan of one int per thread over a 1024-thread block (Hillis-Steele in LDS).
-__device__ __forceinline__ int block_incl_scan(int v, int* buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int o = 1; o < (int)blockDim.x; o <<= 1) {
-    const int add = t >= o ? buf[t - o] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+// Inclusive scan of four ints per thread over a 1024-thread block: shuffle scans inside each wave,
+// then the totals of the earlier waves added from LDS (one barrier).
+struct Scan4 {
+  int v[4];
+};
+
+__device__ __forceinline__ Scan4 block_incl_scan4(Scan4 s, Scan4* wtot /* [kRouteChunk / kWave] */) {
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = __shfl_up(s.v[j], o, kWave);
+      if (lane >= o) s.v[j] += u;
+    }
   }
-  const int r = buf[t];
+  if (lane == kWave - 1) wtot[w] = s;
   __syncthreads();
-  return r;
+  for (int q = 0; q < w; ++q) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s.v[j] += wtot[q].v[j];
+  }
+  return s;
 }
 
 // Given each expert's total (thread e holds expert e's count; threads >= E hold 0), write counts,
 // both offset arrays and the tile table.  Called by all 1024 threads of the block.
 // If s_poff is given, padded_offsets[0..E) are also left there (LDS) for the caller.
-__device__ void finish_tables(int total, int32_t E, int32_t P, int32_t bm_override, int* buf,
+__device__ void finish_tables(int total, int32_t E, int32_t P, int32_t bm_override, Scan4* wtot,
                               int32_t* __restrict__ counts, int32_t* __restrict__ eoff,
                               int32_t* __restrict__ poff, int32_t* __restrict__ sched, int* s_poff) {
   const int e = threadIdx.x;
@@ -73,10 +82,8 @@ __device__ void finish_tables(int total, int32_t E, int32_t P, int32_t bm_overri
     if (small) small_tiles = tiles; else large_tiles = tiles;
     padded = (int)(((int64_t)total + P - 1) / P * P);
   }
-  const int inc_cnt = block_incl_scan(total, buf);
-  const int inc_pad = block_incl_scan(padded, buf);
-  const int inc_small = block_incl_scan(small_tiles, buf);
-  const int inc_large = block_incl_scan(large_tiles, buf);
+  const Scan4 inc = block_incl_scan4(Scan4{{total, padded, small_tiles, large_tiles}}, wtot);
+  const int inc_cnt = inc.v[0], inc_pad = inc.v[1], inc_small = inc.v[2], inc_large = inc.v[3];
   if (s_poff != nullptr && e < E) s_poff[e] = inc_pad - padded;
   if (e < E) {
     eoff[e + 1] = inc_cnt;
@@ -99,21 +106,27 @@ __device__ void finish_tables(int total, int32_t E, int32_t P, int32_t bm_overri
   }
 }
 
-__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ ws, int32_t nchunks, int32_t E,
+__global__ __launch_bounds__(kRouteChunk) void route_scan_kernel(int32_t* __restrict__ ws, int32_t nchunks, int32_t E,
                                                           int32_t P, int32_t bm_override,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ eoff,
                                                           int32_t* __restrict__ poff, int32_t* __restrict__ sched) {
-  __shared__ int buf[1024];
+  __shared__ Scan4 wtot[kRouteChunk / kWave];
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = ws[(int64_t)c * E + e];
-      ws[(int64_t)c * E + e] = total;
-      total += v;
+    // Column prefix over the chunks, 16 loads in flight per batch.
+    for (int c0 = 0; c0 < nchunks; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = c0 + j < nchunks ? ws[(int64_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (c0 + j < nchunks) ws[(int64_t)(c0 + j) * E + e] = total;
+        total += v[j];
+      }
     }
   }
-  finish_tables(total, E, P, bm_override, buf, counts, eoff, poff, sched, nullptr);
+  finish_tables(total, E, P, bm_override, wtot, counts, eoff, poff, sched, nullptr);
 }
 
 // Rank of this lane's expert among the lanes of its wave holding the same expert (values 0..E;
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(kRouteChunk) void route_small_kernel(const int32_t*
                                                                   int32_t* __restrict__ sched) {
   constexpr int kWaves = kRouteChunk / kWave;
   extern __shared__ int32_t wcnt[];  // [kWaves][E]
-  __shared__ int buf[kRouteChunk];
+  __shared__ Scan4 wtot[kRouteChunk / kWave];
   __shared__ int s_poff[kMaxExperts];
   for (int j = threadIdx.x; j < kWaves * E; j += blockDim.x) wcnt[j] = 0;
   for (int64_t r = threadIdx.x; r < M_cap; r += blockDim.x) row_token[r] = -1;
@@ -193,7 +206,7 @@ __global__ __launch_bounds__(kRouteChunk) void route_small_kernel(const int32_t*
   int total = 0;
   if ((int)threadIdx.x < E)
     for (int w = 0; w < kWaves; ++w) total += wcnt[w * E + threadIdx.x];
-  finish_tables(total, E, P, bm_override, buf, counts, eoff, poff, sched, s_poff);
+  finish_tables(total, E, P, bm_override, wtot, counts, eoff, poff, sched, s_poff);
   __syncthreads();  // s_poff and the -1 fill of row_token are complete
   if (i < n) {
     int row = -1;
@@ -223,7 +236,7 @@ hipError_t launch_route(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e
                      topk_ids, n, e0, E, nchunks, ws, row_token, M_cap);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, ws, nchunks, E, P, block_m_override,
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteChunk), 0, stream, ws, nchunks, E, P, block_m_override,
                      counts, eoff, poff, sched);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
