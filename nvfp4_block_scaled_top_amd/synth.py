@@ -134,6 +134,16 @@ def expert_weights(w: Workload, global_expert: int, seed: int = 0, device: str =
     return tuple(out)
 
 
+def device_normal_bf16(shape, seed: int, stream: int, std: float, device: str = "cuda"):
+    """A seeded N(0, std) bf16 tensor drawn on `device` (stand-in stage inputs of full size, e.g.
+    h for the L2 stage and y for the combine).  Streams 6 and up; no method arithmetic."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(_weight_seed(seed, stream, 0))
+    return (torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
 def routing_stats(ids: np.ndarray, w: Workload):
     """Per-expert counts of local assignments (a summary used to pin the recipe)."""
     loc = ids[(ids >= w.expert_begin) & (ids < w.expert_begin + w.num_experts)] - w.expert_begin
