@@ -17,8 +17,8 @@
 //    streamed from HBM straight into registers; every workgroup takes an equal share of the
 //    output columns, its 4 waves split K and add their partial sums in a fixed order through LDS
 //    (deterministic);
-//  * large (256x256 tiles): raw NVFP4 staged in an LDS ring and decoded per wave; each wave
-//    computes a 128x128 block with 64 MFMAs per 32-K step (details below).
+//  * large (256x256 tiles): raw NVFP4 staged in an LDS ring and decoded per wave; 8 waves (4x2)
+//    each compute a 64x128 block, 2 waves per SIMD (details below).
 // Workgroup ids are remapped so that the workgroups on one XCD take neighbouring work (the same A
 // rows stay in that XCD's L2).
 //
@@ -454,19 +454,28 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
 // Stage layout (per operand): codes row-major, kLRowBytes per tile row R, with the 16-byte chunk
 // c (elements 32c..32c+31 of the stage) stored in slot c ^ swizzle(R) so that the 16-byte
 // fragment reads of 8 consecutive rows hit distinct banks; a DMA instruction covers 1024 / 
-// kLRowBytes rows with kLChunks lanes per row (row-contiguous global bytes).  Scales: the stage's
-// block scales of row R for lane half h at h * (kLBm * kLScaleRow / 2) + R * kLScaleRow / 2.
+// kLRowBytes rows with kLChunks lanes per row (row-contiguous global bytes).  Scales: the stage's 8
+// block scales of row R at R * 8 (lane half h reads the 4 bytes at R * 8 + 4h).
 // Lane (p = lane % 32, h = lane / 32) of a 32-row fragment owns elements [h * kLKs/2, +kLKs/2) of
 // its row and feeds [h * kLKs/2 + 8s, +8) to MFMA step s as the MFMA's k = 8h..8h+7.  A and B use
 // the same map, so each dot product runs over every element once.
 //
-// Waves are 2x2, each 128x128 of the tile (4 x 4 MFMA blocks of 32x32, 256 fp32 accumulators).
+// Waves are kLWM x 2 (4 x 2 by default), each (256/kLWM) x 128 of the tile: kLMI x 4 MFMA blocks
+// of 32x32 (128 fp32 accumulators).  Two waves per SIMD hide each other's LDS waits and barrier
+// skew; the price is 6 decode VALU per MFMA instead of 4 with 2 x 2 waves of 128 x 128.
 // L1: tile weight rows 0..127 are gate rows nt*128.., 128..255 the matching up rows, so a wave
 // holds gate and up of the same 64 h columns and applies SiLU(gate)*up in registers.
 // L2: tile weight rows are output rows nt*256..+256.
 // The epilogue stages the bf16 tile in LDS and writes it with 16-byte row-contiguous stores.
 // ============================================================================================
+#ifndef MEGAMOE_LARGE_WM
+#define MEGAMOE_LARGE_WM 4
+#endif
 constexpr int kLBm = kBlockMLarge, kLBn = 256;
+constexpr int kLWM = MEGAMOE_LARGE_WM, kLWN = 2;                 // waves along M and N
+constexpr int kLWaves = kLWM * kLWN, kLThreads = kLWaves * kWave;
+constexpr int kLMI = kLBm / 32 / kLWM;                           // 32-row MFMA blocks per wave
+constexpr int kLRowsPerWave = kLBm / kLWaves;                    // DMA rows per wave and operand
 constexpr int kLKs = 128, kLSlots = 4, kLAhead = 2;               // stage depth, ring slots, prefetch
 constexpr int kLRowBytes = kLKs / 2;                             // code bytes of one row per stage
 constexpr int kLChunks = kLRowBytes / 16;                        // 16-byte chunks per row (2 or 4)
@@ -478,12 +487,14 @@ constexpr int kLScaleBytes = kLBm * kLScaleRow;
 constexpr int kLOpBytes = kLCodeBytes + kLScaleBytes;            // one operand, one stage
 constexpr int kLStageBytes = 2 * kLOpBytes;
 constexpr int kLLdsBytes = kLSlots * kLStageBytes;
-constexpr int kLCodeDma = 64 * kLRowBytes / 1024;                // per wave and operand
-constexpr int kLScaleDma = kLScaleRow / 4;                       // 4-byte DMA per row and half
+constexpr int kLCodeDma = kLRowsPerWave * kLRowBytes / 1024;     // 16-byte DMA per wave and operand
+constexpr int kLScaleDma = kLRowsPerWave * kLScaleRow / 256;     // 4-byte DMA per wave and operand
 constexpr int kLDmaPerWave = 2 * (kLCodeDma + kLScaleDma);
 constexpr int kLOutPitchL1 = 128 * 2 + 16, kLOutPitchL2 = 256 * 2 + 16;  // bf16 staging pitches
 static_assert(kLKs == 64 || kLKs == 128, "stage depth");
 static_assert(kLBm == 256 && kLBn == 256, "large tiles are 256x256");
+static_assert(kLWM == 2 || kLWM == 4, "2x2 or 4x2 waves");
+static_assert(kLCodeDma >= 1 && kLScaleDma >= 1 && kLRowsPerWave * kLScaleRow % 256 == 0, "DMA split");
 static_assert(kLAhead <= kLSlots - 2, "refilled slot must have been read two stages earlier");
 static_assert(kLBm * kLOutPitchL2 <= kLLdsBytes && kLBm * kLOutPitchL1 <= kLLdsBytes, "staging fits");
 
@@ -528,10 +539,10 @@ __device__ __forceinline__ void wait_stage(int stages_after) {
 }
 
 template <bool kL1>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kLThreads, 1) void gemm_large_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLLdsBytes];
   __shared__ int s_pref[kMaxExperts + 1];
-  __shared__ uint32_t s_amax[kGemmThreads / kWave];
+  __shared__ uint32_t s_amax[kLWaves];
   const int E = p.E;
   for (int j = threadIdx.x; j <= E; j += blockDim.x) s_pref[j] = p.sched[sched_pref_large(E) + j];
   __syncthreads();
@@ -541,7 +552,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
   const int Nw = kL1 ? 2 * p.N : p.N;
   const int nks = K / kLKs;
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kLWN, wn = wave % kLWN;
   const int p32 = lane & 31, h2 = lane >> 5;
   const float gs_a = *p.a_gs;
   uint32_t amax_bits = 0;
@@ -555,9 +566,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
   for (int t = tl.t; t < tl.end; t += tl.stride) {
     const TileInfo ti = decode_tile(s_pref, E, ntn, t, kLBm, p.padded_offsets, p.counts);
     // ---- DMA sources of this lane --------------------------------------------------------------
-    // codes: instruction j covers tile rows 64*wave + j*rows_per + lane/kLChunks; lane%kLChunks
-    // picks the LDS slot and the global chunk (lane%kLChunks) ^ swizzle(row) goes there; scales:
-    // tile row 64*wave + lane.
+    // codes: instruction j covers tile rows kLRowsPerWave*wave + j*rows_per + lane/kLChunks;
+    // lane%kLChunks picks the LDS slot and the global chunk (lane%kLChunks) ^ swizzle(row) goes
+    // there; scales: instruction j covers rows kLRowsPerWave*wave + 32j + lane/2, lane%2 picking
+    // the 4-byte half (LDS scale layout: 8 bytes per row).
     auto a_row_of = [&](int R) -> int64_t {
       const int Rv = R < ti.rows_left ? R : 0;  // rows past the expert read row 0; never stored
       const int64_t r = ti.row0 + Rv;
@@ -572,36 +584,43 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
     const uint8_t* b_code_src[kLCodeDma];
 #pragma unroll
     for (int j = 0; j < kLCodeDma; ++j) {
-      const int R = 64 * wave + rows_per * j + lane / kLChunks;
+      const int R = kLRowsPerWave * wave + rows_per * j + lane / kLChunks;
       const int chunk = (lane % kLChunks) ^ ((R >> kLSwzShift) & (kLChunks - 1));
       a_code_src[j] = p.a_codes + a_row_of(R) * Kh + 16 * chunk;
       b_code_src[j] = p.w_codes + b_row_of(R) * Kh + 16 * chunk;
     }
-    const uint8_t* a_scale_src = p.a_scales + a_row_of(64 * wave + lane) * Ks;
-    const uint8_t* b_scale_src = p.w_scales + b_row_of(64 * wave + lane) * Ks;
-
-    f32x16 acc[4][4];
+    static_assert(kLScaleRow == 8, "scale DMA assumes 128-K stages");
+    const uint8_t* a_scale_src[kLScaleDma];
+    const uint8_t* b_scale_src[kLScaleDma];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < kLScaleDma; ++j) {
+      const int R = kLRowsPerWave * wave + 32 * j + lane / 2;
+      a_scale_src[j] = p.a_scales + a_row_of(R) * Ks + 4 * (lane & 1);
+      b_scale_src[j] = p.w_scales + b_row_of(R) * Ks + 4 * (lane & 1);
+    }
+
+    f32x16 acc[kLMI][4];
+#pragma unroll
+    for (int i = 0; i < kLMI; ++i)
 #pragma unroll
       for (int f = 0; f < 4; ++f)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.f;
 
-    // kLDmaPerWave DMA instructions per wave: this wave's 64 rows of both operands for stage ks.
+    // kLDmaPerWave DMA instructions per wave: this wave's kLRowsPerWave rows of both operands.
     auto issue_stage = [&](int ks, int slot) {
       const uint32_t lb = lds_addr(smem + slot * kLStageBytes);
       const int64_t off = (int64_t)ks * kLRowBytes, soff = (int64_t)ks * kLScaleRow;
 #pragma unroll
       for (int j = 0; j < kLCodeDma; ++j) {
-        dma16(a_code_src[j] + off, lb + (64 * wave + rows_per * j) * kLRowBytes);
-        dma16(b_code_src[j] + off, lb + kLOpBytes + (64 * wave + rows_per * j) * kLRowBytes);
+        dma16(a_code_src[j] + off, lb + (kLRowsPerWave * wave + rows_per * j) * kLRowBytes);
+        dma16(b_code_src[j] + off, lb + kLOpBytes + (kLRowsPerWave * wave + rows_per * j) * kLRowBytes);
       }
 #pragma unroll
-      for (int hh = 0; hh < kLScaleDma; ++hh) {
-        const int so = kLCodeBytes + hh * (kLBm * 4) + 64 * wave * 4;
-        dma4(a_scale_src + soff + 4 * hh, lb + so);
-        dma4(b_scale_src + soff + 4 * hh, lb + kLOpBytes + so);
+      for (int j = 0; j < kLScaleDma; ++j) {
+        const int so = kLCodeBytes + (kLRowsPerWave * wave + 32 * j) * kLScaleRow;
+        dma4(a_scale_src[j] + soff, lb + so);
+        dma4(b_scale_src[j] + soff, lb + kLOpBytes + so);
       }
     };
     auto compute_stage = [&](int slot) {
@@ -615,14 +634,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
       const int swz = (p32 >> kLSwzShift) & (kLChunks - 1);
       // scale bytes of this lane half: 2 (64-K stages) or 4 (128-K stages) per row
       auto scale_word = [&](const uint8_t* sp, int row) -> uint32_t {
-        if (kLScaleRow == 8) return *reinterpret_cast<const uint32_t*>(sp + h2 * (kLBm * 4) + row * 4);
-        return *reinterpret_cast<const uint16_t*>(sp + row * 4 + 2 * h2);
+        return *reinterpret_cast<const uint32_t*>(sp + row * kLScaleRow + 4 * h2);
       };
-      u32x4 araw[4][CPL], braw[4][CPL];
-      uint32_t asw[4], bsw[4];
+      u32x4 araw[kLMI][CPL], braw[4][CPL];
+      uint32_t asw[kLMI], bsw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + 32 * i + p32;
+      for (int i = 0; i < kLMI; ++i) {
+        const int row = wm * (32 * kLMI) + 32 * i + p32;
 #pragma unroll
         for (int j = 0; j < CPL; ++j)
           araw[i][j] = *reinterpret_cast<const u32x4*>(a_codes + row * kLRowBytes + 16 * ((CPL * h2 + j) ^ swz));
@@ -637,15 +655,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
         bsw[f] = scale_word(b_scales, row);
       }
       // fp16 scale pairs: pair q covers steps 4q..4q+3 (blocks 2q, 2q+1 of this lane half)
-      f16x2 asc[4][CPL], bsc[4][CPL];
+      f16x2 asc[kLMI][CPL], bsc[4][CPL];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kLMI; ++i) {
         asc[i][0] = e4m3x2_to_f16(asw[i], false);
-        bsc[i][0] = e4m3x2_to_f16(bsw[i], false);
-        if (CPL == 2) {
-          asc[i][CPL - 1] = e4m3x2_to_f16(asw[i], true);
-          bsc[i][CPL - 1] = e4m3x2_to_f16(bsw[i], true);
-        }
+        if (CPL == 2) asc[i][CPL - 1] = e4m3x2_to_f16(asw[i], true);
+      }
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        bsc[f][0] = e4m3x2_to_f16(bsw[f], false);
+        if (CPL == 2) bsc[f][CPL - 1] = e4m3x2_to_f16(bsw[f], true);
       }
       auto sc = [](const f16x2 (&pr)[CPL], int step) {
         const f16x2 v = pr[step >> 2];
@@ -653,6 +672,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
       };
       auto word = [](const u32x4 (&r)[CPL], int step) { return r[step >> 2][step & 3]; };
       // Software pipeline: B fragments of step s+1 are decoded between the MFMAs of step s.
+      constexpr int kBPerI = 4 / kLMI;             // B fragments decoded per A row block
+      constexpr int kVPerM = 2 + 8 * kBPerI / 4;   // VALU per MFMA: (8 for A + 8 per B) / 4 MFMAs
       f16x8 b[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) b[f] = decode8(word(braw[f], 0), sc(bsc[f], 0));
@@ -660,15 +681,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
       for (int st = 0; st < kLSteps; ++st) {
         f16x8 bn[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kLMI; ++i) {
           const f16x8 a = decode8(word(araw[i], st), sc(asc[i], st));
-          if (st + 1 < kLSteps) bn[i] = decode8(word(braw[i], st + 1), sc(bsc[i], st + 1));
+          if (st + 1 < kLSteps) {
+#pragma unroll
+            for (int q = 0; q < kBPerI; ++q) {
+              const int f = kBPerI * i + q;
+              bn[f] = decode8(word(braw[f], st + 1), sc(bsc[f], st + 1));
+            }
+          }
 #pragma unroll
           for (int f = 0; f < 4; ++f) acc[i][f] = mfma32(a, b[f], acc[i][f]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, kVPerM, 0);  // its share of the decode
           }
         }
         if (st + 1 < kLSteps) {
@@ -695,10 +722,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
     const float inv = (float)(1.0 / ((double)gs_a * (double)p.w_gs[ti.e]));
     constexpr int pitch = kL1 ? kLOutPitchL1 : kLOutPitchL2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kLMI; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        const int row = wm * (32 * kLMI) + 32 * i + 8 * (r >> 2) + 4 * h2 + (r & 3);
         const bool ok = row < ti.rows_left;
         if (kL1) {
 #pragma unroll
@@ -724,7 +751,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
       const int nrows = ti.rows_left < kLBm ? ti.rows_left : kLBm;
       uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
       const int col0 = ti.nt * cols;
-      for (int idx = tid; idx < nrows * chunks; idx += kGemmThreads) {
+      for (int idx = tid; idx < nrows * chunks; idx += kLThreads) {
         const int r = idx / chunks, c = idx - r * chunks;
         const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * pitch + 16 * c);
         *reinterpret_cast<u32x4*>(out + (int64_t)(ti.row0 + r) * p.N + col0 + 8 * c) = v;
@@ -738,7 +765,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_large_kernel(GemmArgs p)
     __syncthreads();
     if (tid == 0) {
       uint32_t m = s_amax[0];
-      for (int w = 1; w < kGemmThreads / kWave; ++w) m = m > s_amax[w] ? m : s_amax[w];
+      for (int w = 1; w < kLWaves; ++w) m = m > s_amax[w] ? m : s_amax[w];
       p.amax_out[blockIdx.x] = bf16_bits_to_f32(m);
       if (p.clear_other)
         for (int j = (int)blockIdx.x; j < kAmaxSmallSlots; j += kLargeGrid) p.amax_out[kLargeGrid + j] = 0.0f;
@@ -752,7 +779,7 @@ template <bool kL1>
 static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
   a.clear_other = !(c.large && c.small);
   if (c.large) {
-    hipLaunchKernelGGL(gemm_large_kernel<kL1>, dim3(kLargeGrid), dim3(kGemmThreads), 0, stream, a);
+    hipLaunchKernelGGL(gemm_large_kernel<kL1>, dim3(kLargeGrid), dim3(kLThreads), 0, stream, a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
