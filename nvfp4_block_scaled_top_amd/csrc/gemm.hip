@@ -98,11 +98,12 @@ __device__ __forceinline__ float silu_f32(float g) {
 //    row; L2: a y column, i.e. a weight row).  The units of all small m-tiles are laid end to end
 //    and each workgroup takes an equal contiguous range (workgroups on one XCD get neighbouring
 //    ranges, so the A rows of an m-tile stay in that XCD's L2);
-//  * a workgroup walks its range in groups of up to kSNb 16-column MFMA blocks (one m-tile per
-//    group).  Its 4 waves split the reduction dimension K in four and stream the same groups:
-//    one decoded A fragment feeds kSNb MFMAs;
-//  * weights come straight into registers, 16 B per lane per 128-element chunk, through a
-//    kSDepth-deep ring that runs on across group boundaries;
+//  * a workgroup walks its range in groups of up to kSNb (small_nb) 16-column MFMA blocks (one
+//    m-tile per group).  Its 4 waves split the reduction dimension K in four and stream the same
+//    groups: one decoded A fragment feeds kSNb MFMAs;
+//  * weight codes come straight into registers (CH/8 bytes per lane per CH-element chunk)
+//    through a kSDepth-deep ring that runs on across group boundaries; the weights' block scales
+//    are copied per group into LDS by direct-to-LDS loads (kStaged, see below);
 //  * at the end of a group each wave leaves its kSNb partial blocks in LDS (double-buffered by
 //    group parity) and, after one LDS-only barrier (the weight loads stay in flight), wave w adds
 //    the 4 partials of blocks j = w mod 4 in wave order (deterministic) and stores them.
@@ -112,8 +113,11 @@ __device__ __forceinline__ float silu_f32(float g) {
 // matching up rows, paired after the reduction with a lane shuffle.  L2 block j: weight rows
 // j0+16j..+16.
 // ============================================================================================
-#ifndef MEGAMOE_SMALL_NB
-#define MEGAMOE_SMALL_NB 2
+#ifndef MEGAMOE_SMALL_NB_L1
+#define MEGAMOE_SMALL_NB_L1 2
+#endif
+#ifndef MEGAMOE_SMALL_NB_L2
+#define MEGAMOE_SMALL_NB_L2 2
 #endif
 #ifndef MEGAMOE_SMALL_DEPTH
 #define MEGAMOE_SMALL_DEPTH 2
@@ -121,18 +125,23 @@ __device__ __forceinline__ float silu_f32(float g) {
 #ifndef MEGAMOE_SMALL_OCC
 #define MEGAMOE_SMALL_OCC 2
 #endif
-constexpr int kSNb = MEGAMOE_SMALL_NB;        // MFMA column blocks per group (share A)
+template <bool kL1>
+constexpr int small_nb() { return kL1 ? MEGAMOE_SMALL_NB_L1 : MEGAMOE_SMALL_NB_L2; }  // blocks per group
 constexpr int kSDepth = MEGAMOE_SMALL_DEPTH;  // ring slots (chunks in flight per wave)
 constexpr int kSOcc = MEGAMOE_SMALL_OCC;      // workgroups (of 4 waves) per CU
 constexpr int kSWaves = kGemmThreads / kWave; // K split
 constexpr int kLargeGrid = 256;               // large class: one workgroup per CU (LDS ~148 KB)
 constexpr int kSmallGrid = 256 * kSOcc;       // small class: resident workgroups
 constexpr int kAmaxSmallSlots = MEGAMOE_L1_AMAX_PARTS - kLargeGrid;  // slots [kLargeGrid, PARTS)
+#ifndef MEGAMOE_SMALL_STAGED_KB
+#define MEGAMOE_SMALL_STAGED_KB 48
+#endif
+constexpr size_t kSmallStagedMaxLds = MEGAMOE_SMALL_STAGED_KB * 1024;  // 3 staged scale buffers
 static_assert(kSmallGrid <= kAmaxSmallSlots, "one amax slot per small workgroup");
 static_assert(kSmallGrid % kXcds == 0, "grid split");
 
 template <bool kL1>
-constexpr int small_group_units() { return kL1 ? 8 * kSNb : 16 * kSNb; }
+constexpr int small_group_units() { return kL1 ? 8 * small_nb<kL1>() : 16 * small_nb<kL1>(); }
 
 struct SmallGroup {
   int e;          // expert
@@ -142,15 +151,44 @@ struct SmallGroup {
   int n;          // units in the group
 };
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Direct global -> LDS loads.  Issued through inline assembly so that the compiler does not track
+// them as LDS writes (it would otherwise wait for every outstanding load before any LDS read it
+// cannot prove disjoint, draining the prefetch each stage).  Their ordering is explicit instead:
+// wait_vmcnt() for this wave's loads, then s_barrier for everyone's.  The compiler's own vmcnt
+// waits stay correct because loads retire in order.  Nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is written only here (checked in the ISA)
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform; must live in an SGPR for M0
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t* src, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding: vmcnt bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // One chunk of the reduction dimension for one lane: CH/8 code bytes (CH/32 MFMA steps) and
 // CH/64 scale bytes of its A row and of each of its kSNb weight rows.
-template <int CH>
+template <int CH, int NB>
 struct SmallSlot {
   static constexpr int kQ = CH / 128;  // u32x4 words per lane and row (1 or 2)
   u32x4 a[kQ];
   uint32_t as;
-  u32x4 b[kSNb][kQ];
-  uint32_t bs[kSNb];
+  u32x4 b[NB][kQ];
+  uint32_t bs[NB];
 };
 
 // Wave-uniform read through the scalar data cache (the index must be wave-uniform).  Scalar
@@ -172,11 +210,23 @@ __device__ __forceinline__ void lds_barrier() {
 // CH (128 or 256) is the chunk of K a wave step covers: a lane loads CH/8 contiguous code bytes
 // (CH/32 MFMA steps) and CH/64 scale bytes per row.  256 halves the scale loads per weight byte
 // (one u32 instead of one u16 per 128 elements); 128 serves K that is an odd multiple of 128.
-template <bool kL1, int CH>
+// Weight scales staged in LDS (kStaged): a group's rows of weight block scales (row-contiguous in
+// HBM) are copied by full-line direct-to-LDS loads when the loader enters the group, into buffer
+// (group index) % 3, rows padded by 16 bytes so that the 4-byte reads of 16 rows x 4 lanes hit
+// distinct banks.  The steady state then issues no scale loads for the weights (they carried 4
+// bytes per lane and cost as much issue as the 16-byte code loads).  With a ring of kSDepth
+// steps the loader runs at most 2 groups ahead of the compute (one step per group at least), so 3
+// buffers suffice; every wave has issued at least kSDepth steps of loads after its copy of group
+// q+1 when group q ends, so vmcnt <= kSDepth * (loads per step) there (before the group's
+// barrier) means the copy has landed.
+template <bool kL1, int CH, bool kStaged>
 __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArgs p) {
-  using Slot = SmallSlot<CH>;
+  constexpr int kSNb = small_nb<kL1>();
+  using Slot = SmallSlot<CH, kSNb>;
   constexpr int kQ = Slot::kQ;
   constexpr int kLaneBytes = CH / 8, kLaneScales = CH / 64;
+  constexpr int kLoadsPerStep = kQ * (1 + kSNb) + 1 + (kStaged ? 0 : kSNb);
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_scl[];  // [3][scale buffer] if kStaged
   // Per-expert tables in LDS: reading them inside the loop must not wait on the weight stream.
   __shared__ int s_pref[kMaxExperts + 1];
   __shared__ int s_poff[kMaxExperts];
@@ -258,8 +308,34 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
       lb_c[j] = p.w_codes;
       lb_s[j] = p.w_scales;
     }
+    // Staged scales: buffer geometry (pieces of 16 bytes; P per padded row).
+    const int P = Ks / 16 + 1, SRB = 16 * P;
+    const int npieces = kSNb * 16 * P, ndma = (npieces + 63) / 64;
+    const int buf_bytes = ndma * 1024;
+    int lq = 0;  // loader's group index
+    auto weight_row = [&](const SmallGroup& q, int col) -> int64_t {  // MFMA column -> weight row
+      if (kL1) {
+        const int j = col / 16, c = col % 16;
+        const int hc = 8 * j + (c & 7);
+        const int hcol = q.j0 + (hc < q.n ? hc : 0);
+        return (int64_t)q.e * Nw + (c < 8 ? hcol : p.N + hcol);
+      }
+      return (int64_t)q.e * Nw + q.j0 + (col < q.n ? col : 0);
+    };
+    auto stage_scales = [&](const SmallGroup& q, int buf) {
+      const uint32_t base = lds_addr(s_scl + buf * buf_bytes);
+      for (int i = wave; i < ndma; i += kSWaves) {
+        const int pc = 64 * i + lane;
+        const int cr = pc / P, pi = pc - cr * P;
+        const bool real = cr < kSNb * 16 && pi < P - 1;
+        const uint8_t* src = p.w_scales + weight_row(q, real ? cr : 0) * Ks + (real ? 16 * pi : 0);
+        dma16(src, base + 1024 * i);
+      }
+    };
     auto loader_enter = [&](int64_t u) {
       const SmallGroup q = group_at(u);
+      if (kStaged) stage_scales(q, lq % 3);
+      ++lq;
       int64_t arow;
       if (kL1) {
         int tok = sload(p.row_token, q.row0);
@@ -305,7 +381,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
       for (int j = 0; j < kSNb; ++j) {
 #pragma unroll
         for (int q = 0; q < kQ; ++q) d.b[j][q] = *reinterpret_cast<const u32x4*>(lb_c[j] + off + 16 * q);
-        d.bs[j] = load_scale(lb_s[j] + soff);
+        if (!kStaged) d.bs[j] = load_scale(lb_s[j] + soff);
       }
       if (++lc == c1) {
         lc = c0;
@@ -318,7 +394,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
 
     // ---- compute cursor ---------------------------------------------------------------------------
     int64_t cu = u_begin;
-    int cc = c0, parity = 0;
+    int cc = c0, parity = 0, cq = 0;  // cq: compute cursor's group index
     SmallGroup cg{0, 0, 1, 0, 0};
     if (cu < u_end) cg = group_at(cu);
     f32x4 acc[kSNb];
@@ -327,13 +403,26 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
 
     // MFMA step st takes the lane's code word st (8 elements, scale block st / 2).
     auto compute = [&](const Slot& d) {
+      uint32_t bsw[kSNb];
+      if (kStaged) {
+        // this lane's scale bytes of chunk cc for its row in each block (LDS, padded rows)
+        const uint8_t* sb0 = s_scl + (cq % 3) * buf_bytes + r16 * SRB + cc * (CH / 16) + g * kLaneScales;
+#pragma unroll
+        for (int j = 0; j < kSNb; ++j) {
+          if (kLaneScales == 4) bsw[j] = *reinterpret_cast<const uint32_t*>(sb0 + 16 * j * SRB);
+          else bsw[j] = *reinterpret_cast<const uint16_t*>(sb0 + 16 * j * SRB);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kSNb; ++j) bsw[j] = d.bs[j];
+      }
       f16x2 sa[kQ];
       f16x2 sb[kSNb][kQ];
 #pragma unroll
       for (int q = 0; q < kQ; ++q) {
         sa[q] = e4m3x2_to_f16(d.as, q == 1);
 #pragma unroll
-        for (int j = 0; j < kSNb; ++j) sb[j][q] = e4m3x2_to_f16(d.bs[j], q == 1);
+        for (int j = 0; j < kSNb; ++j) sb[j][q] = e4m3x2_to_f16(bsw[j], q == 1);
       }
 #pragma unroll
       for (int st = 0; st < CH / 32; ++st) {
@@ -348,11 +437,17 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
     };
 
     // End of a group: publish the partial blocks, then wave w finishes blocks j = w (mod ks).
-    auto group_end = [&]() {
+    // (Staged scales: the next group's copy has landed for this wave once vmcnt <= kSDepth steps
+    // of loads; in the predicated tail fewer loads follow it, so wait for all.)
+    auto group_end = [&](bool tail) {
 #pragma unroll
       for (int j = 0; j < kSNb; ++j) {
         s_red[parity][wave][j][lane] = acc[j];
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      if (kStaged) {
+        if (tail) wait_vmcnt<0>();
+        else wait_vmcnt<kSDepth * kLoadsPerStep>();
       }
       lds_barrier();
       const float inv = (float)(1.0 / ((double)gs_a * (double)s_wgs[cg.e]));
@@ -384,10 +479,11 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
       }
       parity ^= 1;
     };
-    auto step_done = [&]() {
+    auto step_done = [&](bool tail) {
       if (++cc == c1) {
-        group_end();
+        group_end(tail);
         cc = c0;
+        ++cq;
         cu += cg.n;
         if (cu < u_end) cg = group_at(cu);
       }
@@ -400,13 +496,17 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
     Slot ring[kSDepth];
 #pragma unroll
     for (int k = 0; k < kSDepth; ++k) load(ring[k]);
+    if (kStaged) {  // the first group's scales (issued before the prologue loads) have landed
+      wait_vmcnt<kSDepth * kLoadsPerStep>();
+      lds_barrier();
+    }
     int64_t s0 = 0;
     for (; s0 + 2 * kSDepth <= S; s0 += kSDepth) {
 #pragma unroll
       for (int k = 0; k < kSDepth; ++k) {
         compute(ring[k]);
         load(ring[k]);
-        step_done();
+        step_done(false);
       }
     }
 #pragma unroll
@@ -414,7 +514,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
       if (s0 + i < S) {
         compute(ring[i % kSDepth]);
         if (s0 + i + kSDepth < S) load(ring[i % kSDepth]);
-        step_done();
+        step_done(true);
       }
     }
   }
@@ -497,35 +597,6 @@ static_assert(kLWM == 2 || kLWM == 4, "2x2 or 4x2 waves");
 static_assert(kLCodeDma >= 1 && kLScaleDma >= 1 && kLRowsPerWave * kLScaleRow % 256 == 0, "DMA split");
 static_assert(kLAhead <= kLSlots - 2, "refilled slot must have been read two stages earlier");
 static_assert(kLBm * kLOutPitchL2 <= kLLdsBytes && kLBm * kLOutPitchL1 <= kLLdsBytes, "staging fits");
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-// Direct global -> LDS loads.  Issued through inline assembly so that the compiler does not track
-// them as LDS writes (it would otherwise wait for every outstanding load before any LDS read it
-// cannot prove disjoint, draining the prefetch each stage).  Their ordering is explicit instead:
-// wait_vmcnt() for this wave's loads, then s_barrier for everyone's.  The compiler's own vmcnt
-// waits stay correct because loads retire in order.  Nothing else in these kernels uses M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // M0 is written only here (checked in the ISA)
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(const lds_u8*)p;
-}
-__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
-  lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform; must live in an SGPR for M0
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const uint8_t* src, uint32_t lds) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding: vmcnt bits 3:0 and 15:14).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // Wait until at most `stages_after` (<= kLAhead) later stages' loads are outstanding for this wave.
 template <int K = kLAhead>
@@ -784,10 +855,20 @@ static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
     if (err != hipSuccess) return err;
   }
   if (c.small) {
-    if (a.K % 256 == 0)
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256>), dim3(kSmallGrid), dim3(kGemmThreads), 0, stream, a);
+    // Staged weight scales need every wave on K (K >= 4 chunks) and 3 buffers within 48 KB.
+    const int Ks = a.K / 16, P = Ks / 16 + 1;
+    const size_t buf = (size_t)((small_nb<kL1>() * 16 * P + 63) / 64) * 1024;
+    const int ch = a.K % 256 == 0 ? 256 : 128;
+    const bool staged = a.K / ch >= kSWaves && 3 * buf <= kSmallStagedMaxLds;
+    const size_t dyn = staged ? 3 * buf : 0;
+    if (ch == 256 && staged)
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
+    else if (ch == 256)
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, false>), dim3(kSmallGrid), dim3(kGemmThreads), 0, stream, a);
+    else if (staged)
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 128, true>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
     else
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 128>), dim3(kSmallGrid), dim3(kGemmThreads), 0, stream, a);
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 128, false>), dim3(kSmallGrid), dim3(kGemmThreads), 0, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -2,9 +2,11 @@
 
 Bars: bit-exact for routing tables, FP4 codes, E4M3 scales and global scales; relative Frobenius
 <= 1e-3 for h (L1) and y (L2) when fed the same quantized inputs; <= 1e-2 with cosine >= 0.9999
-end to end.  Workloads: the tiny workload, two medium workloads that mix both tile classes with
-ragged tails, non-local ids, a zero-token expert and padding to 128, and the decode workload at
-its full size (48 local experts of 384, hidden 7168, intermediate 2048, T = 1, 4, 8).
+end to end.  Workloads: the tiny workload, three medium workloads that mix both tile classes with
+ragged tails, non-local ids, a zero-token expert and padding to 128 (one with hidden 2048 and
+intermediate 1024, long enough in K for the staged-scale path of the 16-row kernels), and the
+decode workload at its full size (48 local experts of 384, hidden 7168, intermediate 2048,
+T = 1, 4, 8).
 """
 import numpy as np
 import pytest
@@ -20,6 +22,9 @@ pytestmark = pytest.mark.gpu
 
 MID = synth.Workload("mid_zipf_e24", 32, 4, 512, 256, (300,), 0, 24, 1, zipf=True)
 MID_PAD = synth.Workload("mid_zipf_e16_pad128", 32, 4, 512, 256, (150,), 8, 16, 128, zipf=True)
+# K of at least 4 chunks of 256 in both GEMMs (hidden 2048, intermediate 1024): the 16-row tile
+# kernels take the path with weight scales staged in LDS; Zipf routing leaves both tile classes.
+MID_K = synth.Workload("mid_k_e12", 24, 4, 2048, 1024, (160,), 4, 12, 1, zipf=True)
 TINY = synth.WORKLOADS[0]
 DECODE = synth.WORKLOADS[1]
 
@@ -58,7 +63,8 @@ def check_tables(L, ref):
     assert sched[1] == small.sum() and sched[2] == large.sum()
 
 
-@pytest.mark.parametrize("wl,T", [(TINY, 16), (MID, 300), (MID_PAD, 150)], ids=["tiny", "mid", "mid_pad128"])
+@pytest.mark.parametrize("wl,T", [(TINY, 16), (MID, 300), (MID_PAD, 150), (MID_K, 160)],
+                         ids=["tiny", "mid", "mid_pad128", "mid_k2048"])
 def test_layer_end_to_end_and_stages(wl, T):
     s = setup_for(wl, T)
     log(f"[run] {wl.name} T={T}: GPU layer")
@@ -97,7 +103,8 @@ def test_layer_end_to_end_and_stages(wl, T):
     assert np.all(np_i32(L.out[:T].view(torch.int16))[none_local] == 0)
 
 
-@pytest.mark.parametrize("wl,T", [(TINY, 16), (MID, 300), (MID_PAD, 150)], ids=["tiny", "mid", "mid_pad128"])
+@pytest.mark.parametrize("wl,T", [(TINY, 16), (MID, 300), (MID_PAD, 150), (MID_K, 160)],
+                         ids=["tiny", "mid", "mid_pad128", "mid_k2048"])
 def test_stage_inputs_from_oracle(wl, T):
     """Requantize h, L2 and combine, each fed the oracle's own inputs for that stage."""
     s = setup_for(wl, T)
