@@ -97,14 +97,20 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
 }
 
-// 4-bit code of one element: sign of x, magnitude = nearest E2M1 index with ties to even.
+// 4-bit code of one element: sign of x, magnitude = nearest E2M1 index with ties to even.  The
+// magnitude is the number of midpoints t[i] = m_i * s that x * gs passes (">=" where the tie goes
+// up to the even code: 0.75, 1.75, 3.5; ">" elsewhere).  The thresholds increase, so passing one
+// implies passing every lower one, and a binary search over them (3 tests instead of 7) gives the
+// same count; each test is the sign of one exactly-rounded fma residual.
 __device__ __forceinline__ uint32_t e2m1_code(uint32_t xbits, float gs, const float t[7], bool zero_scale) {
   const float a = bf16_bits_to_f32(xbits & 0x7FFFu);
   uint32_t mag = 0;
   if (!zero_scale) {
-    mag = (fmaf(a, gs, -t[0]) > 0.0f) + (fmaf(a, gs, -t[1]) >= 0.0f) + (fmaf(a, gs, -t[2]) > 0.0f) +
-          (fmaf(a, gs, -t[3]) >= 0.0f) + (fmaf(a, gs, -t[4]) > 0.0f) + (fmaf(a, gs, -t[5]) >= 0.0f) +
-          (fmaf(a, gs, -t[6]) > 0.0f);
+    const bool b2 = fmaf(a, gs, -t[3]) >= 0.0f;                     // >= 1.75 s: magnitude >= 4
+    const bool b1 = fmaf(a, gs, -(b2 ? t[5] : t[1])) >= 0.0f;       // >= 3.5 s or >= 0.75 s
+    const float t0 = b2 ? (b1 ? t[6] : t[4]) : (b1 ? t[2] : t[0]);  // 5, 2.5, 1.25 or 0.25 s
+    const bool b0 = fmaf(a, gs, -t0) > 0.0f;
+    mag = (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
   }
   return ((xbits >> 12) & 8u) | mag;
 }
