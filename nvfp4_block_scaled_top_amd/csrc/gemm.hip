@@ -92,26 +92,30 @@ __device__ __forceinline__ float silu_f32(float g) {
 // ============================================================================================
 // Small class (m-tiles of 16 token rows; experts with few tokens, e.g. decode).  Each weight byte
 // feeds one 16-row MFMA block, so the kernel streams weights, and decoding NVFP4 to fp16 costs
-// about 2 VALU instructions per weight byte and lane -- the VALU, not HBM, is what runs out
-// first.  The design keeps the VALU work per weight byte low and every workgroup equally busy:
-//  * work unit = one output column of one m-tile (L1: an h column, i.e. a gate row and its up
-//    row; L2: a y column, i.e. a weight row).  The units of all small m-tiles are laid end to end
-//    and each workgroup takes an equal contiguous range (workgroups on one XCD get neighbouring
-//    ranges, so the A rows of an m-tile stay in that XCD's L2);
-//  * a workgroup walks its range in groups of up to kSNb (small_nb) 16-column MFMA blocks (one
-//    m-tile per group).  Its 4 waves split the reduction dimension K in four and stream the same
-//    groups: one decoded A fragment feeds kSNb MFMAs;
-//  * weight codes come straight into registers (CH/8 bytes per lane per CH-element chunk)
-//    through a kSDepth-deep ring that runs on across group boundaries; the weights' block scales
-//    are copied per group into LDS by direct-to-LDS loads (kStaged, see below);
-//  * at the end of a group each wave leaves its kSNb partial blocks in LDS (double-buffered by
-//    group parity) and, after one LDS-only barrier (the weight loads stay in flight), wave w adds
-//    the 4 partials of blocks j = w mod 4 in wave order (deterministic) and stores them.
+// about 2 VALU instructions per weight byte and lane; the design keeps every other VALU cost per
+// weight byte small and every CU equally busy:
+//  * work unit = a group: kSNb (small_nb) 16-column MFMA blocks of one m-tile over the whole K
+//    (L1 block j: MFMA columns 0-7 are gate rows of h columns j0+8j.., columns 8-15 the matching
+//    up rows, paired after the reduction with a lane shuffle; L2 block j: weight rows j0+16j..).
+//    The groups of all small m-tiles are laid end to end and each workgroup takes an equal
+//    contiguous range of whole groups.  The two workgroups that share a CU take neighbouring
+//    ranges and the workgroups of one XCD a contiguous eighth (the A rows of an m-tile stay in
+//    that XCD's L2);
+//  * the 4 waves of a workgroup split K four ways and stream the same groups: weight codes come
+//    straight into registers (CH/8 bytes per lane per CH-element chunk) through a kSDepth-deep
+//    ring that runs on across group boundaries; the weights' block scales are copied per group
+//    into LDS by direct-to-LDS loads (kStaged, see below);
+//  * the A operand takes one of two forms.  M-tiles with at most kTinyRows = 512/CH token rows
+//    (every m-tile at decode) run first, as the "tiny" phase: a lane loads one code word and one
+//    scale byte of a dense [rows x CH] A chunk, decodes its 8 elements once, and the MFMA
+//    fragments are read back from a per-wave LDS buffer (rows past the m-tile read row 0), so the
+//    A operand costs 9 VALU per chunk instead of 8 per MFMA step.  The other m-tiles ("regular"
+//    phase) gather each lane's A row and decode it per MFMA step, shared by the group's blocks;
+//  * at the end of a group each wave leaves its partial blocks in LDS (double-buffered by group
+//    parity) and, after one LDS-only barrier (the weight loads stay in flight), wave w adds the
+//    partials of accumulator row w of every block in wave order (deterministic) and stores them.
 // Lanes whose row lies outside the group or m-tile load a valid row of the same tile instead; the
 // MFMA outputs they feed are never stored.
-// L1 block j of a group: MFMA columns 0-7 are gate rows of h columns j0+8j.., columns 8-15 the
-// matching up rows, paired after the reduction with a lane shuffle.  L2 block j: weight rows
-// j0+16j..+16.
 // ============================================================================================
 #ifndef MEGAMOE_SMALL_NB_L1
 #define MEGAMOE_SMALL_NB_L1 2
@@ -133,15 +137,23 @@ constexpr int kSWaves = kGemmThreads / kWave; // K split
 constexpr int kLargeGrid = 256;               // large class: one workgroup per CU (LDS ~148 KB)
 constexpr int kSmallGrid = 256 * kSOcc;       // small class: resident workgroups
 constexpr int kAmaxSmallSlots = MEGAMOE_L1_AMAX_PARTS - kLargeGrid;  // slots [kLargeGrid, PARTS)
-#ifndef MEGAMOE_SMALL_STAGED_KB
-#define MEGAMOE_SMALL_STAGED_KB 48
-#endif
-constexpr size_t kSmallStagedMaxLds = MEGAMOE_SMALL_STAGED_KB * 1024;  // 3 staged scale buffers
+// Dynamic LDS of the small class: the per-expert tables, then 3 staged scale buffers if kStaged.
+// With kSOcc = 2 a workgroup may use 80 KB; the static arrays take about 21 KB of it.
+constexpr size_t kSmallDynMaxLds = 58 * 1024;
 static_assert(kSmallGrid <= kAmaxSmallSlots, "one amax slot per small workgroup");
-static_assert(kSmallGrid % kXcds == 0, "grid split");
+static_assert(kSmallGrid % kXcds == 0 && (kSmallGrid / kXcds) % kSOcc == 0, "grid split");
 
 template <bool kL1>
 constexpr int small_group_units() { return kL1 ? 8 * small_nb<kL1>() : 16 * small_nb<kL1>(); }
+
+// Bytes of the per-expert tables at the start of the small class's dynamic LDS (16-aligned).
+__host__ __device__ inline size_t small_table_bytes(int E) { return (((size_t)5 * E + 1) * 4 + 15) / 16 * 16; }
+// Bytes of one staged scale buffer: kSNb x 16 weight rows of Ks scale bytes, each row padded to
+// (Ks/16 + 1) pieces of 16 bytes, rounded up to whole 1024-byte DMA instructions.
+__host__ __device__ inline size_t small_scale_buf_bytes(int nb, int K) {
+  const int P = K / 256 + 1;
+  return (size_t)((nb * 16 * P + 63) / 64) * 1024;
+}
 
 struct SmallGroup {
   int e;          // expert
@@ -180,12 +192,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// One chunk of the reduction dimension for one lane: CH/8 code bytes (CH/32 MFMA steps) and
-// CH/64 scale bytes of its A row and of each of its kSNb weight rows.
-template <int CH, int NB>
+// One chunk of the reduction dimension for one lane: CH/8 code bytes (CH/32 MFMA steps) of each
+// of its kSNb weight rows, and its A operand: regular phase, CH/8 code bytes and CH/64 scale
+// bytes of its A row; tiny phase, one code word (8 elements) and one scale byte of the dense
+// A chunk.
+template <int CH, int NB, bool kTiny>
 struct SmallSlot {
-  static constexpr int kQ = CH / 128;  // u32x4 words per lane and row (1 or 2)
-  u32x4 a[kQ];
+  static constexpr int kQ = CH / 128;  // u32x4 words per lane and weight row (1 or 2)
+  static constexpr int kAQ = kTiny ? 1 : kQ;
+  u32x4 a[kAQ];  // tiny: a[0].x only
   uint32_t as;
   u32x4 b[NB][kQ];
   uint32_t bs[NB];
@@ -207,98 +222,196 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+template <bool V>
+struct BoolTag {
+  static constexpr bool value = V;
+};
+
 // CH (128 or 256) is the chunk of K a wave step covers: a lane loads CH/8 contiguous code bytes
-// (CH/32 MFMA steps) and CH/64 scale bytes per row.  256 halves the scale loads per weight byte
-// (one u32 instead of one u16 per 128 elements); 128 serves K that is an odd multiple of 128.
+// (CH/32 MFMA steps) per weight row.  256 halves the scale traffic per weight byte; 128 serves K
+// that is an odd multiple of 128.
 // Weight scales staged in LDS (kStaged): a group's rows of weight block scales (row-contiguous in
 // HBM) are copied by full-line direct-to-LDS loads when the loader enters the group, into buffer
 // (group index) % 3, rows padded by 16 bytes so that the 4-byte reads of 16 rows x 4 lanes hit
-// distinct banks.  The steady state then issues no scale loads for the weights (they carried 4
-// bytes per lane and cost as much issue as the 16-byte code loads).  With a ring of kSDepth
-// steps the loader runs at most 2 groups ahead of the compute (one step per group at least), so 3
-// buffers suffice; every wave has issued at least kSDepth steps of loads after its copy of group
-// q+1 when group q ends, so vmcnt <= kSDepth * (loads per step) there (before the group's
-// barrier) means the copy has landed.
+// distinct banks.  The steady state then issues no scale loads for the weights.  With a ring of
+// kSDepth steps the loader runs at most 2 groups ahead of the compute (one step per group at
+// least), so 3 buffers suffice; every wave has issued at least kSDepth steps of loads after its
+// copy of group q+1 when group q ends, so vmcnt <= kSDepth * (loads per step) there (before the
+// group's barrier) means the copy has landed.
 template <bool kL1, int CH, bool kStaged>
 __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArgs p) {
   constexpr int kSNb = small_nb<kL1>();
-  using Slot = SmallSlot<CH, kSNb>;
-  constexpr int kQ = Slot::kQ;
+  constexpr int kQ = CH / 128;
   constexpr int kLaneBytes = CH / 8, kLaneScales = CH / 64;
-  constexpr int kLoadsPerStep = kQ * (1 + kSNb) + 1 + (kStaged ? 0 : kSNb);
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_scl[];  // [3][scale buffer] if kStaged
-  // Per-expert tables in LDS: reading them inside the loop must not wait on the weight stream.
-  __shared__ int s_pref[kMaxExperts + 1];
-  __shared__ int s_poff[kMaxExperts];
-  __shared__ int s_cnt[kMaxExperts];
-  __shared__ float s_wgs[kMaxExperts];
+  constexpr int kPieces = CH / 8;               // 8-element pieces per row and chunk
+  constexpr int kTinyRows = kWave / kPieces;    // rows of a dense A chunk (2 or 4)
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
   __shared__ f32x4 s_red[2][kSWaves][kSNb][kWave];
+  __shared__ f16x8 s_afrag[kSWaves][kWave];  // tiny phase: this chunk's decoded A pieces
   __shared__ uint32_t s_amax[kSWaves];
+  __shared__ int s_ntiny;
   const int E = p.E;
-  const int32_t* __restrict__ sched = p.sched;
-  for (int j = threadIdx.x; j <= E; j += blockDim.x) {
-    s_pref[j] = sched[sched_pref_small(E) + j];
-    if (j < E) {
+  // Per-expert tables (LDS; reading them inside the loop must not wait on the weight stream):
+  int* s_pref = reinterpret_cast<int*>(s_dyn);  // [E+1] exclusive prefix of regular small m-tiles
+  int* s_poff = s_pref + E + 1;                 // [E] first padded row
+  int* s_cnt = s_poff + E;                      // [E] tokens
+  float* s_inv = reinterpret_cast<float*>(s_cnt + E);  // [E] 1 / (gs_a * gs_w[e])
+  int* s_tiny = reinterpret_cast<int*>(s_inv + E);    // experts whose one m-tile is tiny
+  uint8_t* s_scl = s_dyn + small_table_bytes(E);      // [3][scale buffer] if kStaged
+  const float gs_a = *p.a_gs;
+  {
+    const int32_t* __restrict__ pref = p.sched + sched_pref_small(E);
+    for (int j = threadIdx.x; j < E; j += blockDim.x) {
       s_poff[j] = p.padded_offsets[j];
       s_cnt[j] = p.counts[j];
-      s_wgs[j] = p.w_gs[j];
+      s_inv[j] = (float)(1.0 / ((double)gs_a * (double)p.w_gs[j]));
+      s_pref[j] = pref[j + 1] - pref[j];  // small m-tiles of expert j (scanned below)
     }
+    __syncthreads();
+    if (threadIdx.x < kWave) {  // wave 0: split the small m-tiles into tiny and regular
+      const int lane = lane_id();
+      int reg_carry = 0, tiny_carry = 0;
+      for (int c = 0; c < E; c += kWave) {
+        const int e = c + lane;
+        const int nt = e < E ? s_pref[e] : 0;
+        const int cnt = e < E ? s_cnt[e] : 0;
+        const bool tiny = nt == 1 && cnt <= kTinyRows;
+        const int reg = tiny ? 0 : nt;
+        int incl = reg;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int t = __shfl_up(incl, o, kWave);
+          if (lane >= o) incl += t;
+        }
+        const uint64_t mask = __ballot(tiny);
+        const int tpos = tiny_carry + __popcll(mask & ((1ull << lane) - 1));
+        if (e < E) s_pref[e] = reg_carry + incl - reg;
+        if (tiny) s_tiny[tpos] = e;
+        reg_carry += __shfl(incl, kWave - 1, kWave);
+        tiny_carry += __popcll(mask);
+      }
+      if (lane == 0) {
+        s_pref[E] = reg_carry;
+        s_ntiny = tiny_carry;
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
   const int NU = p.N;  // units per m-tile: L1 h columns (I), L2 output columns (H)
   constexpr int GU = small_group_units<kL1>();
-  const int64_t U = (int64_t)s_pref[E] * NU;
+  const int Gm = (NU + GU - 1) / GU;  // groups per m-tile
   const int K = p.K, Kh = K / 2, Ks = K / 16;
   const int Nw = kL1 ? 2 * p.N : p.N;  // weight rows per expert
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int r16 = lane & 15, g = lane >> 4;
   const int nch = K / CH;
-  const int ks = nch < kSWaves ? nch : kSWaves;  // waves sharing K (all 4 unless K < 512)
+  const int ks = nch < kSWaves ? nch : kSWaves;  // waves sharing K (all 4 unless K < 4 chunks)
   const int c0 = wave < ks ? wave * nch / ks : 0, c1 = wave < ks ? (wave + 1) * nch / ks : 0;
-  const float gs_a = *p.a_gs;
   uint32_t amax_bits = 0;
+  int parity = 0;  // s_red buffer of the next group end (continues across phases)
 
-  // This workgroup's unit range; workgroup b runs on XCD b % 8.
-  const int G = gridDim.x, b = blockIdx.x;
-  const int64_t lb = (int64_t)(b % kXcds) * (G / kXcds) + b / kXcds;
-  const int64_t u_begin = lb * U / G, u_end = (lb + 1) * U / G;
+  // This workgroup's position: workgroup b runs on XCD b % 8; the kSOcc workgroups of a CU (XCD-
+  // local indices i and i + 256/8) get neighbouring positions.
+  const int G = kSmallGrid, b = blockIdx.x;
+  constexpr int kPerXcd = kSmallGrid / kXcds, kCusPerXcd = kPerXcd / kSOcc;
+  const int xi = b / kXcds;
+  const int64_t lb = (int64_t)(b % kXcds) * kPerXcd + (xi % kCusPerXcd) * kSOcc + xi / kCusPerXcd;
 
-  // Number of groups in [u_begin, u_end): groups never cross an m-tile.
-  int64_t ngroups = 0;
-  if (u_begin < u_end) {
-    const int64_t ma = u_begin / NU, mb = (u_end - 1) / NU;
-    if (ma == mb) {
-      ngroups = (u_end - u_begin + GU - 1) / GU;
-    } else {
-      ngroups = ((ma + 1) * NU - u_begin + GU - 1) / GU + (mb - ma - 1) * ((NU + GU - 1) / GU) +
-                (u_end - mb * NU + GU - 1) / GU;
+  // Staged scales: buffer geometry (pieces of 16 bytes; P per padded row).
+  const int P = Ks / 16 + 1, SRB = 16 * P;
+  const int ndma = (kSNb * 16 * P + 63) / 64;
+  const int buf_bytes = ndma * 1024;
+  const float invP = 1.0f / (float)P;
+
+  // One phase: the tiny m-tiles (kTiny) or the regular ones, as a list of groups.
+  auto run_phase = [&](auto tiny_tag) {
+    constexpr bool kTiny = decltype(tiny_tag)::value;
+    using Slot = SmallSlot<CH, kSNb, kTiny>;
+    constexpr int kLoadsPerStep = (kTiny ? 2 : kQ + 1) + kSNb * kQ + (kStaged ? 0 : kSNb);
+    const int nm = kTiny ? s_ntiny : s_pref[E];
+    const int64_t Gt = (int64_t)nm * Gm;
+    const int64_t g_begin = lb * Gt / G, g_end = (lb + 1) * Gt / G;
+    const int ngroups = (int)(g_end - g_begin);
+    if (ngroups == 0) return;
+
+    // Group cursor: m-tile mt (index in this phase's list), group gi within it, and its expert.
+    struct Cursor {
+      int mt, gi, e;
+    };
+    auto cursor_at = [&](int64_t gidx) {
+      Cursor c;
+      c.mt = (int)(gidx / Gm);
+      c.gi = (int)(gidx - (int64_t)c.mt * Gm);
+      c.e = kTiny ? s_tiny[c.mt] : find_expert(s_pref, E, 1, c.mt);
+      return c;
+    };
+    auto cursor_next = [&](Cursor& c) {
+      if (++c.gi == Gm) {
+        c.gi = 0;
+        ++c.mt;
+        if (kTiny) c.e = s_tiny[c.mt];
+        else
+          while (s_pref[c.e + 1] <= c.mt) ++c.e;
+      }
+    };
+    auto group_of = [&](const Cursor& c) {
+      SmallGroup q;
+      q.e = c.e;
+      const int local = kTiny ? 0 : c.mt - s_pref[c.e];
+      q.row0 = s_poff[c.e] + local * kBlockMSmall;
+      q.rows_left = s_cnt[c.e] - local * kBlockMSmall;
+      q.j0 = c.gi * GU;
+      q.n = NU - q.j0 < GU ? NU - q.j0 : GU;
+      return q;
+    };
+
+    // End of a group: publish the partial blocks; after the barrier wave w adds accumulator row
+    // w of every block in wave order and writes it out.
+    auto group_epilogue = [&](const SmallGroup& cg) {
+      const float inv = s_inv[cg.e];
+      const float* red = reinterpret_cast<const float*>(&s_red[parity][0][0][0]);
+      uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
+      const int row = 4 * g + wave;  // MFMA output row of accumulator element `wave`
+#pragma unroll
+      for (int j = 0; j < kSNb; ++j) {
+        float r = red[((0 * kSNb + j) * kWave + lane) * 4 + wave];
+        for (int w = 1; w < ks; ++w) r += red[((w * kSNb + j) * kWave + lane) * 4 + wave];
+        if (kL1) {
+          const float up_raw = __shfl(r, lane + 8, kWave);  // column c+8 holds the up row of c
+          const int hc = 8 * j + r16;
+          if (r16 < 8 && hc < cg.n && row < cg.rows_left) {
+            const float gt = r * inv, up = up_raw * inv;
+            const uint32_t hb = f32_to_bf16_bits(silu_f32(gt) * up);
+            out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + hc] = (uint16_t)hb;
+            const uint32_t mag = hb & 0x7FFFu;
+            amax_bits = amax_bits > mag ? amax_bits : mag;
+          }
+        } else {
+          const int rc = 16 * j + r16;
+          if (rc < cg.n && row < cg.rows_left)
+            out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + rc] = (uint16_t)f32_to_bf16_bits(r * inv);
+        }
+      }
+      parity ^= 1;
+    };
+
+    if (c1 == c0) {
+      // K has fewer than 4 chunks and this wave has none: it keeps the barrier count and takes
+      // its share of the epilogues.
+      Cursor cc = cursor_at(g_begin);
+      for (int q = 0; q < ngroups; ++q) {
+        lds_barrier();
+        group_epilogue(group_of(cc));
+        if (q + 1 < ngroups) cursor_next(cc);
+      }
+      return;
     }
-  }
 
-  auto group_at = [&](int64_t u) {
-    SmallGroup q;
-    const int mtg = (int)(u / NU);
-    q.e = find_expert(s_pref, E, 1, mtg);
-    const int mt = mtg - s_pref[q.e];
-    q.row0 = s_poff[q.e] + mt * kBlockMSmall;
-    q.rows_left = s_cnt[q.e] - mt * kBlockMSmall;
-    q.j0 = (int)(u - (int64_t)mtg * NU);
-    int64_t n = u_end - u;
-    if (n > NU - q.j0) n = NU - q.j0;
-    if (n > GU) n = GU;
-    q.n = (int)n;
-    return q;
-  };
-
-  if (c1 == c0) {
-    // K has fewer than 4 chunks and this wave has none: it only keeps the barrier count.
-    for (int64_t q = 0; q < ngroups; ++q) lds_barrier();
-  } else {
-    // ---- loader cursor: group being loaded, this lane's row pointers, next chunk --------------
+    // ---- loader: group being loaded, this lane's row pointers, next chunk ----------------------
     // Past the last step the loader keeps re-reading its last group's first chunk (valid memory,
     // never consumed), so every step issues the same loads.
-    int64_t lu = u_begin;
-    int lc = c0, ln = 0;
+    Cursor lcur = cursor_at(g_begin);
+    int lgrp = 0, lc = c0;
     const uint8_t* la_c = p.a_codes;
     const uint8_t* la_s = p.a_scales;
     const uint8_t* lb_c[kSNb];
@@ -308,11 +421,6 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
       lb_c[j] = p.w_codes;
       lb_s[j] = p.w_scales;
     }
-    // Staged scales: buffer geometry (pieces of 16 bytes; P per padded row).
-    const int P = Ks / 16 + 1, SRB = 16 * P;
-    const int npieces = kSNb * 16 * P, ndma = (npieces + 63) / 64;
-    const int buf_bytes = ndma * 1024;
-    int lq = 0;  // loader's group index
     auto weight_row = [&](const SmallGroup& q, int col) -> int64_t {  // MFMA column -> weight row
       if (kL1) {
         const int j = col / 16, c = col % 16;
@@ -326,31 +434,54 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
       const uint32_t base = lds_addr(s_scl + buf * buf_bytes);
       for (int i = wave; i < ndma; i += kSWaves) {
         const int pc = 64 * i + lane;
-        const int cr = pc / P, pi = pc - cr * P;
+        const int cr = (int)(((float)pc + 0.5f) * invP);  // pc / P (exact for pc < 2^21)
+        const int pi = pc - cr * P;
         const bool real = cr < kSNb * 16 && pi < P - 1;
         const uint8_t* src = p.w_scales + weight_row(q, real ? cr : 0) * Ks + (real ? 16 * pi : 0);
         dma16(src, base + 1024 * i);
       }
     };
-    auto loader_enter = [&](int64_t u) {
-      const SmallGroup q = group_at(u);
-      if (kStaged) stage_scales(q, lq % 3);
-      ++lq;
-      int64_t arow;
-      if (kL1) {
-        int tok = sload(p.row_token, q.row0);
-        for (int i = 1; i < kBlockMSmall; ++i) {
-          if (i < q.rows_left) {
-            const int t = sload(p.row_token, q.row0 + i);
-            tok = r16 == i ? t : tok;
+    auto loader_enter = [&]() {
+      const SmallGroup q = group_of(lcur);
+      if (kStaged) stage_scales(q, lgrp % 3);
+      ++lgrp;
+      if (kTiny) {
+        // dense A: lane -> (row lane / kPieces, piece lane % kPieces); rows past the m-tile read
+        // row 0
+        const int rr = lane / kPieces, pc = lane % kPieces;
+        int64_t arow;
+        if (kL1) {
+          int tok = sload(p.row_token, q.row0);
+#pragma unroll
+          for (int i = 1; i < kTinyRows; ++i) {
+            if (i < q.rows_left) {
+              const int t = sload(p.row_token, q.row0 + i);
+              tok = rr == i ? t : tok;
+            }
           }
+          arow = tok;
+        } else {
+          arow = q.row0 + (rr < q.rows_left ? rr : 0);
         }
-        arow = tok;
+        la_c = p.a_codes + arow * Kh + 4 * pc;
+        la_s = p.a_scales + arow * Ks + pc / 2;
       } else {
-        arow = q.row0 + (r16 < q.rows_left ? r16 : 0);
+        int64_t arow;
+        if (kL1) {
+          int tok = sload(p.row_token, q.row0);
+          for (int i = 1; i < kBlockMSmall; ++i) {
+            if (i < q.rows_left) {
+              const int t = sload(p.row_token, q.row0 + i);
+              tok = r16 == i ? t : tok;
+            }
+          }
+          arow = tok;
+        } else {
+          arow = q.row0 + (r16 < q.rows_left ? r16 : 0);
+        }
+        la_c = p.a_codes + arow * Kh + g * kLaneBytes;
+        la_s = p.a_scales + arow * Ks + g * kLaneScales;
       }
-      la_c = p.a_codes + arow * Kh + g * kLaneBytes;
-      la_s = p.a_scales + arow * Ks + g * kLaneScales;
 #pragma unroll
       for (int j = 0; j < kSNb; ++j) {
         int64_t brow;
@@ -365,18 +496,22 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
         lb_c[j] = p.w_codes + brow * Kh + g * kLaneBytes;
         lb_s[j] = p.w_scales + brow * Ks + g * kLaneScales;
       }
-      ln = q.n;
     };
-    if (u_begin < u_end) loader_enter(u_begin);
+    loader_enter();
     auto load_scale = [](const uint8_t* q) -> uint32_t {
       if (kLaneScales == 4) return *reinterpret_cast<const uint32_t*>(q);
       return *reinterpret_cast<const uint16_t*>(q);
     };
     auto load = [&](Slot& d) {
       const int64_t off = (int64_t)lc * (CH / 2), soff = (int64_t)lc * (CH / 16);
+      if (kTiny) {
+        d.a[0].x = *reinterpret_cast<const uint32_t*>(la_c + off);
+        d.as = *(la_s + soff);
+      } else {
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) d.a[q] = *reinterpret_cast<const u32x4*>(la_c + off + 16 * q);
-      d.as = load_scale(la_s + soff);
+        for (int q = 0; q < kQ; ++q) d.a[q] = *reinterpret_cast<const u32x4*>(la_c + off + 16 * q);
+        d.as = load_scale(la_s + soff);
+      }
 #pragma unroll
       for (int j = 0; j < kSNb; ++j) {
 #pragma unroll
@@ -385,28 +520,30 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
       }
       if (++lc == c1) {
         lc = c0;
-        if (lu + ln < u_end) {
-          lu += ln;
-          loader_enter(lu);
+        if (lgrp < ngroups) {
+          cursor_next(lcur);
+          loader_enter();
         }
       }
     };
 
     // ---- compute cursor ---------------------------------------------------------------------------
-    int64_t cu = u_begin;
-    int cc = c0, parity = 0, cq = 0;  // cq: compute cursor's group index
-    SmallGroup cg{0, 0, 1, 0, 0};
-    if (cu < u_end) cg = group_at(cu);
+    Cursor ccur = cursor_at(g_begin);
+    SmallGroup cg = group_of(ccur);
+    int cc = c0, cgrp = 0;  // chunk, group index
     f32x4 acc[kSNb];
 #pragma unroll
     for (int j = 0; j < kSNb; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Tiny phase: MFMA step st of lane L takes piece (CH/32)*(L/16) + st of row (L % 16), or of
+    // row 0 when that row is past the m-tile.
+    int tsrc = (r16 < cg.rows_left ? r16 : 0) * kPieces + (CH / 32) * g;
 
     // MFMA step st takes the lane's code word st (8 elements, scale block st / 2).
     auto compute = [&](const Slot& d) {
       uint32_t bsw[kSNb];
       if (kStaged) {
         // this lane's scale bytes of chunk cc for its row in each block (LDS, padded rows)
-        const uint8_t* sb0 = s_scl + (cq % 3) * buf_bytes + r16 * SRB + cc * (CH / 16) + g * kLaneScales;
+        const uint8_t* sb0 = s_scl + (cgrp % 3) * buf_bytes + r16 * SRB + cc * (CH / 16) + g * kLaneScales;
 #pragma unroll
         for (int j = 0; j < kSNb; ++j) {
           if (kLaneScales == 4) bsw[j] = *reinterpret_cast<const uint32_t*>(sb0 + 16 * j * SRB);
@@ -416,27 +553,40 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
 #pragma unroll
         for (int j = 0; j < kSNb; ++j) bsw[j] = d.bs[j];
       }
-      f16x2 sa[kQ];
       f16x2 sb[kSNb][kQ];
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        sa[q] = e4m3x2_to_f16(d.as, q == 1);
+      for (int q = 0; q < kQ; ++q)
 #pragma unroll
         for (int j = 0; j < kSNb; ++j) sb[j][q] = e4m3x2_to_f16(bsw[j], q == 1);
-      }
+      if (kTiny) {
+        s_afrag[wave][lane] = decode8(d.a[0].x, bcast_lo(e4m3x2_to_f16(d.as, false)));
 #pragma unroll
-      for (int st = 0; st < CH / 32; ++st) {
-        const int q = st / 4, w4 = st % 4;
-        const f16x8 a = decode8(d.a[q][w4], w4 < 2 ? bcast_lo(sa[q]) : bcast_hi(sa[q]));
+        for (int st = 0; st < CH / 32; ++st) {
+          const int q = st / 4, w4 = st % 4;
+          const f16x8 a = s_afrag[wave][tsrc + st];
 #pragma unroll
-        for (int j = 0; j < kSNb; ++j) {
-          const f16x8 w = decode8(d.b[j][q][w4], w4 < 2 ? bcast_lo(sb[j][q]) : bcast_hi(sb[j][q]));
-          acc[j] = mfma16(a, w, acc[j]);
+          for (int j = 0; j < kSNb; ++j) {
+            const f16x8 w = decode8(d.b[j][q][w4], w4 < 2 ? bcast_lo(sb[j][q]) : bcast_hi(sb[j][q]));
+            acc[j] = mfma16(a, w, acc[j]);
+          }
+        }
+      } else {
+        f16x2 sa[kQ];
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) sa[q] = e4m3x2_to_f16(d.as, q == 1);
+#pragma unroll
+        for (int st = 0; st < CH / 32; ++st) {
+          const int q = st / 4, w4 = st % 4;
+          const f16x8 a = decode8(d.a[q][w4], w4 < 2 ? bcast_lo(sa[q]) : bcast_hi(sa[q]));
+#pragma unroll
+          for (int j = 0; j < kSNb; ++j) {
+            const f16x8 w = decode8(d.b[j][q][w4], w4 < 2 ? bcast_lo(sb[j][q]) : bcast_hi(sb[j][q]));
+            acc[j] = mfma16(a, w, acc[j]);
+          }
         }
       }
     };
 
-    // End of a group: publish the partial blocks, then wave w finishes blocks j = w (mod ks).
     // (Staged scales: the next group's copy has landed for this wave once vmcnt <= kSDepth steps
     // of loads; in the predicated tail fewer loads follow it, so wait for all.)
     auto group_end = [&](bool tail) {
@@ -450,49 +600,25 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
         else wait_vmcnt<kSDepth * kLoadsPerStep>();
       }
       lds_barrier();
-      const float inv = (float)(1.0 / ((double)gs_a * (double)s_wgs[cg.e]));
-      uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
-#pragma unroll
-      for (int j = 0; j < kSNb; ++j) {
-        if (j % ks != wave) continue;
-        f32x4 r = s_red[parity][0][j][lane];
-        for (int w = 1; w < ks; ++w) r += s_red[parity][w][j][lane];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = 4 * g + q;
-          if (kL1) {
-            const float up_raw = __shfl(r[q], lane + 8, kWave);  // column c+8 holds the up row of c
-            const int hc = 8 * j + r16;
-            if (r16 < 8 && hc < cg.n && row < cg.rows_left) {
-              const float gt = r[q] * inv, up = up_raw * inv;
-              const uint32_t hb = f32_to_bf16_bits(silu_f32(gt) * up);
-              out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + hc] = (uint16_t)hb;
-              const uint32_t mag = hb & 0x7FFFu;
-              amax_bits = amax_bits > mag ? amax_bits : mag;
-            }
-          } else {
-            const int rc = 16 * j + r16;
-            if (rc < cg.n && row < cg.rows_left)
-              out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + rc] = (uint16_t)f32_to_bf16_bits(r[q] * inv);
-          }
-        }
-      }
-      parity ^= 1;
+      group_epilogue(cg);
     };
     auto step_done = [&](bool tail) {
       if (++cc == c1) {
         group_end(tail);
         cc = c0;
-        ++cq;
-        cu += cg.n;
-        if (cu < u_end) cg = group_at(cu);
+        ++cgrp;
+        if (cgrp < ngroups) {
+          cursor_next(ccur);
+          cg = group_of(ccur);
+          if (kTiny) tsrc = (r16 < cg.rows_left ? r16 : 0) * kPieces + (CH / 32) * g;
+        }
       }
     };
 
     // Steady state: step s computes ring slot s % kSDepth and refills it with step s + kSDepth.
     // Loads are unconditional in the prologue and the main loop (so the compiler's in-order vmcnt
     // waits keep kSDepth - 1 steps in flight); only the last < 2 kSDepth steps are predicated.
-    const int64_t S = ngroups * (c1 - c0);
+    const int S = ngroups * (c1 - c0);
     Slot ring[kSDepth];
 #pragma unroll
     for (int k = 0; k < kSDepth; ++k) load(ring[k]);
@@ -500,7 +626,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
       wait_vmcnt<kSDepth * kLoadsPerStep>();
       lds_barrier();
     }
-    int64_t s0 = 0;
+    int s0 = 0;
     for (; s0 + 2 * kSDepth <= S; s0 += kSDepth) {
 #pragma unroll
       for (int k = 0; k < kSDepth; ++k) {
@@ -517,7 +643,10 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
         step_done(true);
       }
     }
-  }
+  };
+
+  run_phase(BoolTag<true>{});
+  run_phase(BoolTag<false>{});
 
   if (kL1) {
     amax_bits = wave_max_u32(amax_bits);
@@ -855,20 +984,20 @@ static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
     if (err != hipSuccess) return err;
   }
   if (c.small) {
-    // Staged weight scales need every wave on K (K >= 4 chunks) and 3 buffers within 48 KB.
-    const int Ks = a.K / 16, P = Ks / 16 + 1;
-    const size_t buf = (size_t)((small_nb<kL1>() * 16 * P + 63) / 64) * 1024;
+    // Staged weight scales need every wave on K (K >= 4 chunks) and 3 buffers beside the tables.
     const int ch = a.K % 256 == 0 ? 256 : 128;
-    const bool staged = a.K / ch >= kSWaves && 3 * buf <= kSmallStagedMaxLds;
-    const size_t dyn = staged ? 3 * buf : 0;
+    const size_t tables = small_table_bytes(a.E);
+    const size_t bufs = 3 * small_scale_buf_bytes(small_nb<kL1>(), a.K);
+    const bool staged = a.K / ch >= kSWaves && tables + bufs <= kSmallDynMaxLds;
+    const size_t dyn = tables + (staged ? bufs : 0);
     if (ch == 256 && staged)
       hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
     else if (ch == 256)
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, false>), dim3(kSmallGrid), dim3(kGemmThreads), 0, stream, a);
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, false>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
     else if (staged)
       hipLaunchKernelGGL((gemm_small_kernel<kL1, 128, true>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
     else
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 128, false>), dim3(kSmallGrid), dim3(kGemmThreads), 0, stream, a);
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 128, false>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;
