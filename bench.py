@@ -16,7 +16,12 @@ FLOPs (prefill, against the 2.5 PFLOP/s dense fp16 MFMA peak) or algorithmic wei
 events on the stream it runs on.  ``cpu_baseline`` times the CPU oracle (float64 NumPy) on a
 bounded sample of the prefill workload: the layer restricted to its most-loaded expert.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+Also reported: per-step p10/p50/p90, GEMM-only time (L1 + L2), the decode aggregate over 64
+routing seeds (sum of weight bytes over sum of step times), and achievable ceilings measured on
+the GPU (a 1 GiB device copy, an 8192^3 fp16 GEMM from the vendor BLAS) with the L1 fractions
+against them.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-seeds N] [--no-cpu-baseline] [--quick]
 """
 from __future__ import annotations
 
@@ -33,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer TFLOP/s + weight GB/s (% roofline) at decode and 8192-token prefill"
 PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (context only: this path multiplies in fp16)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 STAGES = ("route", "quant_x", "l1", "quant_h", "l2", "combine")
 
@@ -104,6 +110,20 @@ def time_workload(wl, T, steps, warmup, copies, use_graph):
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / steps
 
+    # Per-step spread (a second pass with an event pair around every step).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        if graphs is not None:
+            graphs[i % copies].replay()
+        else:
+            step(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    spread = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
+              "p90": float(np.percentile(per_step, 90))}
+
     # Per-stage durations: a short GPU spin ahead of each stage keeps the launch latency out of
     # the event pair that brackets it.
     stage_fns = {
@@ -135,9 +155,90 @@ def time_workload(wl, T, steps, warmup, copies, use_graph):
     w13_bytes = len(active) * (Ws[0].w13_codes[0].numel() + Ws[0].w13_scales[0].numel() + 4)
     del Ws, graphs
     torch.cuda.synchronize()
-    return dict(T=T, ms_per_step=ms_per_step, wall_s=wall, stage_ms=stage_ms, assignments=assign,
+    return dict(T=T, ms_per_step=ms_per_step, wall_s=wall, stage_ms=stage_ms, spread=spread, assignments=assign,
                 active_experts=len(active), flops=flops, weight_bytes=wbytes, w13_bytes=w13_bytes,
                 l1_flops=4.0 * wl.hidden * wl.intermediate * assign)
+
+
+def decode_seed_aggregate(wl, seeds, reps, copies=4):
+    """Decode over routing seeds 0..seeds-1 at every T of the workload: sum of algorithmic weight
+    bytes over sum of step times (all 48 local experts quantized once, `copies` rotated copies;
+    one graph per seed and T holds `copies` layer forwards, one per weight copy)."""
+    import torch
+    from nvfp4_block_scaled_top_amd import layer, synth
+
+    dev = "cuda:0"
+    Ws = build_weights(wl, list(range(wl.num_experts)), copies, dev)
+    per_expert = Ws[0].nbytes_expert()
+    stream = torch.cuda.current_stream()
+    res = {}
+    for T in wl.tokens:
+        L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
+                           expert_begin=wl.expert_begin, device=dev)
+        tot_bytes, tot_ms, tot_active, empty = 0, 0.0, 0, 0
+        for seed in range(seeds):
+            ids, wts = synth.router(wl, T, seed)
+            nact = int(np.count_nonzero(synth.routing_stats(ids, wl)))
+            x = torch.from_numpy(synth.activations(wl, T, seed).view(np.int16)).to(dev)
+            idd, wtd = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
+            for c in range(copies):
+                L.forward(x, idd, wtd, Ws[c])
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in range(copies):
+                    L.forward(x, idd, wtd, Ws[c])
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            tot_ms += a.elapsed_time(b) / (reps * copies)
+            tot_bytes += nact * per_expert
+            tot_active += nact
+            empty += nact == 0
+            del g
+        gbs = tot_bytes / (tot_ms * 1e-3) / 1e9
+        res[f"T{T}"] = {"seeds": seeds, "weight_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "mean_us_per_step": round(tot_ms / seeds * 1e3, 2),
+                        "mean_active_experts": round(tot_active / seeds, 3), "seeds_without_local_work": empty}
+        log(f"[bench] decode T={T} over {seeds} seeds: {gbs:.0f} GB/s, {tot_ms / seeds * 1e3:.1f} us/step")
+        del L
+    del Ws
+    torch.cuda.synchronize()
+    return res
+
+
+def measured_ceilings():
+    """Achievable ceilings on this GPU: a 1 GiB device copy (read + write bytes) and an 8192^3 fp16
+    GEMM from the vendor BLAS (torch.matmul)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.float16, device="cuda")
+    bm = torch.randn(n, n, dtype=torch.float16, device="cuda")
+    out = {}
+    for name, fn, work in (("hbm_copy_GBps", lambda: dst.copy_(src), 2 * COPY_BYTES / 1e9),
+                           ("fp16_gemm_TFLOPs", lambda: torch.matmul(a, bm), 2.0 * n ** 3 / 1e12)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = round(work * 10 / (e0.elapsed_time(e1) * 1e-3), 1)
+    del src, dst, a, bm
+    torch.cuda.synchronize()
+    return out
 
 
 def cpu_baseline(wl, T):
@@ -278,6 +379,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--decode-seeds", type=int, default=64, help="routing seeds of the decode aggregate (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--quick", action="store_true", help="prefill only, no CPU baseline")
@@ -321,7 +423,9 @@ def main():
             gbs = d["weight_bytes"] / (d["ms_per_step"] * 1e-3) / 1e9
             l1_gbs = d["w13_bytes"] / (d["stage_ms"]["l1"] * 1e-3) / 1e9
             decode[f"T{Td}"] = {
-                "ms_per_step": round(d["ms_per_step"], 5), "weight_GBps": round(gbs, 1),
+                "ms_per_step": round(d["ms_per_step"], 5),
+                "ms_per_step_p10_p50_p90": [round(d["spread"][q], 5) for q in ("p10", "p50", "p90")],
+                "gemm_ms": round(d["stage_ms"]["l1"] + d["stage_ms"]["l2"], 5), "weight_GBps": round(gbs, 1),
                 "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "TFLOPs": round(d["flops"] / (d["ms_per_step"] * 1e-3) / 1e12, 3),
                 "active_experts": d["active_experts"], "assignments": d["assignments"],
                 "weight_bytes": d["weight_bytes"], "stage_ms": {k: round(v, 5) for k, v in d["stage_ms"].items()},
@@ -331,6 +435,19 @@ def main():
                              "kernel": "moe_grouped_gemm_l1_silu"},
             }
             log(f"[bench] decode T={Td}: {d['ms_per_step'] * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+
+    seed_agg = None
+    ceilings = None
+    if not args.quick:
+        if args.decode_seeds > 0:
+            log(f"[bench] decode aggregate over {args.decode_seeds} routing seeds")
+            seed_agg = decode_seed_aggregate(synth.WORKLOADS[1], args.decode_seeds, reps=10)
+        log("[bench] measured ceilings")
+        ceilings = measured_ceilings()
+
+    if ceilings:
+        for d in decode.values():
+            d["roofline"]["frac_of_measured_ceiling"] = round(d["roofline"]["achieved"] / ceilings["hbm_copy_GBps"], 4)
 
     cpu = None
     if not args.no_cpu_baseline and not args.quick:
@@ -357,11 +474,18 @@ def main():
                    "active_experts": pre["active_experts"], "assignments": pre["assignments"]},
         "weight_GBps": round(pre["weight_bytes"] / (pre["ms_per_step"] * 1e-3) / 1e9, 1),
         "mfma_frac": round(tflops / PEAK_FP16_TFLOPS, 4),
+        "mfma_frac_vs_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
+        "ms_per_step_p10_p50_p90": [round(pre["spread"][q], 4) for q in ("p10", "p50", "p90")],
         "stage_ms": {k: round(v, 4) for k, v in pre["stage_ms"].items()},
+        "gemm_ms": round(pre["stage_ms"]["l1"] + pre["stage_ms"]["l2"], 4),
         "roofline": {"bound": "mfma", "achieved": round(l1_tflops, 1), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(l1_tflops / PEAK_FP16_TFLOPS, 4), "traffic": recorded_traffic("prefill"),
-                     "kernel": "moe_grouped_gemm_l1_silu"},
+                     "kernel": "moe_grouped_gemm_l1_silu",
+                     "frac_of_measured_ceiling": (round(l1_tflops / ceilings["fp16_gemm_TFLOPs"], 4)
+                                                  if ceilings else None)},
         "decode": decode,
+        "decode_seed_aggregate": seed_agg,
+        "measured_ceilings": ceilings,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
