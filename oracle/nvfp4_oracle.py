@@ -248,6 +248,35 @@ def dequantize_blocks(packed, scale_codes) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Routing: filter, count, offsets, stable permutation
 # ---------------------------------------------------------------------------
+# Router: logits -> top-k ids and weights
+# ---------------------------------------------------------------------------
+
+def router_topk(logits, k: int):
+    """Top-k routing from router logits.
+
+    The runner receives ``topk_ids`` and ``topk_weights`` from the router
+    (CURRENT_BUG.md@2e65594, "Test Plan", Phase 1); the router is a softmax
+    over all global experts followed by the k largest probabilities.  Readings
+    (the pages give no formula): the softmax is taken in float64 over the
+    float32 logits, max-subtracted; the k probabilities are NOT renormalised;
+    order is descending probability, equal probabilities going to the lower
+    expert index; weights are the float64 probabilities rounded to float32.
+    Returns topk_ids int32 [T, k] and topk_weights float32 [T, k].
+    """
+    lg = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    T, Eg = lg.shape
+    if not 1 <= k <= Eg:
+        raise ValueError("need 1 <= k <= number of experts")
+    z = lg - lg.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p = p / p.sum(axis=1, keepdims=True)
+    order = np.argsort(-p, axis=1, kind="stable")[:, :k]
+    return order.astype(np.int32), np.take_along_axis(p, order, axis=1).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Routing tables
+# ---------------------------------------------------------------------------
 
 def row_capacity(T: int, k: int, E: int, P: int) -> int:
     """Rows needed for every local assignment with each expert padded to a multiple of P."""

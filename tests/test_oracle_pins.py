@@ -495,3 +495,61 @@ def test_workloads_follow_pages_shapes():
     assert w1.num_experts == g["num_experts"] / g["ep_degree"] == g["ep_local_experts"]
     assert max(w1.tokens) == g["decode_tokens_max"]
     assert synth.WORKLOADS[2].pad_multiple == g["pad_multiple"]
+
+
+# ---------------------------------------------------------------------------
+# router: softmax over all experts, top-k, ties to the lower index
+# ---------------------------------------------------------------------------
+
+def _router_brute(row, k):
+    """Independent reference: order by (-logit, index) on Python floats, probabilities from
+    math.exp and an exactly rounded sum (math.fsum)."""
+    vals = [float(v) for v in np.asarray(row, np.float32)]
+    m = max(vals)
+    ex = [math.exp(v - m) for v in vals]
+    s = math.fsum(ex)
+    order = sorted(range(len(vals)), key=lambda j: (-vals[j], j))[:k]
+    return order, [np.float32(ex[j] / s) for j in order]
+
+
+@pytest.mark.parametrize("T,E,k,seed", [(40, 7, 3, 0), (25, 64, 6, 1), (9, 384, 6, 2), (5, 130, 130, 3)])
+def test_router_matches_brute_force(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E)).astype(np.float32) * np.float32(2.5)
+    logits[0, : min(4, E)] = logits[0, 0]          # exact ties in one row
+    logits[1, -1] = logits[1].max()                 # a tie for the maximum at the highest index
+    ids, w = O.router_topk(logits, k)
+    assert ids.dtype == np.int32 and w.dtype == np.float32 and ids.shape == (T, k) == w.shape
+    for t in range(T):
+        order, ref = _router_brute(logits[t], k)
+        assert ids[t].tolist() == order
+        # float64 sums in different orders may differ in the last bit, which can move a float32
+        # rounding by one unit at most
+        np.testing.assert_allclose(w[t], np.array(ref, np.float32), rtol=2.0 ** -23, atol=0)
+
+
+def test_router_invariants():
+    rng = np.random.default_rng(7)
+    # logits on a 2^-10 grid, so that adding 4.0 below is exact in float32
+    logits = (np.round(rng.standard_normal((64, 48)) * 1024) / 1024).astype(np.float32)
+    ids, w = O.router_topk(logits, 48)                       # k = E: the full softmax, sorted
+    assert np.all(np.sort(ids, axis=1) == np.arange(48))
+    assert np.all(np.diff(w, axis=1) <= 0) and np.all(w > 0)
+    np.testing.assert_allclose(w.astype(np.float64).sum(axis=1), 1.0, rtol=1e-6)
+    ids6, w6 = O.router_topk(logits, 6)                      # not renormalised: a prefix of the full list
+    assert np.array_equal(ids6, ids[:, :6]) and np.array_equal(w6, w[:, :6])
+    assert np.all(w6.sum(axis=1) < 1)
+    ids_s, w_s = O.router_topk(logits + np.float32(4.0), 6)   # shift invariance
+    assert np.array_equal(ids_s, ids6)
+    np.testing.assert_allclose(w_s, w6, rtol=2.0 ** -22)
+    flat = np.full((3, 10), 0.25, np.float32)                # all equal: the k lowest indices, 1/E each
+    ids_f, w_f = O.router_topk(flat, 4)
+    assert np.all(ids_f == np.arange(4)) and np.all(w_f == np.float32(0.1))
+
+
+def test_router_large_logits_do_not_overflow():
+    logits = np.array([[1000.0, 999.0, -1000.0, 998.0]], np.float32)
+    ids, w = O.router_topk(logits, 2)
+    assert ids.tolist() == [[0, 1]]
+    e = [math.exp(0.0), math.exp(-1.0), math.exp(-2000.0), math.exp(-2.0)]
+    np.testing.assert_allclose(w[0], np.array([e[0], e[1]]) / math.fsum(e), rtol=2.0 ** -23)
