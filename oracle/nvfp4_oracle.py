@@ -259,18 +259,23 @@ def router_topk(logits, k: int):
     over all global experts followed by the k largest probabilities.  Readings
     (the pages give no formula): the softmax is taken in float64 over the
     float32 logits, max-subtracted; the k probabilities are NOT renormalised;
-    order is descending probability, equal probabilities going to the lower
-    expert index; weights are the float64 probabilities rounded to float32.
-    Returns topk_ids int32 [T, k] and topk_weights float32 [T, k].
+    weights are the float64 probabilities rounded to float32.  Order is
+    descending probability with equal values going to the lower expert index,
+    decided on the float32 logits: the exact softmax is strictly increasing in
+    the logit, so this is the exact probabilities' order, and it does not
+    depend on float64 rounding (far below the largest logit every probability
+    underflows to the same 0).  Returns topk_ids int32 [T, k] and topk_weights
+    float32 [T, k].
     """
-    lg = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    lg32 = np.asarray(logits, dtype=np.float32)
+    lg = lg32.astype(np.float64)
     T, Eg = lg.shape
     if not 1 <= k <= Eg:
         raise ValueError("need 1 <= k <= number of experts")
     z = lg - lg.max(axis=1, keepdims=True)
     p = np.exp(z)
     p = p / p.sum(axis=1, keepdims=True)
-    order = np.argsort(-p, axis=1, kind="stable")[:, :k]
+    order = np.argsort(-lg32, axis=1, kind="stable")[:, :k]
     return order.astype(np.int32), np.take_along_axis(p, order, axis=1).astype(np.float32)
 
 
