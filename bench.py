@@ -16,6 +16,10 @@ FLOPs (prefill, against the 2.5 PFLOP/s dense fp16 MFMA peak) or algorithmic wei
 events on the stream it runs on.  ``cpu_baseline`` times the CPU oracle (float64 NumPy) on a
 bounded sample of the prefill workload: the layer restricted to its most-loaded expert.
 
+The routing ids and weights of every workload come from its router logits through the GPU router
+(moe_router_topk), whose time is the "router" entry of stage_ms (the timed step starts from the
+ids, at route/permute).
+
 Also reported: per-step p10/p50/p90, GEMM-only time (L1 + L2), the decode aggregate over 64
 routing seeds (sum of weight bytes over sum of step times), and achievable ceilings measured on
 the GPU (a 1 GiB device copy, an 8192^3 fp16 GEMM from the vendor BLAS) with the L1 fractions
@@ -40,11 +44,26 @@ METRIC = "MoE layer TFLOP/s + weight GB/s (% roofline) at decode and 8192-token 
 PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (context only: this path multiplies in fp16)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-STAGES = ("route", "quant_x", "l1", "quant_h", "l2", "combine")
+STAGES = ("router", "route", "quant_x", "l1", "quant_h", "l2", "combine")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def gpu_routing(wl, T, seed=0, dev="cuda:0"):
+    """Router logits of the workload, routed on the GPU (moe_router_topk): device logits, ids and
+    weights, and the per-local-expert assignment counts on the host (for bookkeeping)."""
+    import torch
+    from nvfp4_block_scaled_top_amd import megamoe, synth
+
+    logits = torch.from_numpy(synth.router_logits(wl, T, seed)).to(dev)
+    ids = torch.empty(T, wl.top_k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, wl.top_k, dtype=torch.float32, device=dev)
+    megamoe.moe_router_topk(logits, wl.top_k, ids, wts)
+    h = ids.cpu().numpy()
+    loc = h[(h >= wl.expert_begin) & (h < wl.expert_begin + wl.num_experts)] - wl.expert_begin
+    return logits, ids, wts, np.bincount(loc, minlength=wl.num_experts)
 
 
 def build_weights(wl, active, copies, dev):
@@ -63,14 +82,12 @@ def build_weights(wl, active, copies, dev):
 
 def time_workload(wl, T, steps, warmup, copies, use_graph):
     import torch
-    from nvfp4_block_scaled_top_amd import layer, synth
+    from nvfp4_block_scaled_top_amd import layer, megamoe, synth
 
     dev = "cuda:0"
-    ids, wts = synth.router(wl, T)
-    counts = synth.routing_stats(ids, wl)
+    logits, ids_d, wts_d, counts = gpu_routing(wl, T, 0, dev)
     active = [int(e) for e in np.nonzero(counts)[0]]
     x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).to(dev)
-    ids_d, wts_d = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
     Ws = build_weights(wl, active, copies, dev)
     L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
                        expert_begin=wl.expert_begin, device=dev)
@@ -127,6 +144,7 @@ def time_workload(wl, T, steps, warmup, copies, use_graph):
     # Per-stage durations: a short GPU spin ahead of each stage keeps the launch latency out of
     # the event pair that brackets it.
     stage_fns = {
+        "router": lambda i: megamoe.moe_router_topk(logits, wl.top_k, ids_d, wts_d),
         "route": lambda i: L.route(ids_d),
         "quant_x": lambda i: L.quantize_x(x),
         "l1": lambda i: L.l1(Ws[i % copies]),
@@ -177,10 +195,9 @@ def decode_seed_aggregate(wl, seeds, reps, copies=4):
                            expert_begin=wl.expert_begin, device=dev)
         tot_bytes, tot_ms, tot_active, empty = 0, 0.0, 0, 0
         for seed in range(seeds):
-            ids, wts = synth.router(wl, T, seed)
-            nact = int(np.count_nonzero(synth.routing_stats(ids, wl)))
+            _, idd, wtd, counts = gpu_routing(wl, T, seed, dev)
+            nact = int(np.count_nonzero(counts))
             x = torch.from_numpy(synth.activations(wl, T, seed).view(np.int16)).to(dev)
-            idd, wtd = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
             for c in range(copies):
                 L.forward(x, idd, wtd, Ws[c])
             torch.cuda.synchronize()
@@ -252,8 +269,8 @@ def cpu_baseline(wl, T):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    ids, wts = synth.router(wl, T)
-    counts = synth.routing_stats(ids, wl)
+    ids, wts = O.router_topk(synth.router_logits(wl, T), wl.top_k)
+    counts = O.route(ids, wl.expert_begin, wl.num_experts, wl.pad_multiple)[0]
     e = int(np.argmax(counts))
     x = O.bf16_from_bits(synth.activations(wl, T))
     w13, w2 = synth.expert_weights(wl, wl.expert_begin + e, device="cpu")
@@ -296,14 +313,12 @@ def traffic_pass(which: str) -> None:
     del src, dst
     wl = synth.WORKLOADS[3] if which == "prefill" else synth.WORKLOADS[1]
     T = wl.tokens[0] if which == "prefill" else 8
-    ids, wts = synth.router(wl, T)
-    counts = synth.routing_stats(ids, wl)
+    _, idd, wtd, counts = gpu_routing(wl, T, 0, "cuda")
     active = [int(e) for e in np.nonzero(counts)[0]]
     W = build_weights(wl, active, 1, "cuda")[0]
     L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
                        expert_begin=wl.expert_begin)
     x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).cuda()
-    idd, wtd = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
     for _ in range(2):
         L.forward(x, idd, wtd, W)
     torch.cuda.synchronize()

@@ -10,6 +10,9 @@
  *   moe_route_permute -> nvfp4_quantize_act(x) -> moe_grouped_gemm_l1_silu
  *   -> nvfp4_quantize_act(h, amax from L1) -> moe_grouped_gemm_l2 -> moe_combine
  *
+ * Starting from router logits instead of top-k ids, moe_route_logits (moe_router_topk, then
+ * moe_route_permute on its ids) takes the place of moe_route_permute.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every pointer argument is a DEVICE pointer owned by the caller.  The library never
@@ -56,6 +59,9 @@ extern "C" {
 /* Largest number of local experts one call handles. */
 #define MEGAMOE_MAX_EXPERTS 1024
 
+/* Largest number of global experts the router takes. */
+#define MEGAMOE_ROUTER_MAX_EXPERTS 1024
+
 /* Slots of the per-workgroup h amax written by moe_grouped_gemm_l1_silu (every slot, every call). */
 #define MEGAMOE_L1_AMAX_PARTS 1280
 
@@ -75,6 +81,40 @@ size_t megamoe_route_workspace_bytes(int32_t T, int32_t k, int32_t num_experts);
 
 /* Scratch bytes nvfp4_quantize_act needs for a [rows, cols] tensor. */
 size_t megamoe_quant_workspace_bytes(int64_t rows, int64_t cols);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_router_topk - router logits -> top-k expert ids and weights.
+ *
+ * The routed experts receive topk_ids and topk_weights from the router (CURRENT_BUG.md@2e65594,
+ * "Test Plan" Phase 1); the router of the workloads is a softmax over all global experts
+ * followed by the k largest probabilities.
+ *
+ * logits             float32 [T, num_experts_global], finite.
+ * topk_ids           int32 [T, k]   global expert ids by descending probability; equal
+ *                    probabilities go to the lower id.
+ * topk_weights       float32 [T, k] softmax probabilities over all num_experts_global experts
+ *                    (float64 arithmetic, max-subtracted, rounded to float32), NOT renormalised
+ *                    over the k chosen.
+ * Limits: 0 <= T, 1 <= num_experts_global <= MEGAMOE_ROUTER_MAX_EXPERTS,
+ * 1 <= k <= min(64, num_experts_global), T*k < 2^31.  Non-finite logits are outside the contract
+ * (the outputs are then unspecified; no error is reported).
+ * ---------------------------------------------------------------------------------------- */
+int32_t moe_router_topk(const float* logits, int32_t T, int32_t num_experts_global, int32_t k,
+                        int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_route_logits - moe_router_topk, then moe_route_permute on the ids it wrote, in one call.
+ *
+ * Arguments as in those two functions; topk_ids and topk_weights are outputs (the ids feed the
+ * permutation, the weights are for moe_combine).  Checks are those of both functions, all made
+ * before any launch.
+ * ---------------------------------------------------------------------------------------- */
+int32_t moe_route_logits(const float* logits, int32_t T, int32_t num_experts_global, int32_t k,
+                         int32_t expert_begin, int32_t num_experts, int32_t pad_multiple,
+                         int32_t block_m_override, int32_t* topk_ids, float* topk_weights,
+                         int32_t* counts, int32_t* expert_offsets, int32_t* padded_offsets,
+                         int32_t* row_token, int32_t* token_rows, int32_t* sched, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * moe_route_permute - local filter, per-expert counts, offsets, stable permutation, tile table.

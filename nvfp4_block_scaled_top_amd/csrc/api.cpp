@@ -49,6 +49,41 @@ bool gemm_shape_ok(int32_t E, int32_t H, int32_t I, int64_t M_cap) {
          M_cap >= 0 && M_cap < (int64_t)1 << 31;
 }
 
+bool router_shape_ok(int32_t T, int32_t Eg, int32_t k) {
+  return T >= 0 && Eg >= 1 && Eg <= MEGAMOE_ROUTER_MAX_EXPERTS && k >= 1 && k <= 64 && k <= Eg &&
+         (int64_t)T * k < ((int64_t)1 << 31);
+}
+
+}  // namespace
+
+extern "C" size_t megamoe_route_workspace_bytes(int32_t T, int32_t k, int32_t num_experts);
+extern "C" int64_t megamoe_row_capacity(int32_t T, int32_t k, int32_t num_experts, int32_t pad_multiple);
+
+namespace {
+
+// Checks of moe_route_permute's arguments (also made by moe_route_logits).
+int32_t route_args_ok(int32_t T, int32_t k, int32_t expert_begin, int32_t num_experts, int32_t pad_multiple,
+                      int32_t block_m_override, const int32_t* topk_ids, const int32_t* counts,
+                      const int32_t* expert_offsets, const int32_t* padded_offsets, const int32_t* row_token,
+                      const int32_t* token_rows, const int32_t* sched, const void* workspace,
+                      size_t workspace_bytes) {
+  if (T < 0 || k < 1 || k > 64 || num_experts < 1 || num_experts > MEGAMOE_MAX_EXPERTS || pad_multiple < 1 ||
+      expert_begin < 0)
+    return MEGAMOE_ERR_SHAPE;
+  if (block_m_override != 0 && block_m_override != kBlockMSmall && block_m_override != kBlockMLarge)
+    return MEGAMOE_ERR_SHAPE;
+  const int64_t n = (int64_t)T * k;
+  const int64_t M_cap = megamoe_row_capacity(T, k, num_experts, pad_multiple);
+  if (n >= ((int64_t)1 << 31) || M_cap >= ((int64_t)1 << 31)) return MEGAMOE_ERR_SHAPE;
+  if (!counts || !expert_offsets || !padded_offsets || !sched) return MEGAMOE_ERR_NULL;
+  if (M_cap > 0 && !row_token) return MEGAMOE_ERR_NULL;
+  if (n > 0 && (!topk_ids || !token_rows)) return MEGAMOE_ERR_NULL;
+  const size_t need = megamoe_route_workspace_bytes(T, k, num_experts);
+  if (workspace_bytes < need) return MEGAMOE_ERR_WORKSPACE;
+  if (need > 0 && !workspace) return MEGAMOE_ERR_NULL;
+  return MEGAMOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -75,24 +110,47 @@ size_t megamoe_quant_workspace_bytes(int64_t rows, int64_t cols) {
   return (size_t)quant_amax_parts(rows, cols) * sizeof(float);
 }
 
+int32_t moe_router_topk(const float* logits, int32_t T, int32_t num_experts_global, int32_t k, int32_t* topk_ids,
+                        float* topk_weights, void* stream) {
+  if (!router_shape_ok(T, num_experts_global, k)) return MEGAMOE_ERR_SHAPE;
+  if (T > 0 && (!logits || !topk_ids || !topk_weights)) return MEGAMOE_ERR_NULL;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  return launch_status(launch_router(logits, T, num_experts_global, k, topk_ids, topk_weights,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_route_logits(const float* logits, int32_t T, int32_t num_experts_global, int32_t k, int32_t expert_begin,
+                         int32_t num_experts, int32_t pad_multiple, int32_t block_m_override, int32_t* topk_ids,
+                         float* topk_weights, int32_t* counts, int32_t* expert_offsets, int32_t* padded_offsets,
+                         int32_t* row_token, int32_t* token_rows, int32_t* sched, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!router_shape_ok(T, num_experts_global, k)) return MEGAMOE_ERR_SHAPE;
+  if (T > 0 && (!logits || !topk_ids || !topk_weights)) return MEGAMOE_ERR_NULL;
+  const int32_t rc = route_args_ok(T, k, expert_begin, num_experts, pad_multiple, block_m_override, topk_ids, counts,
+                                   expert_offsets, padded_offsets, row_token, token_rows, sched, workspace,
+                                   workspace_bytes);
+  if (rc != MEGAMOE_OK) return rc;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t r = launch_status(launch_router(logits, T, num_experts_global, k, topk_ids, topk_weights, s));
+  if (r != MEGAMOE_OK) return r;
+  return launch_status(launch_route(topk_ids, T, k, expert_begin, num_experts, pad_multiple, block_m_override, counts,
+                                    expert_offsets, padded_offsets, row_token,
+                                    megamoe_row_capacity(T, k, num_experts, pad_multiple), token_rows, sched,
+                                    static_cast<int32_t*>(workspace), s));
+}
+
 int32_t moe_route_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t expert_begin, int32_t num_experts,
                           int32_t pad_multiple, int32_t block_m_override, int32_t* counts, int32_t* expert_offsets,
                           int32_t* padded_offsets, int32_t* row_token, int32_t* token_rows, int32_t* sched,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  if (T < 0 || k < 1 || k > 64 || num_experts < 1 || num_experts > MEGAMOE_MAX_EXPERTS || pad_multiple < 1 ||
-      expert_begin < 0)
-    return MEGAMOE_ERR_SHAPE;
-  if (block_m_override != 0 && block_m_override != kBlockMSmall && block_m_override != kBlockMLarge)
-    return MEGAMOE_ERR_SHAPE;
-  const int64_t n = (int64_t)T * k;
+  const int32_t rc = route_args_ok(T, k, expert_begin, num_experts, pad_multiple, block_m_override, topk_ids, counts,
+                                   expert_offsets, padded_offsets, row_token, token_rows, sched, workspace,
+                                   workspace_bytes);
+  if (rc != MEGAMOE_OK) return rc;
   const int64_t M_cap = megamoe_row_capacity(T, k, num_experts, pad_multiple);
-  if (n >= ((int64_t)1 << 31) || M_cap >= ((int64_t)1 << 31)) return MEGAMOE_ERR_SHAPE;
-  if (!counts || !expert_offsets || !padded_offsets || !sched) return MEGAMOE_ERR_NULL;
-  if (M_cap > 0 && !row_token) return MEGAMOE_ERR_NULL;
-  if (n > 0 && (!topk_ids || !token_rows)) return MEGAMOE_ERR_NULL;
-  const size_t need = megamoe_route_workspace_bytes(T, k, num_experts);
-  if (workspace_bytes < need) return MEGAMOE_ERR_WORKSPACE;
-  if (need > 0 && !workspace) return MEGAMOE_ERR_NULL;
   const int32_t dev = check_device();
   if (dev != MEGAMOE_OK) return dev;
   return launch_status(launch_route(topk_ids, T, k, expert_begin, num_experts, pad_multiple, block_m_override, counts,

@@ -37,6 +37,10 @@ hipError_t launch_route(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e
                         int32_t* row_token, int64_t M_cap, int32_t* token_rows, int32_t* sched,
                         int32_t* ws, hipStream_t stream);
 
+// ---- router ----------------------------------------------------------------------------------
+hipError_t launch_router(const float* logits, int32_t T, int32_t Eg, int32_t k, int32_t* ids, float* weights,
+                         hipStream_t stream);
+
 // ---- quantizer -------------------------------------------------------------------------------
 int quant_amax_parts(int64_t rows, int64_t cols);
 hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* row_valid,

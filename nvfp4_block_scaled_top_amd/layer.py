@@ -5,6 +5,7 @@ PyTorch allocates device memory here; every computation is a call into libmegamo
 ``nvfp4_quantize_act`` (one global scale per expert and matrix), and ``MoELayer`` holds the
 intermediate buffers for a fixed (T, k, E, H, I, P) and runs the six-call forward:
 route/permute, quantize x, L1 gate+up + SiLU, quantize h (amax from L1), L2 down, combine.
+``forward_logits`` starts one step earlier, from router logits (router + route/permute in one call).
 """
 from __future__ import annotations
 
@@ -95,6 +96,8 @@ class MoELayer:
         self.h_gs = torch.empty(1, **f32)
         self.y = torch.empty(max(self.M_cap, 1), H, dtype=torch.int16, device=device)
         self.out = torch.empty(max(T, 1), H, dtype=torch.int16, device=device)
+        self.topk_ids = torch.empty(max(T, 1), k, **i32)          # written by route_logits
+        self.topk_weights = torch.empty(max(T, 1), k, **f32)
 
     def _rows(self, t: torch.Tensor, n: int) -> torch.Tensor:
         return t[:n] if n > 0 else t[:0]
@@ -103,6 +106,13 @@ class MoELayer:
         mm.moe_route_permute(topk_ids, self.expert_begin, self.E, self.P, self.counts, self.expert_offsets,
                              self.padded_offsets, self.row_token, self.token_rows, self.sched, self.route_ws,
                              block_m_override=self.block_m_override, stream=stream)
+
+    def route_logits(self, logits: torch.Tensor, stream=None) -> None:
+        """Router (softmax top-k over the float32 logits [T, E_global]) and route/permute."""
+        mm.moe_route_logits(logits, self.k, self.expert_begin, self.E, self.P, self._rows(self.topk_ids, self.T),
+                            self._rows(self.topk_weights, self.T), self.counts, self.expert_offsets,
+                            self.padded_offsets, self.row_token, self.token_rows, self.sched, self.route_ws,
+                            block_m_override=self.block_m_override, stream=stream)
 
     def quantize_x(self, x_bf16: torch.Tensor, stream=None) -> None:
         mm.nvfp4_quantize_act(x_bf16, self._rows(self.x_codes, self.T), self._rows(self.x_scales, self.T),
@@ -137,4 +147,15 @@ class MoELayer:
         self.quantize_h(stream)
         self.l2(w, stream)
         self.combine(topk_weights, stream)
+        return self._rows(self.out, self.T)
+
+    def forward_logits(self, x_bf16: torch.Tensor, logits: torch.Tensor, w: MoEWeights, stream=None) -> torch.Tensor:
+        """x_bf16 int16-viewed bf16 [T, H], logits float32 [T, E_global]; the chosen ids and weights
+        are left in topk_ids / topk_weights."""
+        self.route_logits(logits, stream)
+        self.quantize_x(x_bf16, stream)
+        self.l1(w, stream)
+        self.quantize_h(stream)
+        self.l2(w, stream)
+        self.combine(self._rows(self.topk_weights, self.T), stream)
         return self._rows(self.out, self.T)

@@ -35,6 +35,9 @@ SIGNATURES = {
     "megamoe_sched_len": (_I64, [_I32]),
     "megamoe_route_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "megamoe_quant_workspace_bytes": (_SZ, [_I64, _I64]),
+    "moe_router_topk": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_route_logits": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                _SZ, _P]),
     "moe_route_permute": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_l1_silu": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
@@ -112,6 +115,22 @@ def megamoe_quant_workspace_bytes(rows: int, cols: int) -> int:
 
 
 # ---- entry points --------------------------------------------------------------------------------
+
+def moe_router_topk(logits, k, topk_ids, topk_weights, stream=None):
+    T, Eg = logits.shape
+    _check("moe_router_topk", lib().moe_router_topk(_ptr(logits), T, Eg, k, _ptr(topk_ids), _ptr(topk_weights),
+                                                    _stream(stream)))
+
+
+def moe_route_logits(logits, k, expert_begin, num_experts, pad_multiple, topk_ids, topk_weights, counts,
+                     expert_offsets, padded_offsets, row_token, token_rows, sched, workspace, block_m_override=0,
+                     stream=None):
+    T, Eg = logits.shape
+    _check("moe_route_logits", lib().moe_route_logits(
+        _ptr(logits), T, Eg, k, expert_begin, num_experts, pad_multiple, block_m_override, _ptr(topk_ids),
+        _ptr(topk_weights), _ptr(counts), _ptr(expert_offsets), _ptr(padded_offsets), _ptr(row_token),
+        _ptr(token_rows), _ptr(sched), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
 
 def moe_route_permute(topk_ids, expert_begin, num_experts, pad_multiple, counts, expert_offsets, padded_offsets,
                       row_token, token_rows, sched, workspace, block_m_override=0, stream=None):

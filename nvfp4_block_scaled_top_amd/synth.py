@@ -15,13 +15,13 @@ rows ("Test Plan", Phase 2), and activations with std 0.09 and amax 1.27
 Recipe (seed = 0 by default; every tensor has its own numpy PCG64 stream
 ``default_rng([seed, stream])``):
 
-* stream 0: router logits, ``standard_normal((T, E_global), float32)``, used in float64;
+* stream 0: router logits, ``standard_normal((T, E_global), float32)``;
 * stream 1: Zipf ranks: ``perm = permutation(E_global)``; expert ``perm[i]`` gets rank i+1 and
-  bias ``-1.2 * ln(rank)`` is added to its logits;
+  bias ``-1.2 * ln(rank)`` is added to its logits (in float64, the sum rounded to float32);
 * stream 2: x, ``standard_normal((T, H), float32) * 0.09``, clipped to +-1.27, rounded to bf16;
 * stream 3: outliers, ``choice(T*H, T*H // 1000)`` positions and ``integers(0, 2)`` signs, set to +-8;
-* routing: softmax in float64 over all experts, then the k largest probabilities
-  (ties to the lower expert index), not renormalised; weights stored as float32;
+* routing itself (softmax and top-k) is a step of the layer, not part of this module: the
+  logits go to the router (the GPU router, or the oracle's);
 * weights: ``torch.randn`` (float32) * 0.02, rounded to bf16, drawn on the target
   device from a generator seeded per (seed, matrix, global expert).  Expert e's
   weights are the same in every workload that contains expert e.
@@ -81,21 +81,16 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def router(w: Workload, T: int, seed: int = 0):
-    """topk_ids int32 [T, k] (global expert ids) and topk_weights float32 [T, k]."""
-    logits = _rng(seed, 0).standard_normal((T, w.num_experts_global), dtype=np.float32).astype(np.float64)
+def router_logits(w: Workload, T: int, seed: int = 0) -> np.ndarray:
+    """Router logits, float32 [T, E_global]."""
+    logits = _rng(seed, 0).standard_normal((T, w.num_experts_global), dtype=np.float32)
     if w.zipf:
         perm = _rng(seed, 1).permutation(w.num_experts_global)
         rank = np.empty(w.num_experts_global, dtype=np.int64)
         rank[perm] = np.arange(1, w.num_experts_global + 1)
-        logits = logits + (-ZIPF_S * np.log(rank.astype(np.float64)))[None, :]
-    z = logits - logits.max(axis=1, keepdims=True)
-    p = np.exp(z)
-    p = p / p.sum(axis=1, keepdims=True)
-    order = np.argsort(-p, axis=1, kind="stable")[:, : w.top_k]
-    ids = order.astype(np.int32)
-    weights = np.take_along_axis(p, order, axis=1).astype(np.float32)
-    return ids, weights
+        bias = -ZIPF_S * np.log(rank.astype(np.float64))
+        logits = (logits.astype(np.float64) + bias[None, :]).astype(np.float32)
+    return logits
 
 
 def activations(w: Workload, T: int, seed: int = 0) -> np.ndarray:
@@ -142,9 +137,3 @@ def device_normal_bf16(shape, seed: int, stream: int, std: float, device: str = 
     g = torch.Generator(device=device)
     g.manual_seed(_weight_seed(seed, stream, 0))
     return (torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
-
-
-def routing_stats(ids: np.ndarray, w: Workload):
-    """Per-expert counts of local assignments (a summary used to pin the recipe)."""
-    loc = ids[(ids >= w.expert_begin) & (ids < w.expert_begin + w.num_experts)] - w.expert_begin
-    return np.bincount(loc, minlength=w.num_experts)

@@ -91,7 +91,7 @@ class Setup:
 
 def make_setup(wl: synth.Workload, T: int, seed: int = 0, weight_seed: Optional[int] = None,
                weights_from: Optional[Setup] = None) -> Setup:
-    ids, wts = synth.router(wl, T, seed)
+    ids, wts = O.router_topk(synth.router_logits(wl, T, seed), wl.top_k)
     x_bits = synth.activations(wl, T, seed)
     if weights_from is not None:
         return Setup(wl, T, ids, wts, x_bits, weights_from.gpu_w, weights_from.raw_dev, weights_from.oracle_w)

@@ -77,6 +77,23 @@ def test_route_rejects_bad_args(lib):
     assert f(FAKE, 4, 6, 0, 48, 1, 0, *ok, FAKE, 4, None) == -3               # workspace too small
 
 
+def test_router_rejects_bad_args(lib):
+    f = lib.moe_router_topk
+    assert f(FAKE, 4, 384, 0, FAKE, FAKE, None) == -2        # k < 1
+    assert f(FAKE, 4, 384, 65, FAKE, FAKE, None) == -2       # k > 64
+    assert f(FAKE, 4, 4, 6, FAKE, FAKE, None) == -2          # k > number of experts
+    assert f(FAKE, 4, 2048, 6, FAKE, FAKE, None) == -2       # too many experts
+    assert f(FAKE, -1, 384, 6, FAKE, FAKE, None) == -2       # T < 0
+    assert f(None, 4, 384, 6, FAKE, FAKE, None) == -1        # logits NULL
+    assert f(FAKE, 4, 384, 6, FAKE, None, None) == -1        # weights NULL
+    g = lib.moe_route_logits
+    ok = [FAKE] * 6
+    assert g(FAKE, 4, 384, 0, 0, 48, 1, 0, FAKE, FAKE, *ok, FAKE, 4096, None) == -2         # k < 1
+    assert g(FAKE, 4, 384, 6, 0, 0, 1, 0, FAKE, FAKE, *ok, FAKE, 4096, None) == -2          # E < 1
+    assert g(None, 4, 384, 6, 0, 48, 1, 0, FAKE, FAKE, *ok, FAKE, 4096, None) == -1         # logits NULL
+    assert g(FAKE, 4, 384, 6, 0, 48, 1, 0, FAKE, FAKE, *ok, FAKE, 4, None) == -3            # workspace too small
+
+
 def test_quant_rejects_bad_args(lib):
     f = lib.nvfp4_quantize_act
     assert f(FAKE, 4, 48, None, None, 0, FAKE, FAKE, FAKE, FAKE, 64, None) == -2   # cols % 32

@@ -43,9 +43,9 @@ def test_prefill_full_size_sampled(cfg):
     E, H, I, k, P = wl.num_experts, wl.hidden, wl.intermediate, wl.top_k, wl.pad_multiple
     rng = np.random.default_rng(1234 + cfg)
     log(f"[fullsize] {wl.name} T={T}")
-    ids, wts = synth.router(wl, T)
+    ids, wts = O.router_topk(synth.router_logits(wl, T), wl.top_k)
     x_bits = synth.activations(wl, T)
-    counts = synth.routing_stats(ids, wl)
+    counts = O.route(ids, wl.expert_begin, E, P)[0]
     active = np.nonzero(counts)[0]
     order = active[np.argsort(counts[active], kind="stable")]
     small = [int(e) for e in order if counts[e] <= 16]

@@ -445,7 +445,7 @@ def test_nonlocal_tokens_are_plus_zero():
 
 def test_decode_t1_has_no_local_work():
     w = synth.WORKLOADS[1]
-    ids, _ = synth.router(w, 1)
+    ids, _ = O.router_topk(synth.router_logits(w, 1), w.top_k)
     counts, *_ = O.route(ids, w.expert_begin, w.num_experts, w.pad_multiple)
     assert counts.sum() == 0
 
@@ -457,11 +457,13 @@ def test_decode_t1_has_no_local_work():
 def test_generator_seed0_statistics():
     def counts(i, T):
         w = synth.WORKLOADS[i]
-        return synth.routing_stats(synth.router(w, T)[0], w)
+        ids, _ = O.router_topk(synth.router_logits(w, T), w.top_k)
+        loc = ids[(ids >= w.expert_begin) & (ids < w.expert_begin + w.num_experts)] - w.expert_begin
+        return np.bincount(loc, minlength=w.num_experts)
 
     c0 = counts(0, 16)
     assert c0.tolist() == [3, 6, 3, 3, 4, 4, 5, 4]
-    _, wts = synth.router(synth.WORKLOADS[0], 16)
+    _, wts = O.router_topk(synth.router_logits(synth.WORKLOADS[0], 16), 2)
     assert abs(wts[0, 0] - 0.3327) < 5e-5 and abs(wts[0, 1] - 0.1985) < 5e-5
     assert [counts(1, T).sum() for T in (1, 4, 8)] == [0, 5, 10]
     assert (counts(1, 8) > 0).sum() == 9
@@ -545,6 +547,15 @@ def test_router_invariants():
     flat = np.full((3, 10), 0.25, np.float32)                # all equal: the k lowest indices, 1/E each
     ids_f, w_f = O.router_topk(flat, 4)
     assert np.all(ids_f == np.arange(4)) and np.all(w_f == np.float32(0.1))
+
+
+def test_router_order_survives_underflow():
+    """Far below the largest logit the float64 probabilities all underflow to 0; the order stays
+    that of the logits (the exact probabilities'), not the index order of equal zeros."""
+    logits = np.array([[0.0, -900.0, -800.0, -1000.0, -850.0]], np.float32)
+    ids, w = O.router_topk(logits, 4)
+    assert ids.tolist() == [[0, 2, 4, 1]]
+    assert w[0, 0] == 1 and np.all(w[0, 1:] == 0)
 
 
 def test_router_large_logits_do_not_overflow():
