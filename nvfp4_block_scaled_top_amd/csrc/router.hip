@@ -11,7 +11,7 @@
 // One wave per token: each lane holds Eg/64 logits, a wave max and a float64 wave sum give the
 // softmax denominator, and k rounds of a wave argmax over the (value, -index) order pick the
 // experts; round r takes the best candidate strictly after round r-1's winner in that order, so no
-// per-expert state is kept.
+// per-expert state is kept.  Lane r keeps winner r and the k weights are computed in parallel.
 #include "device_common.h"
 #include "internal.h"
 
@@ -57,6 +57,8 @@ __global__ __launch_bounds__(kRouterWaves* kWave) void router_topk_kernel(const 
 
   float pv = __builtin_huge_valf();  // previous winner (value, index)
   int pj = -1;
+  float wv = 0.0f;  // lane r keeps winner r
+  int wj = 0;
   for (int r = 0; r < k; ++r) {
     float bv = -__builtin_huge_valf();
     int bj = 0x7FFFFFFF;
@@ -80,10 +82,14 @@ __global__ __launch_bounds__(kRouterWaves* kWave) void router_topk_kernel(const 
     }
     pv = bv;
     pj = bj;
-    if (lane == 0) {
-      ids[(int64_t)t * k + r] = bj;
-      weights[(int64_t)t * k + r] = (float)(exp((double)bv - md) / s);
+    if (lane == r) {
+      wv = bv;
+      wj = bj;
     }
+  }
+  if (lane < k) {  // the k weights in parallel, one lane each
+    ids[(int64_t)t * k + lane] = wj;
+    weights[(int64_t)t * k + lane] = (float)(exp((double)wv - md) / s);
   }
 }
 
