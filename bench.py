@@ -20,7 +20,8 @@ The routing ids and weights of every workload come from its router logits throug
 (moe_router_topk), whose time is the "router" entry of stage_ms (the timed step starts from the
 ids, at route/permute).
 
-Also reported: per-step p10/p50/p90, GEMM-only time (L1 + L2), the decode aggregate over 64
+Also reported: the step time with calibrated global scales (x and h quantized with the scales of a
+warm-up forward, nvfp4_quantize_act_gs: no amax pass), per-step p10/p50/p90, GEMM-only time (L1 + L2), the decode aggregate over 64
 routing seeds (sum of weight bytes over sum of step times), and achievable ceilings measured on
 the GPU (a 1 GiB device copy, an 8192^3 fp16 GEMM from the vendor BLAS) with the L1 fractions
 against them.
@@ -141,6 +142,31 @@ def time_workload(wl, T, steps, warmup, copies, use_graph):
     spread = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
               "p90": float(np.percentile(per_step, 90))}
 
+    # Calibrated variant: the global scales of x and h given (those of the warm-up forward), so
+    # neither quantizer derives one from an amax.
+    calibrated_ms = None
+    if graphs is not None:
+        gx, gh = L.x_gs.clone(), L.h_gs.clone()
+        cgraphs = []
+        for c in range(copies):
+            L.forward(x, ids_d, wts_d, Ws[c], x_gs=gx, h_gs=gh)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                L.forward(x, ids_d, wts_d, Ws[c], x_gs=gx, h_gs=gh)
+            cgraphs.append(g)
+        for g in cgraphs:
+            g.replay()
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for i in range(steps):
+            cgraphs[i % copies].replay()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        calibrated_ms = c0.elapsed_time(c1) / steps
+        del cgraphs
+
     # Per-stage durations: a short GPU spin ahead of each stage keeps the launch latency out of
     # the event pair that brackets it.
     stage_fns = {
@@ -173,7 +199,8 @@ def time_workload(wl, T, steps, warmup, copies, use_graph):
     w13_bytes = len(active) * (Ws[0].w13_codes[0].numel() + Ws[0].w13_scales[0].numel() + 4)
     del Ws, graphs
     torch.cuda.synchronize()
-    return dict(T=T, ms_per_step=ms_per_step, wall_s=wall, stage_ms=stage_ms, spread=spread, assignments=assign,
+    return dict(T=T, ms_per_step=ms_per_step, wall_s=wall, stage_ms=stage_ms, spread=spread,
+                calibrated_ms=calibrated_ms, assignments=assign,
                 active_experts=len(active), flops=flops, weight_bytes=wbytes, w13_bytes=w13_bytes,
                 l1_flops=4.0 * wl.hidden * wl.intermediate * assign)
 
@@ -441,6 +468,7 @@ def main():
                 "ms_per_step": round(d["ms_per_step"], 5),
                 "ms_per_step_p10_p50_p90": [round(d["spread"][q], 5) for q in ("p10", "p50", "p90")],
                 "gemm_ms": round(d["stage_ms"]["l1"] + d["stage_ms"]["l2"], 5), "weight_GBps": round(gbs, 1),
+                "calibrated_gs_ms_per_step": None if d["calibrated_ms"] is None else round(d["calibrated_ms"], 5),
                 "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "TFLOPs": round(d["flops"] / (d["ms_per_step"] * 1e-3) / 1e12, 3),
                 "active_experts": d["active_experts"], "assignments": d["assignments"],
                 "weight_bytes": d["weight_bytes"], "stage_ms": {k: round(v, 5) for k, v in d["stage_ms"].items()},
@@ -493,6 +521,7 @@ def main():
         "ms_per_step_p10_p50_p90": [round(pre["spread"][q], 4) for q in ("p10", "p50", "p90")],
         "stage_ms": {k: round(v, 4) for k, v in pre["stage_ms"].items()},
         "gemm_ms": round(pre["stage_ms"]["l1"] + pre["stage_ms"]["l2"], 4),
+        "calibrated_gs_ms_per_step": None if pre["calibrated_ms"] is None else round(pre["calibrated_ms"], 4),
         "roofline": {"bound": "mfma", "achieved": round(l1_tflops, 1), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(l1_tflops / PEAK_FP16_TFLOPS, 4), "traffic": recorded_traffic("prefill"),
                      "kernel": "moe_grouped_gemm_l1_silu",

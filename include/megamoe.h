@@ -176,6 +176,27 @@ int32_t nvfp4_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, const
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * nvfp4_quantize_act_gs - NVFP4 quantization with a global scale given by the caller.
+ *
+ * The calibrated form of the quantizer above: the global scale is not derived from this
+ * tensor's amax but supplied (e.g. measured on warm-up inputs), so no amax pass runs.  The
+ * quantizer multiplies by the global scale before forming the E4M3 block scales
+ * (CURRENT_BUG.md@2fc81cc, "Root Cause"); a global scale too large for the data (the
+ * checkpoint's 3977.6 on amax 2-8 in "Key evidence") makes block_amax * gs / 6 exceed 448:
+ * such a block gets the largest finite scale, 448 (0x7E), never NaN, and its elements saturate
+ * at +-6.  Otherwise the block scale and element rules are those of nvfp4_quantize_act, with
+ * the same bit-exact results for the same gs.
+ *
+ * global_scale_in float [1] on the device, finite and > 0 (other values are outside the
+ *              contract; no error is reported).
+ * Other arguments as in nvfp4_quantize_act; rows with row_valid[r] < 0 get zero codes and
+ * scales.  No workspace.
+ * ---------------------------------------------------------------------------------------- */
+int32_t nvfp4_quantize_act_gs(const void* x_bf16, int64_t rows, int64_t cols, const int32_t* row_valid,
+                              const float* global_scale_in, uint8_t* codes, uint8_t* scales,
+                              void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * moe_grouped_gemm_l1_silu - L1 gate+up grouped GEMM over experts with SiLU(gate)*up.
  *
  * CURRENT_BUG.md@2e65594, "Architecture: DeepSeek-V4 MegaMoE" (persistent grouped GEMM, tile

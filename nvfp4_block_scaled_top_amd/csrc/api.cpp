@@ -174,6 +174,17 @@ int32_t nvfp4_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, const
                                     global_scale, static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
+int32_t nvfp4_quantize_act_gs(const void* x_bf16, int64_t rows, int64_t cols, const int32_t* row_valid,
+                              const float* global_scale_in, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 != 0 || rows > ((int64_t)1 << 40) / cols) return MEGAMOE_ERR_SHAPE;
+  if (!global_scale_in) return MEGAMOE_ERR_NULL;
+  if (rows > 0 && (!x_bf16 || !codes || !scales)) return MEGAMOE_ERR_NULL;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  return launch_status(launch_quant_gs(static_cast<const uint16_t*>(x_bf16), rows, cols, row_valid, global_scale_in,
+                                       codes, scales, static_cast<hipStream_t>(stream)));
+}
+
 int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
                                  const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
                                  const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,

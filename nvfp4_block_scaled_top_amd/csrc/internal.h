@@ -47,6 +47,9 @@ hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int
                         const float* amax_in, int32_t amax_in_count, uint8_t* codes, uint8_t* scales, float* gs, float* ws,
                         hipStream_t stream);
 
+hipError_t launch_quant_gs(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* row_valid, const float* gs,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
 // ---- grouped GEMMs ---------------------------------------------------------------------------
 struct GemmArgs {
   // A operand: NVFP4 activations.  For L1, rows are gathered through row_token from a [T, K]

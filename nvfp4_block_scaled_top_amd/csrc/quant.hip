@@ -219,6 +219,38 @@ __global__ __launch_bounds__(kQuantSmallThreads) void quant_small_kernel(const u
   quant_block(x, b, gs, codes, scales);
 }
 
+// Calibrated variant: the global scale comes from the caller (e.g. from a warm-up pass), so there
+// is no amax pass; blocks whose amax * gs / 6 exceeds 448 get the largest E4M3 scale and their
+// elements saturate at +-6.
+__global__ __launch_bounds__(kQuantThreads) void quant_gs_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                 int64_t cols, const int32_t* __restrict__ row_valid,
+                                                                 const float* __restrict__ gs_in,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales) {
+  const float gs = *gs_in;
+  const int64_t bpr = cols / 16;
+  const int64_t nblk = rows * bpr;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * blockDim.x) {
+    if (row_valid != nullptr && row_valid[b / bpr] < 0) {
+      *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{0u, 0u};
+      scales[b] = 0;
+      continue;
+    }
+    quant_block(x, b, gs, codes, scales);
+  }
+}
+
+hipError_t launch_quant_gs(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* row_valid, const float* gs,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const int64_t nblk = rows * (cols / 16);
+  if (nblk == 0) return hipSuccess;
+  int64_t grid = (nblk + kQuantThreads - 1) / kQuantThreads;
+  if (grid > 2048) grid = 2048;
+  hipLaunchKernelGGL(quant_gs_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream, x, rows, cols, row_valid,
+                     gs, codes, scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* row_valid,
                         const float* amax_in, int32_t amax_in_count, uint8_t* codes, uint8_t* scales, float* gs,
                         float* ws, hipStream_t stream) {

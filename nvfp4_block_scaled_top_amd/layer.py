@@ -96,6 +96,7 @@ class MoELayer:
         self.h_gs = torch.empty(1, **f32)
         self.y = torch.empty(max(self.M_cap, 1), H, dtype=torch.int16, device=device)
         self.out = torch.empty(max(T, 1), H, dtype=torch.int16, device=device)
+        self._gs_x, self._gs_h = self.x_gs, self.h_gs            # global scales the GEMMs read
         self.topk_ids = torch.empty(max(T, 1), k, **i32)          # written by route_logits
         self.topk_weights = torch.empty(max(T, 1), k, **f32)
 
@@ -114,23 +115,36 @@ class MoELayer:
                             self.padded_offsets, self.row_token, self.token_rows, self.sched, self.route_ws,
                             block_m_override=self.block_m_override, stream=stream)
 
-    def quantize_x(self, x_bf16: torch.Tensor, stream=None) -> None:
-        mm.nvfp4_quantize_act(x_bf16, self._rows(self.x_codes, self.T), self._rows(self.x_scales, self.T),
-                              self.x_gs, workspace=self.x_ws, stream=stream)
+    def quantize_x(self, x_bf16: torch.Tensor, stream=None, gs: Optional[torch.Tensor] = None) -> None:
+        """gs given (float32 [1] on the device): the calibrated quantizer with that global scale."""
+        self._gs_x = self.x_gs if gs is None else gs
+        if gs is None:
+            mm.nvfp4_quantize_act(x_bf16, self._rows(self.x_codes, self.T), self._rows(self.x_scales, self.T),
+                                  self.x_gs, workspace=self.x_ws, stream=stream)
+        else:
+            mm.nvfp4_quantize_act_gs(x_bf16, gs, self._rows(self.x_codes, self.T), self._rows(self.x_scales, self.T),
+                                     stream=stream)
 
     def l1(self, w: MoEWeights, stream=None) -> None:
-        mm.moe_grouped_gemm_l1_silu(self.x_codes, self.x_scales, self.x_gs, self.row_token, self.padded_offsets,
+        mm.moe_grouped_gemm_l1_silu(self.x_codes, self.x_scales, self._gs_x, self.row_token, self.padded_offsets,
                                     self.counts, self.sched, w.w13_codes, w.w13_scales, w.w13_gs,
                                     self._rows(self.h, self.M_cap), self.h_amax, self.block_m_override,
                                     self.T, stream=stream)
 
-    def quantize_h(self, stream=None) -> None:
-        mm.nvfp4_quantize_act(self._rows(self.h, self.M_cap), self._rows(self.h_codes, self.M_cap),
-                              self._rows(self.h_scales, self.M_cap), self.h_gs,
-                              row_valid=self._rows(self.row_token, self.M_cap), amax_in=self.h_amax, stream=stream)
+    def quantize_h(self, stream=None, gs: Optional[torch.Tensor] = None) -> None:
+        """gs given (float32 [1] on the device): the calibrated quantizer with that global scale."""
+        self._gs_h = self.h_gs if gs is None else gs
+        if gs is None:
+            mm.nvfp4_quantize_act(self._rows(self.h, self.M_cap), self._rows(self.h_codes, self.M_cap),
+                                  self._rows(self.h_scales, self.M_cap), self.h_gs,
+                                  row_valid=self._rows(self.row_token, self.M_cap), amax_in=self.h_amax, stream=stream)
+        else:
+            mm.nvfp4_quantize_act_gs(self._rows(self.h, self.M_cap), gs, self._rows(self.h_codes, self.M_cap),
+                                     self._rows(self.h_scales, self.M_cap),
+                                     row_valid=self._rows(self.row_token, self.M_cap), stream=stream)
 
     def l2(self, w: MoEWeights, stream=None) -> None:
-        mm.moe_grouped_gemm_l2(self.h_codes, self.h_scales, self.h_gs, self.padded_offsets, self.counts, self.sched,
+        mm.moe_grouped_gemm_l2(self.h_codes, self.h_scales, self._gs_h, self.padded_offsets, self.counts, self.sched,
                                w.w2_codes, w.w2_scales, w.w2_gs, self._rows(self.y, self.M_cap),
                                self.block_m_override, self.T, stream=stream)
 
@@ -139,12 +153,14 @@ class MoELayer:
                        self._rows(self.out, self.T), stream=stream)
 
     def forward(self, x_bf16: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, w: MoEWeights,
-                stream=None) -> torch.Tensor:
-        """x_bf16 int16-viewed bf16 [T, H], topk_ids int32 [T, k], topk_weights float32 [T, k]."""
+                stream=None, x_gs: Optional[torch.Tensor] = None, h_gs: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """x_bf16 int16-viewed bf16 [T, H], topk_ids int32 [T, k], topk_weights float32 [T, k].
+        x_gs / h_gs (float32 [1] on the device): calibrated global scales for x and h (e.g. the
+        x_gs / h_gs buffers of a warm-up forward) instead of ones derived from this call's amax."""
         self.route(topk_ids, stream)
-        self.quantize_x(x_bf16, stream)
+        self.quantize_x(x_bf16, stream, gs=x_gs)
         self.l1(w, stream)
-        self.quantize_h(stream)
+        self.quantize_h(stream, gs=h_gs)
         self.l2(w, stream)
         self.combine(topk_weights, stream)
         return self._rows(self.out, self.T)

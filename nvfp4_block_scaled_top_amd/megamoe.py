@@ -40,6 +40,7 @@ SIGNATURES = {
                                 _SZ, _P]),
     "moe_route_permute": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "nvfp4_quantize_act_gs": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "moe_grouped_gemm_l1_silu": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
                                         _P, _P, _P]),
     "moe_grouped_gemm_l2": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _P, _P]),
@@ -148,6 +149,12 @@ def nvfp4_quantize_act(x_bf16, codes, scales, global_scale, workspace=None, row_
     _check("nvfp4_quantize_act", lib().nvfp4_quantize_act(
         _ptr(x_bf16), rows, cols, _ptr(row_valid), _ptr(amax_in), n_amax, _ptr(codes), _ptr(scales), _ptr(global_scale),
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def nvfp4_quantize_act_gs(x_bf16, global_scale_in, codes, scales, row_valid=None, stream=None):
+    rows, cols = x_bf16.shape
+    _check("nvfp4_quantize_act_gs", lib().nvfp4_quantize_act_gs(
+        _ptr(x_bf16), rows, cols, _ptr(row_valid), _ptr(global_scale_in), _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def moe_grouped_gemm_l1_silu(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes,

@@ -414,19 +414,44 @@ def combine(y, token_rows, topk_weights):
     return bf16_round(acc)
 
 
+def quantize_rows_with_global_scale(v, gs, valid_rows=None):
+    """Calibrated quantization: a given global scale (no amax); invalid rows get zero codes and
+    scales.  Blocks whose amax * gs / 6 exceeds 448 take the largest scale and their elements
+    saturate at +-6 (CURRENT_BUG.md@2fc81cc, "Key evidence": the checkpoint's fixed scale on
+    activations with amax 2-8)."""
+    v = np.asarray(v, dtype=np.float64)
+    rows, K = v.shape
+    valid = np.ones(rows, dtype=bool) if valid_rows is None else np.asarray(valid_rows, dtype=bool)
+    codes = np.zeros((rows, K // 2), dtype=np.uint8)
+    scales = np.zeros((rows, K // 16), dtype=np.uint8)
+    idx = np.nonzero(valid)[0]
+    if len(idx):
+        codes[idx], scales[idx] = quantize_with_global_scale(v[idx], np.float32(gs))
+    return codes, scales
+
+
 def moe_layer(x, topk_ids, topk_weights, expert_begin, num_experts, pad_multiple,
-              w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs):
+              w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs, gs_x=None, gs_h=None):
     """The whole routed-expert layer; returns every intermediate in a dict.
 
     Order (CURRENT_BUG.md@2e65594, "Test Plan" Phase 1): route and permute,
     quantize x, L1 gate+up with SiLU(gate)*up, requantize h over valid rows,
-    L2 down, routing-weighted combine.
+    L2 down, routing-weighted combine.  ``gs_x`` / ``gs_h`` given: the
+    calibrated variant, those global scales instead of the amax-derived ones.
     """
     x = np.asarray(x, dtype=np.float64)
     counts, eoff, poff, row_token, token_rows = route(topk_ids, expert_begin, num_experts, pad_multiple)
-    x_codes, x_scales, gs_x = quantize_nvfp4(x)
+    if gs_x is None:
+        x_codes, x_scales, gs_x = quantize_nvfp4(x)
+    else:
+        gs_x = np.float32(gs_x)
+        x_codes, x_scales = quantize_rows_with_global_scale(x, gs_x)
     h, amax_h = moe_l1(x_codes, x_scales, gs_x, row_token, poff, counts, w13_codes, w13_scales, w13_gs)
-    h_codes, h_scales, gs_h = quantize_nvfp4(h, valid_rows=row_token >= 0)
+    if gs_h is None:
+        h_codes, h_scales, gs_h = quantize_nvfp4(h, valid_rows=row_token >= 0)
+    else:
+        gs_h = np.float32(gs_h)
+        h_codes, h_scales = quantize_rows_with_global_scale(h, gs_h, valid_rows=row_token >= 0)
     y = moe_l2(h_codes, h_scales, gs_h, poff, counts, w2_codes, w2_scales, w2_gs)
     out = combine(y, token_rows, topk_weights)
     return dict(counts=counts, expert_offsets=eoff, padded_offsets=poff, row_token=row_token,

@@ -564,3 +564,38 @@ def test_router_large_logits_do_not_overflow():
     assert ids.tolist() == [[0, 1]]
     e = [math.exp(0.0), math.exp(-1.0), math.exp(-2000.0), math.exp(-2.0)]
     np.testing.assert_allclose(w[0], np.array([e[0], e[1]]) / math.fsum(e), rtol=2.0 ** -23)
+
+
+# ---------------------------------------------------------------------------
+# calibrated variant: a given global scale, saturating block scales and codes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("factor", [0.37, 4.0, 40.0])
+def test_calibrated_quantizer_vs_brute_force(factor):
+    rng = np.random.default_rng(int(factor * 100))
+    x = O.bf16_round(rng.standard_normal((4, 64)) * 0.09)
+    x[1, :16] = 0.0
+    gs = np.float32(O.global_scale(float(np.abs(x).max())) * np.float32(factor))
+    valid = np.array([True, True, False, True])
+    codes, scales = O.quantize_rows_with_global_scale(x, gs, valid_rows=valid)
+    unpacked = O.unpack_nibbles(codes)
+    for r in range(4):
+        for b in range(4):
+            blk = x[r, 16 * b: 16 * b + 16]
+            if not valid[r]:
+                assert scales[r, b] == 0 and np.all(unpacked[r, 16 * b: 16 * b + 16] == 0)
+                continue
+            sc = brute_block_scale(np.abs(blk).max(), gs)
+            assert scales[r, b] == sc
+            for i, v in enumerate(blk):
+                assert unpacked[r, 16 * b + i] == brute_code(v, gs, sc)
+    if factor > 1:  # the scale is too large for the data: saturated blocks and elements occur
+        assert (scales == 0x7E).sum() > 0 and (unpacked[valid.repeat(64).reshape(4, 64)] & 7 == 7).sum() > 0
+
+
+def test_calibrated_equals_amax_derived_at_the_amax_scale():
+    rng = np.random.default_rng(3)
+    x = O.bf16_round(rng.standard_normal((6, 96)))
+    c, s, gs = O.quantize_nvfp4(x)
+    c2, s2 = O.quantize_rows_with_global_scale(x, gs)
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
