@@ -398,10 +398,12 @@ def moe_l2(h_codes, h_scales, gs_h, padded_offsets, counts, w2_codes, w2_scales,
     return y
 
 
-def combine(y, token_rows, topk_weights):
+def combine(y, token_rows, topk_weights, y_shared=None):
     """out[t] = bf16( sum over j ascending of w[t,j] * y[token_rows[t,j]] ), +0 if none local.
 
     The routing weight is applied here and only here, once per (token, expert).
+    ``y_shared`` [T, H] (the shared expert's output, weight 1) is added to the
+    routed sum before the rounding.
     """
     token_rows = np.asarray(token_rows)
     w = np.asarray(topk_weights, dtype=np.float64)
@@ -411,7 +413,34 @@ def combine(y, token_rows, topk_weights):
         r = token_rows[:, j]
         m = r >= 0
         acc[m] += w[m, j, None] * y[r[m]]
+    if y_shared is not None:
+        acc = acc + np.asarray(y_shared, dtype=np.float64)
     return bf16_round(acc)
+
+
+# ---------------------------------------------------------------------------
+# Dense NVFP4 linear layers (one expert for every row) and the shared expert
+# ---------------------------------------------------------------------------
+
+def nvfp4_linear(a_codes, a_scales, gs_a, w_codes, w_scales, gs_w):
+    """out = bf16(A @ W^T / (gs_a * gs_w)) for NVFP4 A [M, K] and W [N, K]: the down projection of
+    one expert applied to every row (the expert GEMM with a single group)."""
+    return l2_down(dequantize_blocks(a_codes, a_scales), dequantize_blocks(w_codes, w_scales), gs_a, gs_w)
+
+
+def nvfp4_linear_gate_up_silu(a_codes, a_scales, gs_a, w13_codes, w13_scales, gs_w):
+    """h = bf16(SiLU(gate) * up) for NVFP4 A [M, K] and W13 [2I, K] (gate rows, then up rows)."""
+    return l1_gate_up_silu(dequantize_blocks(a_codes, a_scales), dequantize_blocks(w13_codes, w13_scales), gs_a, gs_w)
+
+
+def shared_expert(x_codes, x_scales, gs_x, w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs):
+    """A shared expert applied to every token (DeepSeek-style MoE adds one to the routed experts):
+    the same x codes, gate+up with SiLU, h requantized with its own amax over all rows, down
+    projection.  Weights are one expert's: w13 [2I, K], w2 [H, I] with scalar global scales.
+    Returns (y_shared [T, H] bf16 values, h, gs_h)."""
+    h = nvfp4_linear_gate_up_silu(x_codes, x_scales, gs_x, w13_codes, w13_scales, w13_gs)
+    h_codes, h_scales, gs_h = quantize_nvfp4(h)
+    return nvfp4_linear(h_codes, h_scales, gs_h, w2_codes, w2_scales, w2_gs), h, gs_h
 
 
 def quantize_rows_with_global_scale(v, gs, valid_rows=None):
@@ -431,13 +460,15 @@ def quantize_rows_with_global_scale(v, gs, valid_rows=None):
 
 
 def moe_layer(x, topk_ids, topk_weights, expert_begin, num_experts, pad_multiple,
-              w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs, gs_x=None, gs_h=None):
+              w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs, gs_x=None, gs_h=None, shared=None):
     """The whole routed-expert layer; returns every intermediate in a dict.
 
     Order (CURRENT_BUG.md@2e65594, "Test Plan" Phase 1): route and permute,
     quantize x, L1 gate+up with SiLU(gate)*up, requantize h over valid rows,
     L2 down, routing-weighted combine.  ``gs_x`` / ``gs_h`` given: the
     calibrated variant, those global scales instead of the amax-derived ones.
+    ``shared``: (w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs) of a
+    shared expert whose output is added in the combine.
     """
     x = np.asarray(x, dtype=np.float64)
     counts, eoff, poff, row_token, token_rows = route(topk_ids, expert_begin, num_experts, pad_multiple)
@@ -453,7 +484,11 @@ def moe_layer(x, topk_ids, topk_weights, expert_begin, num_experts, pad_multiple
         gs_h = np.float32(gs_h)
         h_codes, h_scales = quantize_rows_with_global_scale(h, gs_h, valid_rows=row_token >= 0)
     y = moe_l2(h_codes, h_scales, gs_h, poff, counts, w2_codes, w2_scales, w2_gs)
-    out = combine(y, token_rows, topk_weights)
+    y_shared = None
+    if shared is not None:
+        y_shared, _, _ = shared_expert(x_codes, x_scales, gs_x, *shared)
+    out = combine(y, token_rows, topk_weights, y_shared)
     return dict(counts=counts, expert_offsets=eoff, padded_offsets=poff, row_token=row_token,
                 token_rows=token_rows, x_codes=x_codes, x_scales=x_scales, gs_x=gs_x,
-                h=h, amax_h=amax_h, h_codes=h_codes, h_scales=h_scales, gs_h=gs_h, y=y, out=out)
+                h=h, amax_h=amax_h, h_codes=h_codes, h_scales=h_scales, gs_h=gs_h, y=y, y_shared=y_shared,
+                out=out)

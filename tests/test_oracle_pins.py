@@ -599,3 +599,72 @@ def test_calibrated_equals_amax_derived_at_the_amax_scale():
     c, s, gs = O.quantize_nvfp4(x)
     c2, s2 = O.quantize_rows_with_global_scale(x, gs)
     assert np.array_equal(c, c2) and np.array_equal(s, s2)
+
+
+# ---------------------------------------------------------------------------
+# dense NVFP4 linear layers, the shared expert and its term in the combine
+# ---------------------------------------------------------------------------
+
+def test_nvfp4_linear_bruteforce_fractions():
+    """out = bf16 of the exact rational A.W^T / (gs_a gs_w), from codes and scales decoded here."""
+    rng = np.random.default_rng(31)
+    a = O.bf16_round(rng.standard_normal((3, 48)) * 0.1)
+    w = O.bf16_round(rng.standard_normal((5, 48)) * 0.02)
+    ac, as_, ag = O.quantize_nvfp4(a)
+    wc, ws, wg = O.quantize_nvfp4(w)
+    got = O.nvfp4_linear(ac, as_, ag, wc, ws, wg)
+    acodes, wcodes = O.unpack_nibbles(ac), O.unpack_nibbles(wc)
+
+    def dec(code, sc):
+        mag = E2M1_FR[code & 7] * E4M3_FR[sc]
+        return -mag if code & 8 else mag
+
+    for i in range(3):
+        for n in range(5):
+            s = sum(dec(int(acodes[i, k]), int(as_[i, k // 16])) * dec(int(wcodes[n, k]), int(ws[n, k // 16]))
+                    for k in range(48))
+            exact = s / (Fraction(float(ag)) * Fraction(float(wg)))
+            # bf16 of the exact value: the nearest of the two bf16 neighbours of float(exact)
+            want = float(O.bf16_round(np.array([float(exact)]))[0])
+            assert got[i, n] == want or abs(Fraction(got[i, n]) - exact) <= abs(Fraction(want) - exact)
+
+
+def test_gate_up_silu_dense_is_the_single_expert_l1():
+    inp = _tiny_layer_inputs(E=1, k=1, T=9, seed=8)
+    r = O.moe_layer(**inp)
+    h = O.nvfp4_linear_gate_up_silu(r["x_codes"], r["x_scales"], r["gs_x"], inp["w13_codes"][0],
+                                    inp["w13_scales"][0], inp["w13_gs"][0])
+    rows = r["token_rows"][:, 0]
+    assert np.array_equal(h, r["h"][rows])
+
+
+def test_shared_expert_equals_routed_single_expert():
+    """A shared expert with expert 0's weights equals the routed layer's y when every token goes
+    to expert 0 alone with weight 1 (E=1, k=1): same x codes, same h amax, same GEMMs."""
+    inp = _tiny_layer_inputs(E=1, k=1, T=11, seed=9)
+    inp["topk_weights"][:] = 1.0
+    r = O.moe_layer(**inp)
+    shared = tuple(inp[n][0] for n in ("w13_codes", "w13_scales", "w13_gs", "w2_codes", "w2_scales", "w2_gs"))
+    ys, h, gs_h = O.shared_expert(r["x_codes"], r["x_scales"], r["gs_x"], *shared)
+    rows = r["token_rows"][:, 0]
+    assert np.array_equal(ys, r["y"][rows]) and gs_h == r["gs_h"]
+    # with it as a shared expert on top of the same routing, out = bf16(y + y) = 2 y exactly
+    r2 = O.moe_layer(**inp, shared=shared)
+    assert np.array_equal(r2["out"], 2 * r["out"])
+
+
+def test_combine_shared_term():
+    rng = np.random.default_rng(10)
+    y = O.bf16_round(rng.standard_normal((12, 32)))
+    ys = O.bf16_round(rng.standard_normal((5, 32)))
+    rows = np.array([[0, 3], [-1, 5], [-1, -1], [7, 8], [11, 2]], np.int32)
+    w = rng.uniform(0.1, 0.5, (5, 2)).astype(np.float32)
+    out = O.combine(y, rows, np.zeros_like(w), ys)
+    assert np.array_equal(out, ys)  # zero routing weights: the shared output alone
+    out = O.combine(y, rows, w, ys)
+    for t in range(5):
+        for c in range(32):
+            s = Fraction(float(ys[t, c])) + sum(Fraction(float(w[t, j])) * Fraction(float(y[rows[t, j], c]))
+                                                for j in range(2) if rows[t, j] >= 0)
+            want = float(O.bf16_round(np.array([float(s)]))[0])
+            assert out[t, c] == want or abs(Fraction(out[t, c]) - s) <= abs(Fraction(want) - s)
