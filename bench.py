@@ -256,6 +256,47 @@ def decode_seed_aggregate(wl, seeds, reps, copies=4):
     return res
 
 
+def dense_linear_bench(reps=20):
+    """nvfp4_linear (the L2 GEMM with one group of every row) at a prefill shape (M=8192, K=7168,
+    N=2048: TFLOP/s) and a decode shape (M=8, same K and N: weight GB/s); operands quantized on the
+    GPU from random bf16."""
+    import torch
+    from nvfp4_block_scaled_top_amd import layer, megamoe
+
+    res = {}
+    stream = torch.cuda.current_stream()
+    K, N = 7168, 2048
+    w = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
+    wc = torch.empty(N, K // 2, dtype=torch.uint8, device="cuda")
+    wsc = torch.empty(N, K // 16, dtype=torch.uint8, device="cuda")
+    wg = torch.empty(1, dtype=torch.float32, device="cuda")
+    layer.quantize_matrix(w, wc, wsc, wg)
+    wbytes = wc.numel() + wsc.numel() + 4
+    for M in (8192, 8):
+        a = (torch.randn(M, K, device="cuda") * 0.09).to(torch.bfloat16)
+        ac = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
+        asc = torch.empty(M, K // 16, dtype=torch.uint8, device="cuda")
+        ag = torch.empty(1, dtype=torch.float32, device="cuda")
+        layer.quantize_matrix(a, ac, asc, ag)
+        out = torch.empty(M, N, dtype=torch.int16, device="cuda")
+        ws = torch.empty(megamoe.megamoe_dense_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+        call = lambda: megamoe.nvfp4_linear(ac, asc, ag, wc, wsc, wg, out, ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[f"M{M}_K{K}_N{N}"] = {"ms": round(ms, 5), "TFLOPs": round(2.0 * M * K * N / (ms * 1e-3) / 1e12, 2),
+                                  "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1)}
+        log(f"[bench] dense linear M={M}: {ms * 1e3:.1f} us, {res[f'M{M}_K{K}_N{N}']['TFLOPs']} TFLOP/s")
+    return res
+
+
 def measured_ceilings():
     """Achievable ceilings on this GPU: a 1 GiB device copy (read + write bytes) and an 8192^3 fp16
     GEMM from the vendor BLAS (torch.matmul)."""
@@ -481,10 +522,13 @@ def main():
 
     seed_agg = None
     ceilings = None
+    dense = None
     if not args.quick:
         if args.decode_seeds > 0:
             log(f"[bench] decode aggregate over {args.decode_seeds} routing seeds")
             seed_agg = decode_seed_aggregate(synth.WORKLOADS[1], args.decode_seeds, reps=10)
+        log("[bench] dense NVFP4 linear")
+        dense = dense_linear_bench()
         log("[bench] measured ceilings")
         ceilings = measured_ceilings()
 
@@ -529,6 +573,7 @@ def main():
                                                   if ceilings else None)},
         "decode": decode,
         "decode_seed_aggregate": seed_agg,
+        "dense_linear": dense,
         "measured_ceilings": ceilings,
         "cpu_baseline": cpu,
     }

@@ -82,6 +82,10 @@ size_t megamoe_route_workspace_bytes(int32_t T, int32_t k, int32_t num_experts);
 /* Scratch bytes nvfp4_quantize_act needs for a [rows, cols] tensor. */
 size_t megamoe_quant_workspace_bytes(int64_t rows, int64_t cols);
 
+/* Scratch bytes nvfp4_linear and nvfp4_linear_gate_up_silu need for M rows (0 if M is out of
+ * range). */
+size_t megamoe_dense_workspace_bytes(int64_t M);
+
 /* ------------------------------------------------------------------------------------------
  * moe_router_topk - router logits -> top-k expert ids and weights.
  *
@@ -252,6 +256,45 @@ int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, con
                             int32_t max_rows_per_expert, void* y_bf16, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * nvfp4_linear - dense NVFP4 linear layer: the L2 GEMM with one group holding every row.
+ *
+ * The expert GEMM of moe_grouped_gemm_l2 (CURRENT_BUG.md@2e65594, "What's Been Verified": NVFP4
+ * L1/L2) for a single expert applied to all M rows, as for a dense projection:
+ *   out[m, n] = bf16( sum_k dec(a[m, k]) * dec(W[n, k]) / (gs_a * gs_w) )
+ * a_codes/a_scales/a_gs   NVFP4 A [M, K/2], [M, K/16], [1] (e.g. from nvfp4_quantize_act).
+ * w_codes/w_scales/w_gs   NVFP4 W [N, K/2], [N, K/16], [1].
+ * out_bf16     bf16 [M, N].
+ * workspace    >= megamoe_dense_workspace_bytes(0) bytes (64; the group's tables are written
+ *              there before the GEMM runs).
+ * Limits: 0 <= M < 2^31, K >= 128 and a multiple of 128, N >= 256 and a multiple of 256.
+ * ---------------------------------------------------------------------------------------- */
+int32_t nvfp4_linear(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs, int64_t M,
+                     int32_t K, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                     int32_t N, void* out_bf16, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * nvfp4_linear_gate_up_silu - dense gate+up projection with SiLU(gate)*up: the L1 GEMM with one
+ * group holding every row.
+ *
+ * As moe_grouped_gemm_l1_silu (CURRENT_BUG.md@2e65594, "Test Plan" Phase 1: L1 gate+up, then
+ * SiLU) for a single expert applied to all M rows, e.g. a shared expert:
+ *   h[m, i] = bf16( SiLU(g) * u ),  g / u = sum_k dec(a[m, k]) * dec(W13[i or I+i, k]) / (gs_a * gs_w)
+ * a_codes/a_scales/a_gs   NVFP4 A [M, K/2], [M, K/16], [1].
+ * w13_codes/w13_scales/w13_gs   [2I, K/2], [2I, K/16], [1]; rows 0..I-1 gate, I..2I-1 up.
+ * h_bf16       bf16 [M, I].  h_amax_parts float [MEGAMOE_L1_AMAX_PARTS]: as for
+ *              moe_grouped_gemm_l1_silu (max |h| = max over the slots; every slot written).
+ * workspace    >= megamoe_dense_workspace_bytes(M) bytes (the group's tables and an identity
+ *              row map).
+ * Limits: 0 <= M < 2^31, K >= 256 and a multiple of 256, I >= 128 and a multiple of 128.
+ * ---------------------------------------------------------------------------------------- */
+int32_t nvfp4_linear_gate_up_silu(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                  int64_t M, int32_t K, const uint8_t* w13_codes,
+                                  const uint8_t* w13_scales, const float* w13_gs, int32_t I,
+                                  void* h_bf16, float* h_amax_parts, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * moe_combine - routing-weighted combine of the expert outputs back into token order.
  *
  * The routing weight of each (token, expert) is applied exactly once, here:
@@ -261,7 +304,15 @@ int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, con
  *
  * y_bf16 [M_cap, H] bf16;  token_rows int32 [T*k];  topk_weights float [T, k];
  * out_bf16 bf16 [T, H];  T >= 0, 1 <= k <= 64, H a multiple of 8.
+ *
+ * moe_combine_shared adds a shared expert's output (weight 1, one row per token, bf16 [T, H],
+ * e.g. from nvfp4_linear) to the routed sum before the rounding:
+ *   out[t, :] = bf16( (sum over j as above) + y_shared[t, :] )
  * ---------------------------------------------------------------------------------------- */
+int32_t moe_combine_shared(const void* y_bf16, const int32_t* token_rows, const float* topk_weights,
+                           int32_t T, int32_t k, int32_t H, const void* y_shared_bf16, void* out_bf16,
+                           void* stream);
+
 int32_t moe_combine(const void* y_bf16, const int32_t* token_rows, const float* topk_weights,
                     int32_t T, int32_t k, int32_t H, void* out_bf16, void* stream);
 

@@ -16,7 +16,7 @@ LIB_NAME = "libmegamoe.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["router.hip", "route.hip", "quant.hip", "gemm.hip", "combine.hip", "api.cpp"]
+SOURCES = ["router.hip", "route.hip", "quant.hip", "gemm.hip", "dense.hip", "combine.hip", "api.cpp"]
 
 # Device code: gfx950 only, no fast-math (the quantizer relies on IEEE division, fma and rint),
 # and packed fp32 instructions disabled.

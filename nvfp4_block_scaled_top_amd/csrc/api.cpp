@@ -228,8 +228,64 @@ int32_t moe_combine(const void* y_bf16, const int32_t* token_rows, const float* 
   if (T > 0 && (!y_bf16 || !token_rows || !topk_weights || !out_bf16)) return MEGAMOE_ERR_NULL;
   const int32_t dev = check_device();
   if (dev != MEGAMOE_OK) return dev;
-  return launch_status(launch_combine(static_cast<const uint16_t*>(y_bf16), token_rows, topk_weights, T, k, H,
+  return launch_status(launch_combine(static_cast<const uint16_t*>(y_bf16), token_rows, topk_weights, T, k, H, nullptr,
                                       static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_combine_shared(const void* y_bf16, const int32_t* token_rows, const float* topk_weights, int32_t T,
+                           int32_t k, int32_t H, const void* y_shared_bf16, void* out_bf16, void* stream) {
+  if (T < 0 || k < 1 || k > 64 || H < 8 || H % 8 != 0) return MEGAMOE_ERR_SHAPE;
+  if (T > 0 && (!y_bf16 || !token_rows || !topk_weights || !y_shared_bf16 || !out_bf16)) return MEGAMOE_ERR_NULL;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  return launch_status(launch_combine(static_cast<const uint16_t*>(y_bf16), token_rows, topk_weights, T, k, H,
+                                      static_cast<const uint16_t*>(y_shared_bf16), static_cast<uint16_t*>(out_bf16),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t megamoe_dense_workspace_bytes(int64_t M) {
+  if (M < 0 || M >= ((int64_t)1 << 31)) return 0;
+  return (size_t)(kDenseHeader + M) * sizeof(int32_t);
+}
+
+int32_t nvfp4_linear(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs, int64_t M, int32_t K,
+                     const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int32_t N, void* out_bf16,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!gemm_shape_ok(1, N, K, M)) return MEGAMOE_ERR_SHAPE;
+  if (!a_gs || !w_codes || !w_scales || !w_gs || !workspace) return MEGAMOE_ERR_NULL;
+  if (M > 0 && (!a_codes || !a_scales || !out_bf16)) return MEGAMOE_ERR_NULL;
+  if (workspace_bytes < (size_t)kDenseHeader * sizeof(int32_t)) return MEGAMOE_ERR_WORKSPACE;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  if (M == 0) return MEGAMOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* ws = static_cast<int32_t*>(workspace);
+  const int32_t r = launch_status(launch_dense_setup((int32_t)M, ws, false, s));
+  if (r != MEGAMOE_OK) return r;
+  const GemmClasses cls{M <= kSmallClassMaxTokens, M > kSmallClassMaxTokens};  // exactly the group's class
+  GemmArgs ga{a_codes, a_scales, a_gs, nullptr, ws + kDensePoff, ws + kDenseCounts, ws + kDenseSched, w_codes,
+              w_scales, w_gs, 1, K, N, out_bf16, nullptr, 0};
+  return launch_status(launch_gemm_l2(ga, cls, s));
+}
+
+int32_t nvfp4_linear_gate_up_silu(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs, int64_t M,
+                                  int32_t K, const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
+                                  int32_t I, void* h_bf16, float* h_amax_parts, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!gemm_shape_ok(1, K, I, M)) return MEGAMOE_ERR_SHAPE;
+  if (!a_gs || !w13_codes || !w13_scales || !w13_gs || !h_amax_parts || !workspace) return MEGAMOE_ERR_NULL;
+  if (M > 0 && (!a_codes || !a_scales || !h_bf16)) return MEGAMOE_ERR_NULL;
+  if (workspace_bytes < megamoe_dense_workspace_bytes(M)) return MEGAMOE_ERR_WORKSPACE;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* ws = static_cast<int32_t*>(workspace);
+  const int32_t r = launch_status(launch_dense_setup((int32_t)M, ws, true, s));
+  if (r != MEGAMOE_OK) return r;
+  const GemmClasses cls{M <= kSmallClassMaxTokens, M > kSmallClassMaxTokens};  // exactly the group's class
+  GemmArgs ga{a_codes, a_scales, a_gs, ws + kDenseHeader, ws + kDensePoff, ws + kDenseCounts, ws + kDenseSched,
+              w13_codes, w13_scales, w13_gs, 1, K, I, h_bf16, h_amax_parts, 0};
+  return launch_status(launch_gemm_l1(ga, cls, s));
 }
 
 }  // extern "C"

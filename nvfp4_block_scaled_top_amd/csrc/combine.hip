@@ -4,7 +4,8 @@
 // and the k contributions of a token are summed in slot order in fp32 (the runner takes
 // topk_weights from the router: nvfp4-megamoe-kernel CURRENT_BUG.md@2e65594, "Test Plan"
 // Phase 1).  A gather per token (not a scatter with atomics) keeps the result deterministic.
-// Memory-bound: one thread per 8 output columns (16-byte loads and stores).
+// Memory-bound: one thread per 8 output columns (16-byte loads and stores).  A shared expert's
+// output (y_shared, weight 1, one row per token) is added after the routed sum, before rounding.
 #include "device_common.h"
 #include "internal.h"
 
@@ -12,6 +13,7 @@ namespace megamoe {
 
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ token_rows,
                                                       const float* __restrict__ w, int32_t T, int32_t k, int32_t H,
+                                                      const uint16_t* __restrict__ y_shared,
                                                       uint16_t* __restrict__ out) {
   const int64_t per = H / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -29,6 +31,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       acc[2 * q + 1] = fmaf(wt, bf16_bits_to_f32(v[q] >> 16), acc[2 * q + 1]);
     }
   }
+  if (y_shared != nullptr) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(y_shared + t * H + c8 * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += bf16_bits_to_f32(v[q] & 0xFFFFu);
+      acc[2 * q + 1] += bf16_bits_to_f32(v[q] >> 16);
+    }
+  }
   u32x4 o;
 #pragma unroll
   for (int q = 0; q < 4; ++q) o[q] = f32_to_bf16_bits(acc[2 * q]) | (f32_to_bf16_bits(acc[2 * q + 1]) << 16);
@@ -36,11 +46,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 }
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* token_rows, const float* w, int32_t T, int32_t k,
-                          int32_t H, uint16_t* out, hipStream_t stream) {
+                          int32_t H, const uint16_t* y_shared, uint16_t* out, hipStream_t stream) {
   const int64_t n = (int64_t)T * (H / 8);
   if (n == 0) return hipSuccess;
   const int64_t grid = (n + 255) / 256;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, y, token_rows, w, T, k, H, out);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, y, token_rows, w, T, k, H, y_shared,
+                     out);
   return hipGetLastError();
 }
 

@@ -76,8 +76,15 @@ struct GemmClasses {
 hipError_t launch_gemm_l1(const GemmArgs& a, GemmClasses c, hipStream_t stream);
 hipError_t launch_gemm_l2(const GemmArgs& a, GemmClasses c, hipStream_t stream);
 
+// ---- dense layers (one group of M rows) -------------------------------------------------------
+// int32 workspace layout: counts [1], padded offsets [2], tile table [sched_len(1)], then the
+// identity row map [M] (gate+up only).
+constexpr int kDenseCounts = 0, kDensePoff = 1, kDenseSched = 4, kDenseHeader = 16;
+static_assert(kDenseSched + 4 + 3 * 1 + 2 <= kDenseHeader, "dense tables fit the header");
+hipError_t launch_dense_setup(int32_t M, int32_t* ws, bool with_rows, hipStream_t stream);
+
 // ---- combine ---------------------------------------------------------------------------------
 hipError_t launch_combine(const uint16_t* y, const int32_t* token_rows, const float* w, int32_t T,
-                          int32_t k, int32_t H, uint16_t* out, hipStream_t stream);
+                          int32_t k, int32_t H, const uint16_t* y_shared, uint16_t* out, hipStream_t stream);
 
 }  // namespace megamoe

@@ -6,6 +6,9 @@ PyTorch allocates device memory here; every computation is a call into libmegamo
 intermediate buffers for a fixed (T, k, E, H, I, P) and runs the six-call forward:
 route/permute, quantize x, L1 gate+up + SiLU, quantize h (amax from L1), L2 down, combine.
 ``forward_logits`` starts one step earlier, from router logits (router + route/permute in one call).
+A shared expert (one expert's weights applied to every token, ``MoEWeights`` with E = 1) can be
+passed to ``forward``: its dense gate+up+SiLU and down projections run on the same x codes and its
+output is added in the combine.
 """
 from __future__ import annotations
 
@@ -100,6 +103,33 @@ class MoELayer:
         self.topk_ids = torch.empty(max(T, 1), k, **i32)          # written by route_logits
         self.topk_weights = torch.empty(max(T, 1), k, **f32)
 
+    def _shared_buffers(self, shared: MoEWeights) -> None:
+        Is, dev = shared.intermediate, self.out.device
+        if getattr(self, "_sh_I", None) == Is:
+            return
+        T, H = max(self.T, 1), self.H
+        self._sh_I = Is
+        self.sh_h = torch.empty(T, Is, dtype=torch.int16, device=dev)
+        self.sh_h_amax = torch.empty(mm.L1_AMAX_PARTS, dtype=torch.float32, device=dev)
+        self.sh_h_codes = torch.empty(T, Is // 2, dtype=torch.uint8, device=dev)
+        self.sh_h_scales = torch.empty(T, Is // 16, dtype=torch.uint8, device=dev)
+        self.sh_h_gs = torch.empty(1, dtype=torch.float32, device=dev)
+        self.sh_y = torch.empty(T, H, dtype=torch.int16, device=dev)
+        self.sh_ws = torch.empty(mm.megamoe_dense_workspace_bytes(self.T), dtype=torch.uint8, device=dev)
+
+    def shared_expert(self, shared: MoEWeights, stream=None) -> None:
+        """Dense gate+up+SiLU on the x codes, requantize its h (own amax), dense down: sh_y [T, H]."""
+        self._shared_buffers(shared)
+        T = self.T
+        mm.nvfp4_linear_gate_up_silu(self._rows(self.x_codes, T), self._rows(self.x_scales, T), self._gs_x,
+                                     shared.w13_codes[0], shared.w13_scales[0], shared.w13_gs[0:1],
+                                     self._rows(self.sh_h, T), self.sh_h_amax, self.sh_ws, stream=stream)
+        mm.nvfp4_quantize_act(self._rows(self.sh_h, T), self._rows(self.sh_h_codes, T),
+                              self._rows(self.sh_h_scales, T), self.sh_h_gs, amax_in=self.sh_h_amax, stream=stream)
+        mm.nvfp4_linear(self._rows(self.sh_h_codes, T), self._rows(self.sh_h_scales, T), self.sh_h_gs,
+                        shared.w2_codes[0], shared.w2_scales[0], shared.w2_gs[0:1], self._rows(self.sh_y, T),
+                        self.sh_ws, stream=stream)
+
     def _rows(self, t: torch.Tensor, n: int) -> torch.Tensor:
         return t[:n] if n > 0 else t[:0]
 
@@ -148,21 +178,30 @@ class MoELayer:
                                w.w2_codes, w.w2_scales, w.w2_gs, self._rows(self.y, self.M_cap),
                                self.block_m_override, self.T, stream=stream)
 
-    def combine(self, topk_weights: torch.Tensor, stream=None) -> None:
-        mm.moe_combine(self._rows(self.y, self.M_cap), self._rows(self.token_rows, self.T * self.k), topk_weights,
-                       self._rows(self.out, self.T), stream=stream)
+    def combine(self, topk_weights: torch.Tensor, stream=None, shared: bool = False) -> None:
+        if shared:
+            mm.moe_combine_shared(self._rows(self.y, self.M_cap), self._rows(self.token_rows, self.T * self.k),
+                                  topk_weights, self._rows(self.sh_y, self.T), self._rows(self.out, self.T),
+                                  stream=stream)
+        else:
+            mm.moe_combine(self._rows(self.y, self.M_cap), self._rows(self.token_rows, self.T * self.k),
+                           topk_weights, self._rows(self.out, self.T), stream=stream)
 
     def forward(self, x_bf16: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, w: MoEWeights,
-                stream=None, x_gs: Optional[torch.Tensor] = None, h_gs: Optional[torch.Tensor] = None) -> torch.Tensor:
+                stream=None, x_gs: Optional[torch.Tensor] = None, h_gs: Optional[torch.Tensor] = None,
+                shared: Optional[MoEWeights] = None) -> torch.Tensor:
         """x_bf16 int16-viewed bf16 [T, H], topk_ids int32 [T, k], topk_weights float32 [T, k].
         x_gs / h_gs (float32 [1] on the device): calibrated global scales for x and h (e.g. the
-        x_gs / h_gs buffers of a warm-up forward) instead of ones derived from this call's amax."""
+        x_gs / h_gs buffers of a warm-up forward) instead of ones derived from this call's amax.
+        shared: a shared expert (E = 1) whose output is added in the combine."""
         self.route(topk_ids, stream)
         self.quantize_x(x_bf16, stream, gs=x_gs)
         self.l1(w, stream)
         self.quantize_h(stream, gs=h_gs)
         self.l2(w, stream)
-        self.combine(topk_weights, stream)
+        if shared is not None:
+            self.shared_expert(shared, stream)
+        self.combine(topk_weights, stream, shared=shared is not None)
         return self._rows(self.out, self.T)
 
     def forward_logits(self, x_bf16: torch.Tensor, logits: torch.Tensor, w: MoEWeights, stream=None) -> torch.Tensor:

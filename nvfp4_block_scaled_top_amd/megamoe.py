@@ -45,6 +45,10 @@ SIGNATURES = {
                                         _P, _P, _P]),
     "moe_grouped_gemm_l2": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
+    "moe_combine_shared": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P]),
+    "megamoe_dense_workspace_bytes": (_SZ, [_I64]),
+    "nvfp4_linear": (_I32, [_P, _P, _P, _I64, _I32, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "nvfp4_linear_gate_up_silu": (_I32, [_P, _P, _P, _I64, _I32, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -185,3 +189,36 @@ def moe_combine(y_bf16, token_rows, topk_weights, out_bf16, stream=None):
     H = out_bf16.shape[1]
     _check("moe_combine", lib().moe_combine(
         _ptr(y_bf16), _ptr(token_rows), _ptr(topk_weights), T, k, H, _ptr(out_bf16), _stream(stream)))
+
+
+def moe_combine_shared(y_bf16, token_rows, topk_weights, y_shared_bf16, out_bf16, stream=None):
+    T, k = topk_weights.shape
+    H = out_bf16.shape[1]
+    _check("moe_combine_shared", lib().moe_combine_shared(
+        _ptr(y_bf16), _ptr(token_rows), _ptr(topk_weights), T, k, H, _ptr(y_shared_bf16), _ptr(out_bf16),
+        _stream(stream)))
+
+
+# ---- dense layers ------------------------------------------------------------------------------
+
+def megamoe_dense_workspace_bytes(M: int) -> int:
+    return int(lib().megamoe_dense_workspace_bytes(M))
+
+
+def nvfp4_linear(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, out_bf16, workspace, stream=None):
+    M, Kh = a_codes.shape
+    N = w_codes.shape[0]
+    _check("nvfp4_linear", lib().nvfp4_linear(
+        _ptr(a_codes), _ptr(a_scales), _ptr(a_gs), M, 2 * Kh, _ptr(w_codes), _ptr(w_scales), _ptr(w_gs), N,
+        _ptr(out_bf16), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def nvfp4_linear_gate_up_silu(a_codes, a_scales, a_gs, w13_codes, w13_scales, w13_gs, h_bf16, h_amax_parts,
+                              workspace, stream=None):
+    M, Kh = a_codes.shape
+    I = w13_codes.shape[0] // 2
+    if h_amax_parts.numel() < L1_AMAX_PARTS:
+        raise MegaMoEError(f"h_amax_parts needs {L1_AMAX_PARTS} floats")
+    _check("nvfp4_linear_gate_up_silu", lib().nvfp4_linear_gate_up_silu(
+        _ptr(a_codes), _ptr(a_scales), _ptr(a_gs), M, 2 * Kh, _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), I,
+        _ptr(h_bf16), _ptr(h_amax_parts), _ptr(workspace), _nbytes(workspace), _stream(stream)))
