@@ -664,10 +664,11 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
 }
 
 // ============================================================================================
-// Large class: 256x256 tiles, stages of raw NVFP4 streamed straight into an LDS ring.
+// Large class: 256x256 tiles (128x512 for an expert's last rows when they are at most 128),
+// stages of raw NVFP4 streamed straight into an LDS ring.
 //
 // Global -> LDS: gfx950's global_load_lds_dwordx4 writes each lane's 16 bytes into LDS without a
-// register round trip (lane i of an instruction lands at base + 16*i).  Stage ks+kLAhead is
+// register round trip (lane i of an instruction lands at base + 16*i).  Stage ks+kAhead is
 // requested while stage ks is computed; a stage is consumed after an explicit s_waitcnt vmcnt
 // (this wave's loads) and one s_barrier (everyone's).  The slot being refilled was last read two
 // stages earlier, so that single barrier per stage orders both directions.  (__syncthreads()
@@ -676,288 +677,349 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
 //
 // LDS holds raw codes and scales (0.5625 B/element) and each wave decodes the fragments it needs
 // right before its MFMAs.  Decoding into fp16 tiles in LDS instead would move ~3.5x more LDS
-// bytes per MFMA; per-wave decoding costs 4 VALU instructions per 32-cycle
+// bytes per MFMA (measured slower); per-wave decoding costs 6 VALU instructions per 32-cycle
 // v_mfma_f32_32x32x16_f16, which the VALU issues while the matrix core runs (the 32x32x16 shape
 // sustains ~97% of the fp16 peak on gfx950, the 16x16x32 shape only ~55%).
 //
 // Stage layout (per operand): codes row-major, kLRowBytes per tile row R, with the 16-byte chunk
 // c (elements 32c..32c+31 of the stage) stored in slot c ^ swizzle(R) so that the 16-byte
-// fragment reads of 8 consecutive rows hit distinct banks; a DMA instruction covers 1024 / 
+// fragment reads of 8 consecutive rows hit distinct banks; a DMA instruction covers 1024 /
 // kLRowBytes rows with kLChunks lanes per row (row-contiguous global bytes).  Scales: the stage's 8
 // block scales of row R at R * 8 (lane half h reads the 4 bytes at R * 8 + 4h).
 // Lane (p = lane % 32, h = lane / 32) of a 32-row fragment owns elements [h * kLKs/2, +kLKs/2) of
 // its row and feeds [h * kLKs/2 + 8s, +8) to MFMA step s as the MFMA's k = 8h..8h+7.  A and B use
 // the same map, so each dot product runs over every element once.
 //
-// Waves are kLWM x 2 (4 x 2 by default), each (256/kLWM) x 128 of the tile: kLMI x 4 MFMA blocks
-// of 32x32 (128 fp32 accumulators).  Two waves per SIMD hide each other's LDS waits and barrier
-// skew; the price is 6 decode VALU per MFMA instead of 4 with 2 x 2 waves of 128 x 128.
-// L1: tile weight rows 0..127 are gate rows nt*128.., 128..255 the matching up rows, so a wave
-// holds gate and up of the same 64 h columns and applies SiLU(gate)*up in registers.
-// L2: tile weight rows are output rows nt*256..+256.
+// Two tile shapes with the same per-wave block: 8 waves, each 64 token rows x 128 weight rows
+// (2 x 4 MFMA blocks of 32x32, 128 fp32 accumulators), two per SIMD (they hide each other's LDS
+// waits and barrier skew).  Full tiles are 256x256 with the waves 4 (M) x 2 (N); tail tiles are
+// 128x512 with the waves 2 x 4 and serve an expert's last m-tile when it holds at most 128 token
+// rows, which halves the padded rows there (on the 8192-token Zipf prefill the MFMA work of the
+// class drops to 92%).  Both shapes cost the same per tile, so one persistent list holds them.
+// L1: tile weight rows 0..BN/2-1 are gate rows nt*BN/2.., the next BN/2 the matching up rows, so a
+// wave holds gate and up of the same 64 h columns and applies SiLU(gate)*up in registers.
+// L2: tile weight rows are output rows nt*BN..+BN.
 // The epilogue stages the bf16 tile in LDS and writes it with 16-byte row-contiguous stores.
 // ============================================================================================
-#ifndef MEGAMOE_LARGE_WM
-#define MEGAMOE_LARGE_WM 4
-#endif
-constexpr int kLBm = kBlockMLarge, kLBn = 256;
-constexpr int kLWM = MEGAMOE_LARGE_WM, kLWN = 2;                 // waves along M and N
-constexpr int kLWaves = kLWM * kLWN, kLThreads = kLWaves * kWave;
-constexpr int kLMI = kLBm / 32 / kLWM;                           // 32-row MFMA blocks per wave
-constexpr int kLRowsPerWave = kLBm / kLWaves;                    // DMA rows per wave and operand
-constexpr int kLKs = 128, kLSlots = 4, kLAhead = 2;               // stage depth, ring slots, prefetch
+constexpr int kLWaves = 8, kLThreads = kLWaves * kWave;
+constexpr int kLKs = 128;                                        // stage depth (K elements)
 constexpr int kLRowBytes = kLKs / 2;                             // code bytes of one row per stage
-constexpr int kLChunks = kLRowBytes / 16;                        // 16-byte chunks per row (2 or 4)
-constexpr int kLSwzShift = kLChunks == 2 ? 2 : 1;                // row bits that pick the swizzle
+constexpr int kLChunks = kLRowBytes / 16;                        // 16-byte chunks per row
+constexpr int kLSwzShift = 1;                                    // row bits that pick the swizzle
 constexpr int kLScaleRow = kLKs / 16;                            // scale bytes of one row per stage
 constexpr int kLSteps = kLKs / 16;                               // 32x32x16 MFMA steps per stage
-constexpr int kLCodeBytes = kLBm * kLRowBytes;
-constexpr int kLScaleBytes = kLBm * kLScaleRow;
-constexpr int kLOpBytes = kLCodeBytes + kLScaleBytes;            // one operand, one stage
-constexpr int kLStageBytes = 2 * kLOpBytes;
-constexpr int kLLdsBytes = kLSlots * kLStageBytes;
-constexpr int kLCodeDma = kLRowsPerWave * kLRowBytes / 1024;     // 16-byte DMA per wave and operand
-constexpr int kLScaleDma = kLRowsPerWave * kLScaleRow / 256;     // 4-byte DMA per wave and operand
-constexpr int kLDmaPerWave = 2 * (kLCodeDma + kLScaleDma);
-constexpr int kLOutPitchL1 = 128 * 2 + 16, kLOutPitchL2 = 256 * 2 + 16;  // bf16 staging pitches
-static_assert(kLKs == 64 || kLKs == 128, "stage depth");
-static_assert(kLBm == 256 && kLBn == 256, "large tiles are 256x256");
-static_assert(kLWM == 2 || kLWM == 4, "2x2 or 4x2 waves");
-static_assert(kLCodeDma >= 1 && kLScaleDma >= 1 && kLRowsPerWave * kLScaleRow % 256 == 0, "DMA split");
-static_assert(kLAhead <= kLSlots - 2, "refilled slot must have been read two stages earlier");
-static_assert(kLBm * kLOutPitchL2 <= kLLdsBytes && kLBm * kLOutPitchL1 <= kLLdsBytes, "staging fits");
+constexpr int kLMI = 2;                                          // 32-row MFMA blocks per wave
 
-// Wait until at most `stages_after` (<= kLAhead) later stages' loads are outstanding for this wave.
-template <int K = kLAhead>
+template <int BM, int BN, int Slots, int Ahead>
+struct LShape {
+  static constexpr int kBm = BM, kBn = BN;
+  static constexpr int kWM = BM / 64, kWN = BN / 128;            // waves along M and N
+  static constexpr int kSlots = Slots, kAhead = Ahead;           // ring slots, stages in flight
+  static constexpr int kARows = BM / kLWaves, kBRows = BN / kLWaves;  // DMA rows per wave
+  static constexpr int kACodeDma = kARows * kLRowBytes / 1024;   // 16-byte DMA per wave
+  static constexpr int kBCodeDma = kBRows * kLRowBytes / 1024;
+  static constexpr int kBScaleDma = kBRows * kLScaleRow / 256;   // 4-byte DMA per wave
+  // A scales: one 4-byte DMA per wave covers 32 rows; with BM < 256 two waves load the same rows
+  // (same bytes to the same place), which keeps every wave's load count equal.
+  static constexpr int kAScaleRows = 32;
+  static constexpr int kDmaPerWave = kACodeDma + kBCodeDma + 1 + kBScaleDma;
+  static constexpr int kACodeBytes = BM * kLRowBytes, kBCodeBytes = BN * kLRowBytes;
+  static constexpr int kAOpBytes = kACodeBytes + BM * kLScaleRow;
+  static constexpr int kStageBytes = kAOpBytes + BN * (kLRowBytes + kLScaleRow);
+  static constexpr int kRingBytes = Slots * kStageBytes;
+  static constexpr int kPitchL1 = BN + 16, kPitchL2 = 2 * BN + 16;  // bf16 staging pitches
+  static_assert(kWM * kWN == kLWaves, "8 waves of 64 x 128");
+  static_assert(kACodeDma >= 1 && kBCodeDma >= 1 && kBScaleDma >= 1 && BM % kAScaleRows == 0, "DMA split");
+  static_assert(kBRows * kLScaleRow % 256 == 0 && kARows <= kAScaleRows, "scale DMA split");
+  static_assert(kAhead <= kSlots - 2, "refilled slot must have been read two stages earlier");
+};
+using LFull = LShape<kBlockMLarge, 256, 4, 2>;
+using LTail = LShape<128, 512, 3, 1>;
+constexpr int kLLdsBytes = LFull::kRingBytes > LTail::kRingBytes ? LFull::kRingBytes : LTail::kRingBytes;
+static_assert(LFull::kBm * LFull::kPitchL2 <= kLLdsBytes && LTail::kBm * LTail::kPitchL2 <= kLLdsBytes,
+              "staging fits");
+
+// Wait until at most `stages_after` (<= S::kAhead) later stages' loads are outstanding for this wave.
+template <class S, int K = S::kAhead>
 __device__ __forceinline__ void wait_stage(int stages_after) {
   if constexpr (K == 0) {
     wait_vmcnt<0>();
   } else {
-    if (stages_after >= K) wait_vmcnt<K * kLDmaPerWave>();
-    else wait_stage<K - 1>(stages_after);
+    if (stages_after >= K) wait_vmcnt<K * S::kDmaPerWave>();
+    else wait_stage<S, K - 1>(stages_after);
   }
+}
+
+// One output tile of shape S: expert e, m-tile rows [row0, row0 + min(rows_left, BM)), n-tile nt.
+template <bool kL1, class S>
+__device__ __forceinline__ void large_tile(const GemmArgs& p, uint8_t* smem, int e, int row0, int rows_left, int nt,
+                                           float gs_a, uint32_t& amax_bits) {
+  constexpr int BM = S::kBm, BN = S::kBn;
+  const int K = p.K, Kh = K / 2, Ks = K / 16;
+  const int Nw = kL1 ? 2 * p.N : p.N;
+  const int nks = K / kLKs;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  const int wm = wave / S::kWN, wn = wave % S::kWN;
+  const int p32 = lane & 31, h2 = lane >> 5;
+
+  // first tile weight row of this wave's 32-column fragment f
+  auto brow_of = [&](int f) {
+    return kL1 ? (f < 2 ? wn * 64 + 32 * f : BN / 2 + wn * 64 + 32 * (f - 2)) : wn * 128 + 32 * f;
+  };
+  // ---- DMA sources of this lane ----------------------------------------------------------------
+  // codes: instruction j covers tile rows base + j*rows_per + lane/kLChunks; lane%kLChunks picks
+  // the LDS slot and the global chunk (lane%kLChunks) ^ swizzle(row) goes there; scales:
+  // instruction j covers rows base + 32j + lane/2, lane%2 picking the 4-byte half (LDS scale
+  // layout: 8 bytes per row).
+  auto a_row_of = [&](int R) -> int64_t {
+    const int Rv = R < rows_left ? R : 0;  // rows past the expert read row 0; never stored
+    const int64_t r = row0 + Rv;
+    return kL1 ? (int64_t)p.row_token[r] : r;
+  };
+  auto b_row_of = [&](int R) -> int64_t {
+    if (kL1) return (int64_t)e * Nw + (R < BN / 2 ? nt * (BN / 2) + R : p.N + nt * (BN / 2) + R - BN / 2);
+    return (int64_t)e * Nw + nt * BN + R;
+  };
+  constexpr int rows_per = 1024 / kLRowBytes;
+  const uint8_t* a_code_src[S::kACodeDma];
+  const uint8_t* b_code_src[S::kBCodeDma];
+#pragma unroll
+  for (int j = 0; j < S::kACodeDma; ++j) {
+    const int R = S::kARows * wave + rows_per * j + lane / kLChunks;
+    const int chunk = (lane % kLChunks) ^ ((R >> kLSwzShift) & (kLChunks - 1));
+    a_code_src[j] = p.a_codes + a_row_of(R) * Kh + 16 * chunk;
+  }
+#pragma unroll
+  for (int j = 0; j < S::kBCodeDma; ++j) {
+    const int R = S::kBRows * wave + rows_per * j + lane / kLChunks;
+    const int chunk = (lane % kLChunks) ^ ((R >> kLSwzShift) & (kLChunks - 1));
+    b_code_src[j] = p.w_codes + b_row_of(R) * Kh + 16 * chunk;
+  }
+  static_assert(kLScaleRow == 8, "scale DMA assumes 128-K stages");
+  const int a_scale_row0 = S::kAScaleRows * (wave % (BM / S::kAScaleRows));
+  const uint8_t* a_scale_src = p.a_scales + a_row_of(a_scale_row0 + lane / 2) * Ks + 4 * (lane & 1);
+  const uint8_t* b_scale_src[S::kBScaleDma];
+#pragma unroll
+  for (int j = 0; j < S::kBScaleDma; ++j) {
+    const int R = S::kBRows * wave + 32 * j + lane / 2;
+    b_scale_src[j] = p.w_scales + b_row_of(R) * Ks + 4 * (lane & 1);
+  }
+
+  f32x16 acc[kLMI][4];
+#pragma unroll
+  for (int i = 0; i < kLMI; ++i)
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.f;
+
+  // S::kDmaPerWave DMA instructions per wave: this wave's rows of both operands.
+  auto issue_stage = [&](int ks, int slot) {
+    const uint32_t lb = lds_addr(smem + slot * S::kStageBytes);
+    const uint32_t lbb = lb + S::kAOpBytes;
+    const int64_t off = (int64_t)ks * kLRowBytes, soff = (int64_t)ks * kLScaleRow;
+#pragma unroll
+    for (int j = 0; j < S::kACodeDma; ++j)
+      dma16(a_code_src[j] + off, lb + (S::kARows * wave + rows_per * j) * kLRowBytes);
+#pragma unroll
+    for (int j = 0; j < S::kBCodeDma; ++j)
+      dma16(b_code_src[j] + off, lbb + (S::kBRows * wave + rows_per * j) * kLRowBytes);
+    dma4(a_scale_src + soff, lb + S::kACodeBytes + a_scale_row0 * kLScaleRow);
+#pragma unroll
+    for (int j = 0; j < S::kBScaleDma; ++j)
+      dma4(b_scale_src[j] + soff, lbb + S::kBCodeBytes + (S::kBRows * wave + 32 * j) * kLScaleRow);
+  };
+  auto compute_stage = [&](int slot) {
+    const uint8_t* base = smem + slot * S::kStageBytes;
+    const uint8_t* a_codes = base;
+    const uint8_t* a_scales = base + S::kACodeBytes;
+    const uint8_t* b_codes = base + S::kAOpBytes;
+    const uint8_t* b_scales = b_codes + S::kBCodeBytes;
+    constexpr int CPL = kLChunks / 2;  // chunks per lane half
+    // rows 32i + p and brow_of(f) + p share (row >> shift) with p: offsets are multiples of 32
+    const int swz = (p32 >> kLSwzShift) & (kLChunks - 1);
+    // scale bytes of this lane half: 4 per row (128-K stages)
+    auto scale_word = [&](const uint8_t* sp, int row) -> uint32_t {
+      return *reinterpret_cast<const uint32_t*>(sp + row * kLScaleRow + 4 * h2);
+    };
+    u32x4 araw[kLMI][CPL], braw[4][CPL];
+    uint32_t asw[kLMI], bsw[4];
+#pragma unroll
+    for (int i = 0; i < kLMI; ++i) {
+      const int row = wm * (32 * kLMI) + 32 * i + p32;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+        araw[i][j] = *reinterpret_cast<const u32x4*>(a_codes + row * kLRowBytes + 16 * ((CPL * h2 + j) ^ swz));
+      asw[i] = scale_word(a_scales, row);
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int row = brow_of(f) + p32;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+        braw[f][j] = *reinterpret_cast<const u32x4*>(b_codes + row * kLRowBytes + 16 * ((CPL * h2 + j) ^ swz));
+      bsw[f] = scale_word(b_scales, row);
+    }
+    // fp16 scale pairs: pair q covers steps 4q..4q+3 (blocks 2q, 2q+1 of this lane half)
+    f16x2 asc[kLMI][CPL], bsc[4][CPL];
+#pragma unroll
+    for (int i = 0; i < kLMI; ++i) {
+      asc[i][0] = e4m3x2_to_f16(asw[i], false);
+      asc[i][1] = e4m3x2_to_f16(asw[i], true);
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      bsc[f][0] = e4m3x2_to_f16(bsw[f], false);
+      bsc[f][1] = e4m3x2_to_f16(bsw[f], true);
+    }
+    auto sc = [](const f16x2 (&pr)[CPL], int step) {
+      const f16x2 v = pr[step >> 2];
+      return (step & 2) ? bcast_hi(v) : bcast_lo(v);
+    };
+    auto word = [](const u32x4 (&r)[CPL], int step) { return r[step >> 2][step & 3]; };
+    // Software pipeline: B fragments of step s+1 are decoded between the MFMAs of step s.
+    constexpr int kBPerI = 4 / kLMI;             // B fragments decoded per A row block
+    constexpr int kVPerM = 2 + 8 * kBPerI / 4;   // VALU per MFMA: (8 for A + 8 per B) / 4 MFMAs
+    f16x8 b[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) b[f] = decode8(word(braw[f], 0), sc(bsc[f], 0));
+#pragma unroll
+    for (int st = 0; st < kLSteps; ++st) {
+      f16x8 bn[4];
+#pragma unroll
+      for (int i = 0; i < kLMI; ++i) {
+        const f16x8 a = decode8(word(araw[i], st), sc(asc[i], st));
+        if (st + 1 < kLSteps) {
+#pragma unroll
+          for (int q = 0; q < kBPerI; ++q) {
+            const int f = kBPerI * i + q;
+            bn[f] = decode8(word(braw[f], st + 1), sc(bsc[f], st + 1));
+          }
+        }
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[i][f] = mfma32(a, b[f], acc[i][f]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, kVPerM, 0);  // its share of the decode
+        }
+      }
+      if (st + 1 < kLSteps) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) b[f] = bn[f];
+      }
+    }
+  };
+
+  for (int ks = 0; ks < S::kAhead && ks < nks; ++ks) issue_stage(ks, ks);
+  for (int ks = 0; ks < nks; ++ks) {
+    // Request stage ks+kAhead into the slot last read by stage ks-2 (every wave has passed the
+    // barrier of stage ks-1 since), then wait until this wave's stage-ks loads have landed.
+    if (ks + S::kAhead < nks) issue_stage(ks + S::kAhead, (ks + S::kAhead) % S::kSlots);
+    const int after = nks - 1 - ks;
+    wait_stage<S>(after < S::kAhead ? after : S::kAhead);
+    __builtin_amdgcn_s_barrier();  // everyone's stage-ks loads have landed
+    compute_stage(ks % S::kSlots);
+  }
+  __syncthreads();  // all waves are done reading the ring before it is reused for staging
+
+  // ---- epilogue: scale, (SiLU*up), bf16, stage in LDS, coalesced stores ------------------------
+  // accumulator r of block (i, f) is row 32i + 8(r/4) + 4h + r%4, column 32f + p of the wave tile
+  const float inv = (float)(1.0 / ((double)gs_a * (double)p.w_gs[e]));
+  constexpr int pitch = kL1 ? S::kPitchL1 : S::kPitchL2;
+#pragma unroll
+  for (int i = 0; i < kLMI; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * (32 * kLMI) + 32 * i + 8 * (r >> 2) + 4 * h2 + (r & 3);
+      const bool ok = row < rows_left;
+      if (kL1) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const float gt = acc[i][f][r] * inv, up = acc[i][f + 2][r] * inv;
+          const uint32_t hb = f32_to_bf16_bits(silu_f32(gt) * up);
+          *reinterpret_cast<uint16_t*>(smem + row * pitch + 2 * (wn * 64 + 32 * f + p32)) = (uint16_t)hb;
+          const uint32_t mag = ok ? (hb & 0x7FFFu) : 0u;
+          amax_bits = amax_bits > mag ? amax_bits : mag;
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          *reinterpret_cast<uint16_t*>(smem + row * pitch + 2 * (wn * 128 + 32 * f + p32)) =
+              (uint16_t)f32_to_bf16_bits(acc[i][f][r] * inv);
+      }
+    }
+  }
+  __syncthreads();
+  {
+    constexpr int cols = kL1 ? BN / 2 : BN;
+    constexpr int chunks = cols * 2 / 16;  // 16-byte chunks per row
+    const int nrows = rows_left < BM ? rows_left : BM;
+    uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
+    const int col0 = nt * cols;
+    for (int idx = tid; idx < nrows * chunks; idx += kLThreads) {
+      const int r = idx / chunks, c = idx - r * chunks;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * pitch + 16 * c);
+      *reinterpret_cast<u32x4*>(out + (int64_t)(row0 + r) * p.N + col0 + 8 * c) = v;
+    }
+  }
+  __syncthreads();  // staging reads done before the next tile's DMA refills the ring
 }
 
 template <bool kL1>
 __global__ __launch_bounds__(kLThreads, 1) void gemm_large_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLLdsBytes];
-  __shared__ int s_pref[kMaxExperts + 1];
+  __shared__ int s_tpref[kMaxExperts + 1];  // exclusive prefix of tiles per expert
+  __shared__ int s_mt[kMaxExperts];         // 2 * (large m-tiles) + (last one is a tail tile)
   __shared__ uint32_t s_amax[kLWaves];
   const int E = p.E;
-  for (int j = threadIdx.x; j <= E; j += blockDim.x) s_pref[j] = p.sched[sched_pref_large(E) + j];
-  __syncthreads();
-  const int ntn = kL1 ? p.N / 128 : p.N / kLBn;
-  const int total = s_pref[E] * ntn;
-  const int K = p.K, Kh = K / 2, Ks = K / 16;
-  const int Nw = kL1 ? 2 * p.N : p.N;
-  const int nks = K / kLKs;
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-  const int wm = wave / kLWN, wn = wave % kLWN;
-  const int p32 = lane & 31, h2 = lane >> 5;
+  // n-tiles per m-tile: full tiles cover 256 weight rows, tail tiles 512 (L1: half gate, half up)
+  const int ntn_full = kL1 ? p.N / 128 : p.N / 256;
+  const bool tails = kL1 ? p.N % 256 == 0 : p.N % 512 == 0;
+  const int ntn_tail = kL1 ? p.N / 256 : p.N / 512;
+  {
+    const int32_t* __restrict__ pref = p.sched + sched_pref_large(E);
+    for (int j = tid; j < E; j += blockDim.x) {
+      const int nm = pref[j + 1] - pref[j];
+      const int last = p.counts[j] - kBlockMLarge * (nm - 1);
+      const int tail = tails && nm > 0 && last <= LTail::kBm ? 1 : 0;
+      s_mt[j] = 2 * nm + tail;
+      s_tpref[j] = (nm - tail) * ntn_full + tail * ntn_tail;  // tiles of expert j (scanned below)
+    }
+    __syncthreads();
+    if (tid < kWave) {  // wave 0: exclusive prefix over the experts
+      int carry = 0;
+      for (int c = 0; c < E; c += kWave) {
+        const int e = c + lane;
+        const int v = e < E ? s_tpref[e] : 0;
+        int incl = v;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int t = __shfl_up(incl, o, kWave);
+          if (lane >= o) incl += t;
+        }
+        if (e < E) s_tpref[e] = carry + incl - v;
+        carry += __shfl(incl, kWave - 1, kWave);
+      }
+      if (lane == 0) s_tpref[E] = carry;
+    }
+    __syncthreads();
+  }
   const float gs_a = *p.a_gs;
   uint32_t amax_bits = 0;
 
-  // first tile weight row of this wave's 32-column fragment f
-  auto brow_of = [&](int f) {
-    return kL1 ? (f < 2 ? wn * 64 + 32 * f : 128 + wn * 64 + 32 * (f - 2)) : wn * 128 + 32 * f;
-  };
-
-  const XcdTiles tl(total);
+  const XcdTiles tl(s_tpref[E]);
   for (int t = tl.t; t < tl.end; t += tl.stride) {
-    const TileInfo ti = decode_tile(s_pref, E, ntn, t, kLBm, p.padded_offsets, p.counts);
-    // ---- DMA sources of this lane --------------------------------------------------------------
-    // codes: instruction j covers tile rows kLRowsPerWave*wave + j*rows_per + lane/kLChunks;
-    // lane%kLChunks picks the LDS slot and the global chunk (lane%kLChunks) ^ swizzle(row) goes
-    // there; scales: instruction j covers rows kLRowsPerWave*wave + 32j + lane/2, lane%2 picking
-    // the 4-byte half (LDS scale layout: 8 bytes per row).
-    auto a_row_of = [&](int R) -> int64_t {
-      const int Rv = R < ti.rows_left ? R : 0;  // rows past the expert read row 0; never stored
-      const int64_t r = ti.row0 + Rv;
-      return kL1 ? (int64_t)p.row_token[r] : r;
-    };
-    auto b_row_of = [&](int R) -> int64_t {
-      if (kL1) return (int64_t)ti.e * Nw + (R < 128 ? ti.nt * 128 + R : p.N + ti.nt * 128 + R - 128);
-      return (int64_t)ti.e * Nw + ti.nt * kLBn + R;
-    };
-    constexpr int rows_per = 1024 / kLRowBytes;
-    const uint8_t* a_code_src[kLCodeDma];
-    const uint8_t* b_code_src[kLCodeDma];
-#pragma unroll
-    for (int j = 0; j < kLCodeDma; ++j) {
-      const int R = kLRowsPerWave * wave + rows_per * j + lane / kLChunks;
-      const int chunk = (lane % kLChunks) ^ ((R >> kLSwzShift) & (kLChunks - 1));
-      a_code_src[j] = p.a_codes + a_row_of(R) * Kh + 16 * chunk;
-      b_code_src[j] = p.w_codes + b_row_of(R) * Kh + 16 * chunk;
-    }
-    static_assert(kLScaleRow == 8, "scale DMA assumes 128-K stages");
-    const uint8_t* a_scale_src[kLScaleDma];
-    const uint8_t* b_scale_src[kLScaleDma];
-#pragma unroll
-    for (int j = 0; j < kLScaleDma; ++j) {
-      const int R = kLRowsPerWave * wave + 32 * j + lane / 2;
-      a_scale_src[j] = p.a_scales + a_row_of(R) * Ks + 4 * (lane & 1);
-      b_scale_src[j] = p.w_scales + b_row_of(R) * Ks + 4 * (lane & 1);
-    }
-
-    f32x16 acc[kLMI][4];
-#pragma unroll
-    for (int i = 0; i < kLMI; ++i)
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.f;
-
-    // kLDmaPerWave DMA instructions per wave: this wave's kLRowsPerWave rows of both operands.
-    auto issue_stage = [&](int ks, int slot) {
-      const uint32_t lb = lds_addr(smem + slot * kLStageBytes);
-      const int64_t off = (int64_t)ks * kLRowBytes, soff = (int64_t)ks * kLScaleRow;
-#pragma unroll
-      for (int j = 0; j < kLCodeDma; ++j) {
-        dma16(a_code_src[j] + off, lb + (kLRowsPerWave * wave + rows_per * j) * kLRowBytes);
-        dma16(b_code_src[j] + off, lb + kLOpBytes + (kLRowsPerWave * wave + rows_per * j) * kLRowBytes);
-      }
-#pragma unroll
-      for (int j = 0; j < kLScaleDma; ++j) {
-        const int so = kLCodeBytes + (kLRowsPerWave * wave + 32 * j) * kLScaleRow;
-        dma4(a_scale_src[j] + soff, lb + so);
-        dma4(b_scale_src[j] + soff, lb + kLOpBytes + so);
-      }
-    };
-    auto compute_stage = [&](int slot) {
-      const uint8_t* base = smem + slot * kLStageBytes;
-      const uint8_t* a_codes = base;
-      const uint8_t* a_scales = base + kLCodeBytes;
-      const uint8_t* b_codes = base + kLOpBytes;
-      const uint8_t* b_scales = b_codes + kLCodeBytes;
-      constexpr int CPL = kLChunks / 2;  // chunks per lane half
-      // rows 32i + p and brow_of(f) + p share (row >> shift) with p: offsets are multiples of 32
-      const int swz = (p32 >> kLSwzShift) & (kLChunks - 1);
-      // scale bytes of this lane half: 2 (64-K stages) or 4 (128-K stages) per row
-      auto scale_word = [&](const uint8_t* sp, int row) -> uint32_t {
-        return *reinterpret_cast<const uint32_t*>(sp + row * kLScaleRow + 4 * h2);
-      };
-      u32x4 araw[kLMI][CPL], braw[4][CPL];
-      uint32_t asw[kLMI], bsw[4];
-#pragma unroll
-      for (int i = 0; i < kLMI; ++i) {
-        const int row = wm * (32 * kLMI) + 32 * i + p32;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-          araw[i][j] = *reinterpret_cast<const u32x4*>(a_codes + row * kLRowBytes + 16 * ((CPL * h2 + j) ^ swz));
-        asw[i] = scale_word(a_scales, row);
-      }
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int row = brow_of(f) + p32;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-          braw[f][j] = *reinterpret_cast<const u32x4*>(b_codes + row * kLRowBytes + 16 * ((CPL * h2 + j) ^ swz));
-        bsw[f] = scale_word(b_scales, row);
-      }
-      // fp16 scale pairs: pair q covers steps 4q..4q+3 (blocks 2q, 2q+1 of this lane half)
-      f16x2 asc[kLMI][CPL], bsc[4][CPL];
-#pragma unroll
-      for (int i = 0; i < kLMI; ++i) {
-        asc[i][0] = e4m3x2_to_f16(asw[i], false);
-        if (CPL == 2) asc[i][CPL - 1] = e4m3x2_to_f16(asw[i], true);
-      }
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        bsc[f][0] = e4m3x2_to_f16(bsw[f], false);
-        if (CPL == 2) bsc[f][CPL - 1] = e4m3x2_to_f16(bsw[f], true);
-      }
-      auto sc = [](const f16x2 (&pr)[CPL], int step) {
-        const f16x2 v = pr[step >> 2];
-        return (step & 2) ? bcast_hi(v) : bcast_lo(v);
-      };
-      auto word = [](const u32x4 (&r)[CPL], int step) { return r[step >> 2][step & 3]; };
-      // Software pipeline: B fragments of step s+1 are decoded between the MFMAs of step s.
-      constexpr int kBPerI = 4 / kLMI;             // B fragments decoded per A row block
-      constexpr int kVPerM = 2 + 8 * kBPerI / 4;   // VALU per MFMA: (8 for A + 8 per B) / 4 MFMAs
-      f16x8 b[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) b[f] = decode8(word(braw[f], 0), sc(bsc[f], 0));
-#pragma unroll
-      for (int st = 0; st < kLSteps; ++st) {
-        f16x8 bn[4];
-#pragma unroll
-        for (int i = 0; i < kLMI; ++i) {
-          const f16x8 a = decode8(word(araw[i], st), sc(asc[i], st));
-          if (st + 1 < kLSteps) {
-#pragma unroll
-            for (int q = 0; q < kBPerI; ++q) {
-              const int f = kBPerI * i + q;
-              bn[f] = decode8(word(braw[f], st + 1), sc(bsc[f], st + 1));
-            }
-          }
-#pragma unroll
-          for (int f = 0; f < 4; ++f) acc[i][f] = mfma32(a, b[f], acc[i][f]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // 1 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, kVPerM, 0);  // its share of the decode
-          }
-        }
-        if (st + 1 < kLSteps) {
-#pragma unroll
-          for (int f = 0; f < 4; ++f) b[f] = bn[f];
-        }
-      }
-    };
-
-    for (int ks = 0; ks < kLAhead && ks < nks; ++ks) issue_stage(ks, ks);
-    for (int ks = 0; ks < nks; ++ks) {
-      // Request stage ks+kLAhead into the slot last read by stage ks-2 (every wave has passed the
-      // barrier of stage ks-1 since), then wait until this wave's stage-ks loads have landed.
-      if (ks + kLAhead < nks) issue_stage(ks + kLAhead, (ks + kLAhead) % kLSlots);
-      const int after = nks - 1 - ks;
-      wait_stage(after < kLAhead ? after : kLAhead);
-      __builtin_amdgcn_s_barrier();  // everyone's stage-ks loads have landed
-      compute_stage(ks % kLSlots);
-    }
-    __syncthreads();  // all waves are done reading the ring before it is reused for staging
-
-    // ---- epilogue: scale, (SiLU*up), bf16, stage in LDS, coalesced stores ----------------------
-    // accumulator r of block (i, f) is row 32i + 8(r/4) + 4h + r%4, column 32f + p of the wave tile
-    const float inv = (float)(1.0 / ((double)gs_a * (double)p.w_gs[ti.e]));
-    constexpr int pitch = kL1 ? kLOutPitchL1 : kLOutPitchL2;
-#pragma unroll
-    for (int i = 0; i < kLMI; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * (32 * kLMI) + 32 * i + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        const bool ok = row < ti.rows_left;
-        if (kL1) {
-#pragma unroll
-          for (int f = 0; f < 2; ++f) {
-            const float gt = acc[i][f][r] * inv, up = acc[i][f + 2][r] * inv;
-            const uint32_t hb = f32_to_bf16_bits(silu_f32(gt) * up);
-            *reinterpret_cast<uint16_t*>(smem + row * pitch + 2 * (wn * 64 + 32 * f + p32)) = (uint16_t)hb;
-            const uint32_t mag = ok ? (hb & 0x7FFFu) : 0u;
-            amax_bits = amax_bits > mag ? amax_bits : mag;
-          }
-        } else {
-#pragma unroll
-          for (int f = 0; f < 4; ++f)
-            *reinterpret_cast<uint16_t*>(smem + row * pitch + 2 * (wn * 128 + 32 * f + p32)) =
-                (uint16_t)f32_to_bf16_bits(acc[i][f][r] * inv);
-        }
-      }
-    }
-    __syncthreads();
-    {
-      constexpr int cols = kL1 ? 128 : 256;
-      constexpr int chunks = cols * 2 / 16;  // 16-byte chunks per row
-      const int nrows = ti.rows_left < kLBm ? ti.rows_left : kLBm;
-      uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
-      const int col0 = ti.nt * cols;
-      for (int idx = tid; idx < nrows * chunks; idx += kLThreads) {
-        const int r = idx / chunks, c = idx - r * chunks;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * pitch + 16 * c);
-        *reinterpret_cast<u32x4*>(out + (int64_t)(ti.row0 + r) * p.N + col0 + 8 * c) = v;
-      }
-    }
-    __syncthreads();  // staging reads done before the next tile's DMA refills the ring
+    const int e = find_expert(s_tpref, E, 1, t);
+    const int local = t - s_tpref[e];
+    const int nm = s_mt[e] >> 1, tail = s_mt[e] & 1;
+    const int nfull = (nm - tail) * ntn_full;
+    const int mt = local < nfull ? local / ntn_full : nm - 1;
+    const int row0 = p.padded_offsets[e] + kBlockMLarge * mt;
+    const int rows_left = p.counts[e] - kBlockMLarge * mt;
+    if (local < nfull) large_tile<kL1, LFull>(p, smem, e, row0, rows_left, local - mt * ntn_full, gs_a, amax_bits);
+    else large_tile<kL1, LTail>(p, smem, e, row0, rows_left, local - nfull, gs_a, amax_bits);
   }
   if (kL1) {
     amax_bits = wave_max_u32(amax_bits);
