@@ -393,6 +393,28 @@ def traffic_pass(which: str) -> None:
     log(f"[traffic-pass] {which} T={T} done")
 
 
+def trace_steps(n: int) -> None:
+    """Launch sequence for a rocprofv3 kernel trace: for the prefill (T=8192) and decode (T=1, 4, 8)
+    workloads in turn, quantize the weights, then run n eager layer forwards (no timing)."""
+    import torch
+    from nvfp4_block_scaled_top_amd import layer, synth
+
+    for wl, T, copies in ((synth.WORKLOADS[3], 8192, 1), (synth.WORKLOADS[1], 1, 4), (synth.WORKLOADS[1], 4, 4),
+                          (synth.WORKLOADS[1], 8, 4)):
+        _, idd, wtd, counts = gpu_routing(wl, T, 0, "cuda")
+        # expert 0 is always quantized too, so weight quantization separates every workload in
+        # the trace (decode T=1 has no local expert at seed 0)
+        Ws = build_weights(wl, sorted({0} | {int(e) for e in np.nonzero(counts)[0]}), copies, "cuda")
+        L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
+                           expert_begin=wl.expert_begin)
+        x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).cuda()
+        for i in range(n):
+            L.forward(x, idd, wtd, Ws[i % copies])
+        torch.cuda.synchronize()
+        log(f"[trace-steps] {wl.name} T={T}: {n} forwards")
+        del Ws, L
+
+
 def _counter_medians(path: str, counter: str) -> dict:
     """Median per-dispatch value of `counter` for each kernel name in a rocprofv3 counter CSV."""
     import csv
@@ -468,6 +490,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="prefill only, no CPU baseline")
     ap.add_argument("--traffic-pass", choices=("prefill", "decode"),
                     help="launch sequence for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (no timing)")
+    ap.add_argument("--trace-steps", type=int, default=0, metavar="N",
+                    help="launch sequence for a rocprofv3 kernel trace: N forwards per workload (no timing)")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="CSV",
                     help="prefill FETCH_SIZE, prefill WRITE_SIZE, decode FETCH_SIZE, decode WRITE_SIZE counter CSVs")
     args = ap.parse_args()
@@ -487,6 +511,9 @@ def main():
     torch.cuda.set_device(0)
     if args.traffic_pass:
         traffic_pass(args.traffic_pass)
+        return
+    if args.trace_steps:
+        trace_steps(args.trace_steps)
         return
 
     pre_wl = synth.WORKLOADS[3]
