@@ -152,6 +152,27 @@ int32_t moe_route_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * moe_route_quantize - moe_route_permute and nvfp4_quantize_act of x in one call.
+ *
+ * The first two steps of the layer (route/permute, then quantize x: CURRENT_BUG.md@2e65594,
+ * "Test Plan" Phase 1) do not depend on each other.  At decode sizes (T*k <= 1024 and
+ * T*H <= 65536) they run as one launch, routing in one workgroup beside the quantization;
+ * otherwise as the two calls would.  Results are those of the two calls, bit for bit.
+ *
+ * Routing arguments as in moe_route_permute (route_workspace = its workspace).  x_bf16 bf16
+ * [T, H] with H > 0 a multiple of 32; x_codes [T, H/2], x_scales [T, H/16], x_global_scale [1];
+ * quant_workspace >= megamoe_quant_workspace_bytes(T, H) bytes.  Checks are those of both
+ * functions, all made before any launch.
+ * ---------------------------------------------------------------------------------------- */
+int32_t moe_route_quantize(const int32_t* topk_ids, int32_t T, int32_t k, int32_t expert_begin,
+                           int32_t num_experts, int32_t pad_multiple, int32_t block_m_override,
+                           int32_t* counts, int32_t* expert_offsets, int32_t* padded_offsets,
+                           int32_t* row_token, int32_t* token_rows, int32_t* sched,
+                           void* route_workspace, size_t route_workspace_bytes, const void* x_bf16,
+                           int64_t H, uint8_t* x_codes, uint8_t* x_scales, float* x_global_scale,
+                           void* quant_workspace, size_t quant_workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * nvfp4_quantize_act - NVFP4 quantization with a global scale derived from amax.
  *
  * The FP4 quantizer multiplies the input by a global scale before forming E4M3 block scales

@@ -158,6 +158,40 @@ int32_t moe_route_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t
                                     static_cast<int32_t*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
+int32_t moe_route_quantize(const int32_t* topk_ids, int32_t T, int32_t k, int32_t expert_begin, int32_t num_experts,
+                           int32_t pad_multiple, int32_t block_m_override, int32_t* counts, int32_t* expert_offsets,
+                           int32_t* padded_offsets, int32_t* row_token, int32_t* token_rows, int32_t* sched,
+                           void* route_workspace, size_t route_workspace_bytes, const void* x_bf16, int64_t H,
+                           uint8_t* x_codes, uint8_t* x_scales, float* x_global_scale, void* quant_workspace,
+                           size_t quant_workspace_bytes, void* stream) {
+  const int32_t rc = route_args_ok(T, k, expert_begin, num_experts, pad_multiple, block_m_override, topk_ids, counts,
+                                   expert_offsets, padded_offsets, row_token, token_rows, sched, route_workspace,
+                                   route_workspace_bytes);
+  if (rc != MEGAMOE_OK) return rc;
+  if (H <= 0 || H % 32 != 0 || (int64_t)T > ((int64_t)1 << 40) / H) return MEGAMOE_ERR_SHAPE;
+  if (!x_global_scale) return MEGAMOE_ERR_NULL;
+  if (T > 0 && (!x_bf16 || !x_codes || !x_scales)) return MEGAMOE_ERR_NULL;
+  const size_t qneed = megamoe_quant_workspace_bytes(T, H);
+  if (quant_workspace_bytes < qneed) return MEGAMOE_ERR_WORKSPACE;
+  if (qneed > 0 && !quant_workspace) return MEGAMOE_ERR_NULL;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t M_cap = megamoe_row_capacity(T, k, num_experts, pad_multiple);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  if (route_quant_fusable(T, k, H))
+    return launch_status(launch_route_quant_small(topk_ids, T, k, expert_begin, num_experts, pad_multiple,
+                                                  block_m_override, counts, expert_offsets, padded_offsets, row_token,
+                                                  M_cap, token_rows, sched, x, H, x_codes, x_scales, x_global_scale,
+                                                  s));
+  const int32_t r = launch_status(launch_route(topk_ids, T, k, expert_begin, num_experts, pad_multiple,
+                                               block_m_override, counts, expert_offsets, padded_offsets, row_token,
+                                               M_cap, token_rows, sched, static_cast<int32_t*>(route_workspace), s));
+  if (r != MEGAMOE_OK) return r;
+  return launch_status(launch_quant(x, T, H, nullptr, nullptr, 0, x_codes, x_scales, x_global_scale,
+                                    static_cast<float*>(quant_workspace), s));
+}
+
 int32_t nvfp4_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, const int32_t* row_valid,
                            const float* amax_in, int32_t amax_in_count, uint8_t* codes, uint8_t* scales,
                            float* global_scale, void* workspace, size_t workspace_bytes, void* stream) {

@@ -41,6 +41,14 @@ hipError_t launch_route(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e
 hipError_t launch_router(const float* logits, int32_t T, int32_t Eg, int32_t k, int32_t* ids, float* weights,
                          hipStream_t stream);
 
+// Routing and the quantization of x in one launch (decode sizes: T*k <= 1024, T*H <= 2^16).
+bool route_quant_fusable(int32_t T, int32_t k, int64_t H);
+hipError_t launch_route_quant_small(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e0, int32_t E, int32_t P,
+                                    int32_t block_m_override, int32_t* counts, int32_t* eoff, int32_t* poff,
+                                    int32_t* row_token, int64_t M_cap, int32_t* token_rows, int32_t* sched,
+                                    const uint16_t* x, int64_t H, uint8_t* codes, uint8_t* scales, float* gs,
+                                    hipStream_t stream);
+
 // ---- quantizer -------------------------------------------------------------------------------
 int quant_amax_parts(int64_t rows, int64_t cols);
 hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* row_valid,

@@ -22,6 +22,7 @@
 // elements (decode activations) take a single launch (quant_small_kernel).
 #include "device_common.h"
 #include "internal.h"
+#include "quant_device.h"
 
 namespace megamoe {
 
@@ -34,17 +35,6 @@ int quant_amax_parts(int64_t rows, int64_t cols) {
   if (b < 1) b = 1;
   if (b > kQuantMaxParts) b = kQuantMaxParts;
   return (int)b;
-}
-
-__device__ __forceinline__ uint32_t bf16_abs_max8(u32x4 v) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = v[j] & 0x7FFFu, hi = (v[j] >> 16) & 0x7FFFu;
-    m = m > lo ? m : lo;
-    m = m > hi ? m : hi;
-  }
-  return m;
 }
 
 // Block-level max of a non-negative uint (256 threads).
@@ -75,75 +65,6 @@ __global__ __launch_bounds__(kQuantThreads) void quant_amax_kernel(const uint16_
   if (threadIdx.x == 0) parts[blockIdx.x] = bf16_bits_to_f32(m);
 }
 
-// E4M3FN code of the non-negative double q, round to nearest even, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_code_rne(double q) {
-  if (q >= 464.0) return 0x7Eu;
-  if (q < 0.015625) return (uint32_t)rint(q * 512.0);  // subnormal grid m * 2^-9 (m = 8 is 2^-6)
-  int ex;
-  (void)frexp(q, &ex);  // q in [2^(ex-1), 2^ex)
-  const int E = ex - 1;
-  double mant = rint(ldexp(q, 3 - E));  // in [8, 16]
-  int Eq = E;
-  if (mant >= 16.0) {
-    mant = 8.0;
-    Eq += 1;
-  }
-  const uint32_t code = ((uint32_t)(Eq + 7) << 3) | ((uint32_t)mant - 8u);
-  return code > 0x7Eu ? 0x7Eu : code;
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = c >> 3, m = c & 7u;
-  return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
-}
-
-// 4-bit code of one element: sign of x, magnitude = nearest E2M1 index with ties to even.  The
-// magnitude is the number of midpoints t[i] = m_i * s that x * gs passes (">=" where the tie goes
-// up to the even code: 0.75, 1.75, 3.5; ">" elsewhere).  The thresholds increase, so passing one
-// implies passing every lower one, and a binary search over them (3 tests instead of 7) gives the
-// same count; each test is the sign of one exactly-rounded fma residual.
-__device__ __forceinline__ uint32_t e2m1_code(uint32_t xbits, float gs, const float t[7], bool zero_scale) {
-  const float a = bf16_bits_to_f32(xbits & 0x7FFFu);
-  uint32_t mag = 0;
-  if (!zero_scale) {
-    const bool b2 = fmaf(a, gs, -t[3]) >= 0.0f;                     // >= 1.75 s: magnitude >= 4
-    const bool b1 = fmaf(a, gs, -(b2 ? t[5] : t[1])) >= 0.0f;       // >= 3.5 s or >= 0.75 s
-    const float t0 = b2 ? (b1 ? t[6] : t[4]) : (b1 ? t[2] : t[0]);  // 5, 2.5, 1.25 or 0.25 s
-    const bool b0 = fmaf(a, gs, -t0) > 0.0f;
-    mag = (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
-  }
-  return ((xbits >> 12) & 8u) | mag;
-}
-
-// Quantize one 16-element block b of the tensor (row-major blocks) with global scale gs.
-__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int64_t b, float gs,
-                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const u32x4 v0 = *reinterpret_cast<const u32x4*>(x + b * 16);
-  const u32x4 v1 = *reinterpret_cast<const u32x4*>(x + b * 16 + 8);
-  uint32_t bmax = bf16_abs_max8(v0);
-  const uint32_t bm1 = bf16_abs_max8(v1);
-  bmax = bmax > bm1 ? bmax : bm1;
-  const double q = ((double)bf16_bits_to_f32(bmax) * (double)gs) / 6.0;
-  const uint32_t sc = e4m3_code_rne(q);
-  const float s = e4m3_value(sc);
-  const float t[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
-  const bool zs = sc == 0;
-  uint32_t out[2] = {0u, 0u};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t w = j < 4 ? v0[j] : v1[j - 4];
-    const uint32_t c0 = e2m1_code(w & 0xFFFFu, gs, t, zs);
-    const uint32_t c1 = e2m1_code(w >> 16, gs, t, zs);
-    out[j >> 2] |= (c0 | (c1 << 4)) << (8 * (j & 3));
-  }
-  *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{out[0], out[1]};
-  scales[b] = (uint8_t)sc;
-}
-
-__device__ __forceinline__ float global_scale_of(float amax) {
-  return amax > 0.0f ? 2688.0f / amax : 1.0f;  // IEEE division (correctly rounded)
-}
-
 __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                               const int32_t* __restrict__ row_valid,
                                                               const float* __restrict__ amax_src, int nparts,
@@ -171,14 +92,6 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint16_t* __
   }
 }
 
-// Small tensors (decode activations, up to 2^16 elements): one launch of ceil(blocks / 1024)
-// workgroups of 1024 threads.  Every workgroup reduces the amax of the whole tensor itself (at most
-// 8 loads of 16 bytes per thread, all in flight, from L2 after the first workgroup), so no
-// workgroup waits for another; then each thread quantizes one 16-element block.
-constexpr int kQuantSmallThreads = 1024;
-constexpr int kQuantSmallLoads = 8;
-constexpr int64_t kQuantSmallElems = (int64_t)kQuantSmallThreads * kQuantSmallLoads * 8;
-
 __global__ __launch_bounds__(kQuantSmallThreads) void quant_small_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                                          int64_t cols,
                                                                          const int32_t* __restrict__ row_valid,
@@ -186,37 +99,7 @@ __global__ __launch_bounds__(kQuantSmallThreads) void quant_small_kernel(const u
                                                                          uint8_t* __restrict__ scales,
                                                                          float* __restrict__ gs_out) {
   __shared__ uint32_t red[kQuantSmallThreads / kWave];
-  const int nvec = (int)(rows * cols / 8);
-  u32x4 d[kQuantSmallLoads];
-#pragma unroll
-  for (int j = 0; j < kQuantSmallLoads; ++j) {
-    const int v = (int)threadIdx.x + j * kQuantSmallThreads;
-    d[j] = u32x4{0u, 0u, 0u, 0u};
-    if (v < nvec && (row_valid == nullptr || row_valid[((int64_t)v * 8) / cols] >= 0))
-      d[j] = *reinterpret_cast<const u32x4*>(x + (int64_t)v * 8);
-  }
-  uint32_t m = 0;
-#pragma unroll
-  for (int j = 0; j < kQuantSmallLoads; ++j) {
-    const uint32_t t = bf16_abs_max8(d[j]);
-    m = m > t ? m : t;
-  }
-  m = wave_max_u32(m);
-  if (lane_id() == 0) red[threadIdx.x / kWave] = m;
-  __syncthreads();
-  m = red[0];
-  for (int j = 1; j < kQuantSmallThreads / kWave; ++j) m = m > red[j] ? m : red[j];
-  const float gs = global_scale_of(bf16_bits_to_f32(m));
-  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
-  const int64_t bpr = cols / 16;
-  const int64_t b = (int64_t)blockIdx.x * kQuantSmallThreads + threadIdx.x;
-  if (b >= rows * bpr) return;
-  if (row_valid != nullptr && row_valid[b / bpr] < 0) {
-    *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{0u, 0u};
-    scales[b] = 0;
-    return;
-  }
-  quant_block(x, b, gs, codes, scales);
+  quant_small_body(x, rows, cols, row_valid, codes, scales, gs_out, (int)blockIdx.x, red);
 }
 
 // Calibrated variant: the global scale comes from the caller (e.g. from a warm-up pass), so there

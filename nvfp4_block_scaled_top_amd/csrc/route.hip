@@ -17,6 +17,7 @@
 //               waves, so rows inside an expert follow ascending (token, slot) order.
 #include "device_common.h"
 #include "internal.h"
+#include "quant_device.h"
 
 namespace megamoe {
 
@@ -177,18 +178,18 @@ __global__ __launch_bounds__(kRouteChunk) void route_scatter_kernel(const int32_
   }
 }
 
+
 // Whole routing step in one workgroup when T*k <= kRouteChunk (decode): count, scan and scatter
 // with barriers in between instead of three launches.
-__global__ __launch_bounds__(kRouteChunk) void route_small_kernel(const int32_t* __restrict__ ids, int32_t n, int32_t k,
-                                                                  int32_t e0, int32_t E, int32_t P, int32_t bm_override,
-                                                                  int32_t* __restrict__ counts, int32_t* __restrict__ eoff,
-                                                                  int32_t* __restrict__ poff, int32_t* __restrict__ row_token,
-                                                                  int64_t M_cap, int32_t* __restrict__ token_rows,
-                                                                  int32_t* __restrict__ sched) {
+// The whole routing of up to 1024 assignments by one 1024-thread workgroup.  LDS: wcnt
+// [kWaves][E], wtot [kWaves], s_poff [E].
+__device__ __forceinline__ void route_small_body(const int32_t* __restrict__ ids, int32_t n, int32_t k, int32_t e0,
+                                                 int32_t E, int32_t P, int32_t bm_override,
+                                                 int32_t* __restrict__ counts, int32_t* __restrict__ eoff,
+                                                 int32_t* __restrict__ poff, int32_t* __restrict__ row_token,
+                                                 int64_t M_cap, int32_t* __restrict__ token_rows,
+                                                 int32_t* __restrict__ sched, int32_t* wcnt, Scan4* wtot, int* s_poff) {
   constexpr int kWaves = kRouteChunk / kWave;
-  extern __shared__ int32_t wcnt[];  // [kWaves][E]
-  __shared__ Scan4 wtot[kRouteChunk / kWave];
-  __shared__ int s_poff[kMaxExperts];
   for (int j = threadIdx.x; j < kWaves * E; j += blockDim.x) wcnt[j] = 0;
   for (int64_t r = threadIdx.x; r < M_cap; r += blockDim.x) row_token[r] = -1;
   __syncthreads();
@@ -218,6 +219,57 @@ __global__ __launch_bounds__(kRouteChunk) void route_small_kernel(const int32_t*
     }
     token_rows[i] = row;
   }
+}
+
+__global__ __launch_bounds__(kRouteChunk) void route_small_kernel(const int32_t* __restrict__ ids, int32_t n, int32_t k,
+                                                                  int32_t e0, int32_t E, int32_t P, int32_t bm_override,
+                                                                  int32_t* __restrict__ counts, int32_t* __restrict__ eoff,
+                                                                  int32_t* __restrict__ poff, int32_t* __restrict__ row_token,
+                                                                  int64_t M_cap, int32_t* __restrict__ token_rows,
+                                                                  int32_t* __restrict__ sched) {
+  extern __shared__ int32_t wcnt[];  // [kWaves][E]
+  __shared__ Scan4 wtot[kRouteChunk / kWave];
+  __shared__ int s_poff[kMaxExperts];
+  route_small_body(ids, n, k, e0, E, P, bm_override, counts, eoff, poff, row_token, M_cap, token_rows, sched, wcnt,
+                   wtot, s_poff);
+}
+
+// Decode: routing (workgroup 0) and the quantization of x (workgroups 1..) in one launch; they
+// are independent, so one kernel replaces two launches and the two run side by side.
+static_assert(kQuantSmallThreads == kRouteChunk, "both parts use 1024-thread workgroups");
+__global__ __launch_bounds__(kRouteChunk) void route_quant_small_kernel(
+    const int32_t* __restrict__ ids, int32_t n, int32_t k, int32_t e0, int32_t E, int32_t P, int32_t bm_override,
+    int32_t* __restrict__ counts, int32_t* __restrict__ eoff, int32_t* __restrict__ poff,
+    int32_t* __restrict__ row_token, int64_t M_cap, int32_t* __restrict__ token_rows, int32_t* __restrict__ sched,
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ gs_out) {
+  extern __shared__ int32_t wcnt[];  // [kWaves][E]
+  __shared__ Scan4 wtot[kRouteChunk / kWave];
+  __shared__ int s_poff[kMaxExperts];
+  __shared__ uint32_t red[kQuantSmallThreads / kWave];
+  if (blockIdx.x == 0)
+    route_small_body(ids, n, k, e0, E, P, bm_override, counts, eoff, poff, row_token, M_cap, token_rows, sched, wcnt,
+                     wtot, s_poff);
+  else
+    quant_small_body(x, rows, cols, nullptr, codes, scales, gs_out, (int)blockIdx.x - 1, red);
+}
+
+bool route_quant_fusable(int32_t T, int32_t k, int64_t H) {
+  return (int64_t)T * k <= kRouteChunk && (int64_t)T * H <= kQuantSmallElems;
+}
+
+hipError_t launch_route_quant_small(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e0, int32_t E, int32_t P,
+                                    int32_t block_m_override, int32_t* counts, int32_t* eoff, int32_t* poff,
+                                    int32_t* row_token, int64_t M_cap, int32_t* token_rows, int32_t* sched,
+                                    const uint16_t* x, int64_t H, uint8_t* codes, uint8_t* scales, float* gs,
+                                    hipStream_t stream) {
+  const size_t wcnt_bytes = (size_t)(kRouteChunk / kWave) * E * sizeof(int32_t);
+  const int64_t nblk = (int64_t)T * (H / 16);
+  const int qgrid = (int)((nblk + kQuantSmallThreads - 1) / kQuantSmallThreads);
+  hipLaunchKernelGGL(route_quant_small_kernel, dim3(1 + (qgrid > 0 ? qgrid : 1)), dim3(kRouteChunk), wcnt_bytes, stream,
+                     topk_ids, T * k, k, e0, E, P, block_m_override, counts, eoff, poff, row_token, M_cap, token_rows,
+                     sched, x, (int64_t)T, H, codes, scales, gs);
+  return hipGetLastError();
 }
 
 hipError_t launch_route(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e0, int32_t E, int32_t P,

@@ -145,6 +145,14 @@ class MoELayer:
                             self.padded_offsets, self.row_token, self.token_rows, self.sched, self.route_ws,
                             block_m_override=self.block_m_override, stream=stream)
 
+    def route_quantize(self, topk_ids: torch.Tensor, x_bf16: torch.Tensor, stream=None) -> None:
+        """Route/permute and quantize x in one call (one launch at decode sizes)."""
+        self._gs_x = self.x_gs
+        mm.moe_route_quantize(topk_ids, self.expert_begin, self.E, self.P, self.counts, self.expert_offsets,
+                              self.padded_offsets, self.row_token, self.token_rows, self.sched, self.route_ws,
+                              x_bf16, self._rows(self.x_codes, self.T), self._rows(self.x_scales, self.T), self.x_gs,
+                              self.x_ws, block_m_override=self.block_m_override, stream=stream)
+
     def quantize_x(self, x_bf16: torch.Tensor, stream=None, gs: Optional[torch.Tensor] = None) -> None:
         """gs given (float32 [1] on the device): the calibrated quantizer with that global scale."""
         self._gs_x = self.x_gs if gs is None else gs
@@ -194,8 +202,11 @@ class MoELayer:
         x_gs / h_gs (float32 [1] on the device): calibrated global scales for x and h (e.g. the
         x_gs / h_gs buffers of a warm-up forward) instead of ones derived from this call's amax.
         shared: a shared expert (E = 1) whose output is added in the combine."""
-        self.route(topk_ids, stream)
-        self.quantize_x(x_bf16, stream, gs=x_gs)
+        if x_gs is None:
+            self.route_quantize(topk_ids, x_bf16, stream)
+        else:
+            self.route(topk_ids, stream)
+            self.quantize_x(x_bf16, stream, gs=x_gs)
         self.l1(w, stream)
         self.quantize_h(stream, gs=h_gs)
         self.l2(w, stream)

@@ -38,6 +38,8 @@ SIGNATURES = {
     "moe_router_topk": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P]),
     "moe_route_logits": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _SZ, _P]),
+    "moe_route_quantize": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _I64,
+                                  _P, _P, _P, _P, _SZ, _P]),
     "moe_route_permute": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_quantize_act_gs": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -144,6 +146,18 @@ def moe_route_permute(topk_ids, expert_begin, num_experts, pad_multiple, counts,
         _ptr(topk_ids), T, k, expert_begin, num_experts, pad_multiple, block_m_override, _ptr(counts),
         _ptr(expert_offsets), _ptr(padded_offsets), _ptr(row_token), _ptr(token_rows), _ptr(sched),
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_route_quantize(topk_ids, expert_begin, num_experts, pad_multiple, counts, expert_offsets, padded_offsets,
+                       row_token, token_rows, sched, route_workspace, x_bf16, x_codes, x_scales, x_global_scale,
+                       quant_workspace, block_m_override=0, stream=None):
+    T, k = topk_ids.shape
+    H = x_bf16.shape[1]
+    _check("moe_route_quantize", lib().moe_route_quantize(
+        _ptr(topk_ids), T, k, expert_begin, num_experts, pad_multiple, block_m_override, _ptr(counts),
+        _ptr(expert_offsets), _ptr(padded_offsets), _ptr(row_token), _ptr(token_rows), _ptr(sched),
+        _ptr(route_workspace), _nbytes(route_workspace), _ptr(x_bf16), H, _ptr(x_codes), _ptr(x_scales),
+        _ptr(x_global_scale), _ptr(quant_workspace), _nbytes(quant_workspace), _stream(stream)))
 
 
 def nvfp4_quantize_act(x_bf16, codes, scales, global_scale, workspace=None, row_valid=None, amax_in=None,

@@ -93,6 +93,18 @@ def test_router_rejects_bad_args(lib):
     assert g(None, 4, 384, 6, 0, 48, 1, 0, FAKE, FAKE, *ok, FAKE, 4096, None) == -1         # logits NULL
     assert g(FAKE, 4, 384, 6, 0, 48, 1, 0, FAKE, FAKE, *ok, FAKE, 4, None) == -3            # workspace too small
 
+    h = lib.moe_route_quantize
+    r = [FAKE] * 6 + [FAKE, 1 << 20]
+    assert h(FAKE, 4, 0, 0, 48, 1, 0, *r, FAKE, 7168, FAKE, FAKE, FAKE, FAKE, 4096, None) == -2    # k < 1
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, FAKE, 48, FAKE, FAKE, FAKE, FAKE, 4096, None) == -2      # H % 32
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 4096, None) == -2       # H 0
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, None, 7168, FAKE, FAKE, FAKE, FAKE, 4096, None) == -1    # x NULL
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, FAKE, 7168, FAKE, FAKE, None, FAKE, 4096, None) == -1    # scale NULL
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *[FAKE] * 6, FAKE, 4, FAKE, 7168, FAKE, FAKE, FAKE, FAKE, 4096,
+             None) == -3                                                                         # route ws
+    assert h(FAKE, 100000, 6, 0, 48, 1, 0, *r, FAKE, 7168, FAKE, FAKE, FAKE, FAKE, 64, None) == -3  # quant ws
+    assert h(FAKE, 100000, 6, 0, 48, 1, 0, *r, FAKE, 7168, FAKE, FAKE, FAKE, None, 4096, None) == -1
+
 
 def test_quant_rejects_bad_args(lib):
     f = lib.nvfp4_quantize_act

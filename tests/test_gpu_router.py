@@ -105,3 +105,32 @@ def test_forward_logits_equals_forward_from_ids(i, T):
     out_b = Lb.forward(x, La.topk_ids[:T].clone(), La.topk_weights[:T].clone(), s.gpu_w)
     torch.cuda.synchronize()
     assert np.array_equal(np_i32(out_a.view(torch.int16)), np_i32(out_b.view(torch.int16)))
+
+
+@pytest.mark.parametrize("T,E,H,k", [(1, 48, 7168, 6), (8, 48, 7168, 6), (16, 8, 256, 2), (170, 384, 256, 6),
+                                     (171, 384, 256, 6), (300, 384, 7168, 6), (0, 48, 7168, 6)])
+def test_route_quantize_equals_separate_calls(T, E, H, k):
+    """moe_route_quantize (one launch at decode sizes, two calls above them) gives the bits of
+    moe_route_permute and nvfp4_quantize_act; T=170/171 straddle the one-launch limit."""
+    rng = np.random.default_rng(T + H)
+    ids = np.array([rng.permutation(384)[:k] for _ in range(T)], np.int32).reshape(T, k)
+    x = O.bf16_round(rng.standard_normal((T, H)) * 0.09)
+    from gpu_util import np2bf16_t
+    xd, idd = np2bf16_t(x), torch.from_numpy(ids).to(DEV)
+    La = layer.MoELayer(T, k, E, H, 128, 1, device=DEV)
+    Lb = layer.MoELayer(T, k, E, H, 128, 1, device=DEV)
+    for t in (La.row_token, La.token_rows, La.x_codes, Lb.row_token, Lb.token_rows, Lb.x_codes):
+        t.fill_(0x55)
+    La.route_quantize(idd, xd)
+    Lb.route(idd)
+    Lb.quantize_x(xd)
+    torch.cuda.synchronize()
+    for name in ("counts", "expert_offsets", "padded_offsets", "sched", "x_gs"):
+        assert np.array_equal(getattr(La, name).cpu().numpy(), getattr(Lb, name).cpu().numpy()), name
+    assert np.array_equal(np_i32(La.row_token[:La.M_cap]), np_i32(Lb.row_token[:Lb.M_cap]))
+    assert np.array_equal(np_i32(La.token_rows[:T * k]), np_i32(Lb.token_rows[:T * k]))
+    assert np.array_equal(np_i32(La.x_codes[:T]), np_i32(Lb.x_codes[:T]))
+    assert np.array_equal(np_i32(La.x_scales[:T]), np_i32(Lb.x_scales[:T]))
+    if T:
+        ref_c, ref_s, ref_g = O.quantize_nvfp4(x)
+        assert np.array_equal(np_i32(La.x_codes[:T]), ref_c) and La.x_gs.item() == float(ref_g)
