@@ -160,17 +160,22 @@ int32_t moe_route_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t
  * otherwise as the two calls would.  Results are those of the two calls, bit for bit.
  *
  * Routing arguments as in moe_route_permute (route_workspace = its workspace).  x_bf16 bf16
- * [T, H] with H > 0 a multiple of 32; x_codes [T, H/2], x_scales [T, H/16], x_global_scale [1];
- * quant_workspace >= megamoe_quant_workspace_bytes(T, H) bytes.  Checks are those of both
- * functions, all made before any launch.
+ * [T, H] with H > 0 a multiple of 32; x_codes [T, H/2], x_scales [T, H/16].
+ * x_gs_in      NULL: the global scale comes from the amax of x, as in nvfp4_quantize_act, and is
+ *              written to x_global_scale [1]; quant_workspace >= megamoe_quant_workspace_bytes(T,
+ *              H) bytes.  Non-NULL (float [1] on the device): a calibrated scale, as in
+ *              nvfp4_quantize_act_gs; x_global_scale and quant_workspace are then not used and
+ *              may be NULL.
+ * Checks are those of both functions, all made before any launch.
  * ---------------------------------------------------------------------------------------- */
 int32_t moe_route_quantize(const int32_t* topk_ids, int32_t T, int32_t k, int32_t expert_begin,
                            int32_t num_experts, int32_t pad_multiple, int32_t block_m_override,
                            int32_t* counts, int32_t* expert_offsets, int32_t* padded_offsets,
                            int32_t* row_token, int32_t* token_rows, int32_t* sched,
                            void* route_workspace, size_t route_workspace_bytes, const void* x_bf16,
-                           int64_t H, uint8_t* x_codes, uint8_t* x_scales, float* x_global_scale,
-                           void* quant_workspace, size_t quant_workspace_bytes, void* stream);
+                           int64_t H, const float* x_gs_in, uint8_t* x_codes, uint8_t* x_scales,
+                           float* x_global_scale, void* quant_workspace, size_t quant_workspace_bytes,
+                           void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * nvfp4_quantize_act - NVFP4 quantization with a global scale derived from amax.
@@ -255,6 +260,34 @@ int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales
                                  int32_t E, int32_t H, int32_t I, int64_t M_cap,
                                  int32_t block_m_override, int32_t max_rows_per_expert,
                                  void* h_bf16, float* h_amax_parts, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_grouped_gemm_l1_silu_nvfp4 - moe_grouped_gemm_l1_silu with h written as NVFP4 under a
+ * calibrated global scale, in the GEMM's epilogue.
+ *
+ * The L1 of the layer followed by the requantization of h (CURRENT_BUG.md@2e65594, "Test Plan"
+ * Phase 1: L1 gate+up, SiLU, requantize, L2) when the global scale of h is known beforehand
+ * (CURRENT_BUG.md@2fc81cc, "Root Cause": the checkpoint carries per-layer input scales): each
+ * 16-column block of a row of h is quantized as soon as the tile that holds it is done, so h
+ * never goes through memory in bf16 and no separate quantization launch runs.  For every row
+ * holding an assignment, h_codes and h_scales equal bit for bit those nvfp4_quantize_act_gs
+ * writes for the bf16 h of moe_grouped_gemm_l1_silu with the same h_gs; other rows are not
+ * written.  h_amax_parts is written as by moe_grouped_gemm_l1_silu (max |h| of the bf16 h), so
+ * a caller can watch the calibration.
+ *
+ * Arguments as for moe_grouped_gemm_l1_silu, with h_bf16 replaced by
+ * h_gs         float [1] on the device: the global scale of h (e.g. from a warm-up pass).
+ * h_codes      uint8 [M_cap, I/2];   h_scales  uint8 [M_cap, I/16].
+ * ---------------------------------------------------------------------------------------- */
+int32_t moe_grouped_gemm_l1_silu_nvfp4(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                       const int32_t* row_token, const int32_t* padded_offsets,
+                                       const int32_t* counts, const int32_t* sched,
+                                       const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                       const float* w13_gs, int32_t E, int32_t H, int32_t I,
+                                       int64_t M_cap, int32_t block_m_override,
+                                       int32_t max_rows_per_expert, const float* h_gs,
+                                       uint8_t* h_codes, uint8_t* h_scales, float* h_amax_parts,
+                                       void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * moe_grouped_gemm_l2 - L2 down grouped GEMM over experts.

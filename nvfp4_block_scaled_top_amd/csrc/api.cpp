@@ -162,16 +162,16 @@ int32_t moe_route_quantize(const int32_t* topk_ids, int32_t T, int32_t k, int32_
                            int32_t pad_multiple, int32_t block_m_override, int32_t* counts, int32_t* expert_offsets,
                            int32_t* padded_offsets, int32_t* row_token, int32_t* token_rows, int32_t* sched,
                            void* route_workspace, size_t route_workspace_bytes, const void* x_bf16, int64_t H,
-                           uint8_t* x_codes, uint8_t* x_scales, float* x_global_scale, void* quant_workspace,
-                           size_t quant_workspace_bytes, void* stream) {
+                           const float* x_gs_in, uint8_t* x_codes, uint8_t* x_scales, float* x_global_scale,
+                           void* quant_workspace, size_t quant_workspace_bytes, void* stream) {
   const int32_t rc = route_args_ok(T, k, expert_begin, num_experts, pad_multiple, block_m_override, topk_ids, counts,
                                    expert_offsets, padded_offsets, row_token, token_rows, sched, route_workspace,
                                    route_workspace_bytes);
   if (rc != MEGAMOE_OK) return rc;
   if (H <= 0 || H % 32 != 0 || (int64_t)T > ((int64_t)1 << 40) / H) return MEGAMOE_ERR_SHAPE;
-  if (!x_global_scale) return MEGAMOE_ERR_NULL;
+  if (!x_gs_in && !x_global_scale) return MEGAMOE_ERR_NULL;
   if (T > 0 && (!x_bf16 || !x_codes || !x_scales)) return MEGAMOE_ERR_NULL;
-  const size_t qneed = megamoe_quant_workspace_bytes(T, H);
+  const size_t qneed = x_gs_in ? 0 : megamoe_quant_workspace_bytes(T, H);
   if (quant_workspace_bytes < qneed) return MEGAMOE_ERR_WORKSPACE;
   if (qneed > 0 && !quant_workspace) return MEGAMOE_ERR_NULL;
   const int32_t dev = check_device();
@@ -183,11 +183,12 @@ int32_t moe_route_quantize(const int32_t* topk_ids, int32_t T, int32_t k, int32_
     return launch_status(launch_route_quant_small(topk_ids, T, k, expert_begin, num_experts, pad_multiple,
                                                   block_m_override, counts, expert_offsets, padded_offsets, row_token,
                                                   M_cap, token_rows, sched, x, H, x_codes, x_scales, x_global_scale,
-                                                  s));
+                                                  x_gs_in, s));
   const int32_t r = launch_status(launch_route(topk_ids, T, k, expert_begin, num_experts, pad_multiple,
                                                block_m_override, counts, expert_offsets, padded_offsets, row_token,
                                                M_cap, token_rows, sched, static_cast<int32_t*>(route_workspace), s));
   if (r != MEGAMOE_OK) return r;
+  if (x_gs_in) return launch_status(launch_quant_gs(x, T, H, nullptr, x_gs_in, x_codes, x_scales, s));
   return launch_status(launch_quant(x, T, H, nullptr, nullptr, 0, x_codes, x_scales, x_global_scale,
                                     static_cast<float*>(quant_workspace), s));
 }
@@ -235,6 +236,28 @@ int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales
   if (dev != MEGAMOE_OK) return dev;
   GemmArgs a{x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
              E, H, I, h_bf16, h_amax_parts, 0};
+  return launch_status(launch_gemm_l1(a, cls, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_grouped_gemm_l1_silu_nvfp4(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                       const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
+                                       const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                       const float* w13_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap,
+                                       int32_t block_m_override, int32_t max_rows_per_expert, const float* h_gs,
+                                       uint8_t* h_codes, uint8_t* h_scales, float* h_amax_parts, void* stream) {
+  GemmClasses cls;
+  if (!gemm_shape_ok(E, H, I, M_cap) || !classes_of(block_m_override, max_rows_per_expert, &cls))
+    return MEGAMOE_ERR_SHAPE;
+  if (!x_codes || !x_scales || !x_gs || !row_token || !padded_offsets || !counts || !sched || !w13_codes ||
+      !w13_scales || !w13_gs || !h_gs || !h_codes || !h_scales || !h_amax_parts)
+    return MEGAMOE_ERR_NULL;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  GemmArgs a{x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
+             E, H, I, nullptr, h_amax_parts, 0};
+  a.q_gs = h_gs;
+  a.q_codes = h_codes;
+  a.q_scales = h_scales;
   return launch_status(launch_gemm_l1(a, cls, static_cast<hipStream_t>(stream)));
 }
 

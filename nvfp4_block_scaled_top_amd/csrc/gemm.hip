@@ -28,6 +28,7 @@
 // same permutation, so each dot product is unchanged; it lets a lane read contiguous bytes.
 #include "device_common.h"
 #include "internal.h"
+#include "quant_device.h"
 
 namespace megamoe {
 
@@ -113,7 +114,9 @@ __device__ __forceinline__ float silu_f32(float g) {
 //    phase) gather each lane's A row and decode it per MFMA step, shared by the group's blocks;
 //  * at the end of a group each wave leaves its partial blocks in LDS (double-buffered by group
 //    parity) and, after one LDS-only barrier (the weight loads stay in flight), wave w adds the
-//    partials of accumulator row w of every block in wave order (deterministic) and stores them.
+//    partials of accumulator row w of every block in wave order (deterministic) and stores them
+//    (L1 with a given global scale for h: each row's 16 h columns of a block pair are gathered
+//    into one lane and stored as one NVFP4 block).
 // Lanes whose row lies outside the group or m-tile load a valid row of the same tile instead; the
 // MFMA outputs they feed are never stored.
 // ============================================================================================
@@ -240,6 +243,7 @@ struct BoolTag {
 // group's barrier) means the copy has landed.
 template <bool kL1, int CH, bool kStaged>
 __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArgs p) {
+  static_assert(!kStaged || CH == 256, "staged scales copy whole 16-byte pieces: one per 256-element chunk");
   constexpr int kSNb = small_nb<kL1>();
   constexpr int kQ = CH / 128;
   constexpr int kLaneBytes = CH / 8, kLaneScales = CH / 64;
@@ -259,6 +263,8 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
   int* s_tiny = reinterpret_cast<int*>(s_inv + E);    // experts whose one m-tile is tiny
   uint8_t* s_scl = s_dyn + small_table_bytes(E);      // [3][scale buffer] if kStaged
   const float gs_a = *p.a_gs;
+  const bool quant_out = kL1 && p.q_codes != nullptr;  // L1: NVFP4 h instead of bf16 h
+  const float gs_q = quant_out ? *p.q_gs : 1.0f;
   {
     const int32_t* __restrict__ pref = p.sched + sched_pref_small(E);
     for (int j = threadIdx.x; j < E; j += blockDim.x) {
@@ -372,6 +378,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
       const float* red = reinterpret_cast<const float*>(&s_red[parity][0][0][0]);
       uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
       const int row = 4 * g + wave;  // MFMA output row of accumulator element `wave`
+      uint32_t hq[kSNb];             // L1: bf16 h of column 8j + r16 (lanes r16 < 8)
 #pragma unroll
       for (int j = 0; j < kSNb; ++j) {
         float r = red[((0 * kSNb + j) * kWave + lane) * 4 + wave];
@@ -379,10 +386,10 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
         if (kL1) {
           const float up_raw = __shfl(r, lane + 8, kWave);  // column c+8 holds the up row of c
           const int hc = 8 * j + r16;
+          const uint32_t hb = f32_to_bf16_bits(silu_f32(r * inv) * (up_raw * inv));
+          hq[j] = hb;
           if (r16 < 8 && hc < cg.n && row < cg.rows_left) {
-            const float gt = r * inv, up = up_raw * inv;
-            const uint32_t hb = f32_to_bf16_bits(silu_f32(gt) * up);
-            out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + hc] = (uint16_t)hb;
+            if (!quant_out) out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + hc] = (uint16_t)hb;
             const uint32_t mag = hb & 0x7FFFu;
             amax_bits = amax_bits > mag ? amax_bits : mag;
           }
@@ -390,6 +397,31 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
           const int rc = 16 * j + r16;
           if (rc < cg.n && row < cg.rows_left)
             out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + rc] = (uint16_t)f32_to_bf16_bits(r * inv);
+        }
+      }
+      if (kL1 && quant_out) {
+        // NVFP4 h: the 16 columns 16b.. of row `row` are blocks j = 2b, 2b+1 in lanes 16g + 0..7;
+        // lane 16g gathers them and quantizes the block (groups hold whole blocks: I % 16 == 0).
+#pragma unroll
+        for (int b = 0; b < kSNb / 2; ++b) {
+          const uint32_t pair = (hq[2 * b] & 0xFFFFu) | (hq[2 * b + 1] << 16);
+          uint32_t w[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i] = __shfl(pair, (lane & ~15) + i, kWave);
+          if (r16 == 0 && row < cg.rows_left) {
+            u32x4 v0, v1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              v0[q] = (w[2 * q] & 0xFFFFu) | (w[2 * q + 1] << 16);
+              v1[q] = (w[2 * q] >> 16) | (w[2 * q + 1] & 0xFFFF0000u);
+            }
+            uint32_t c[2];
+            const uint32_t sc = quant16(v0, v1, gs_q, c);
+            const int64_t orow = cg.row0 + row;
+            const int col = cg.j0 + 16 * b;
+            *reinterpret_cast<u32x2*>(p.q_codes + orow * (p.N / 2) + col / 2) = u32x2{c[0], c[1]};
+            p.q_scales[orow * (p.N / 16) + col / 16] = (uint8_t)sc;
+          }
         }
       }
       parity ^= 1;
@@ -699,7 +731,8 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
 // L1: tile weight rows 0..BN/2-1 are gate rows nt*BN/2.., the next BN/2 the matching up rows, so a
 // wave holds gate and up of the same 64 h columns and applies SiLU(gate)*up in registers.
 // L2: tile weight rows are output rows nt*BN..+BN.
-// The epilogue stages the bf16 tile in LDS and writes it with 16-byte row-contiguous stores.
+// The epilogue stages the bf16 tile in LDS and writes it with 16-byte row-contiguous stores, or
+// (L1 with a given global scale for h) quantizes each 16-column block of a staged row to NVFP4.
 // ============================================================================================
 constexpr int kLWaves = 8, kLThreads = kLWaves * kWave;
 constexpr int kLKs = 128;                                        // stage depth (K elements)
@@ -951,7 +984,24 @@ __device__ __forceinline__ void large_tile(const GemmArgs& p, uint8_t* smem, int
     }
   }
   __syncthreads();
-  {
+  if (kL1 && p.q_codes != nullptr) {
+    // NVFP4 h: one thread per 16-column block of a staged row (quantized with the given scale)
+    constexpr int cols = BN / 2, nb = cols / 16;
+    const int nrows = rows_left < BM ? rows_left : BM;
+    const float gs_q = *p.q_gs;
+    const int col0 = nt * cols;
+    for (int idx = tid; idx < nrows * nb; idx += kLThreads) {
+      const int r = idx / nb, c = idx - r * nb;
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(smem + r * pitch + 32 * c);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(smem + r * pitch + 32 * c + 16);
+      uint32_t q[2];
+      const uint32_t sc = quant16(v0, v1, gs_q, q);
+      const int64_t orow = row0 + r;
+      const int col = col0 + 16 * c;
+      *reinterpret_cast<u32x2*>(p.q_codes + orow * (p.N / 2) + col / 2) = u32x2{q[0], q[1]};
+      p.q_scales[orow * (p.N / 16) + col / 16] = (uint8_t)sc;
+    }
+  } else {
     constexpr int cols = kL1 ? BN / 2 : BN;
     constexpr int chunks = cols * 2 / 16;  // 16-byte chunks per row
     const int nrows = rows_left < BM ? rows_left : BM;
@@ -1046,18 +1096,18 @@ static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
     if (err != hipSuccess) return err;
   }
   if (c.small) {
-    // Staged weight scales need every wave on K (K >= 4 chunks) and 3 buffers beside the tables.
+    // Staged weight scales need whole 16-byte scale pieces per chunk (K a multiple of 256: a
+    // staged row of K/16 bytes is K/256 whole pieces), every wave on K (K >= 4 chunks) and 3
+    // buffers beside the tables.
     const int ch = a.K % 256 == 0 ? 256 : 128;
     const size_t tables = small_table_bytes(a.E);
     const size_t bufs = 3 * small_scale_buf_bytes(small_nb<kL1>(), a.K);
-    const bool staged = a.K / ch >= kSWaves && tables + bufs <= kSmallDynMaxLds;
+    const bool staged = ch == 256 && a.K / ch >= kSWaves && tables + bufs <= kSmallDynMaxLds;
     const size_t dyn = tables + (staged ? bufs : 0);
-    if (ch == 256 && staged)
+    if (staged)
       hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
     else if (ch == 256)
       hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, false>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
-    else if (staged)
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 128, true>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
     else
       hipLaunchKernelGGL((gemm_small_kernel<kL1, 128, false>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
     return hipGetLastError();

@@ -47,7 +47,7 @@ hipError_t launch_route_quant_small(const int32_t* topk_ids, int32_t T, int32_t 
                                     int32_t block_m_override, int32_t* counts, int32_t* eoff, int32_t* poff,
                                     int32_t* row_token, int64_t M_cap, int32_t* token_rows, int32_t* sched,
                                     const uint16_t* x, int64_t H, uint8_t* codes, uint8_t* scales, float* gs,
-                                    hipStream_t stream);
+                                    const float* gs_in, hipStream_t stream);
 
 // ---- quantizer -------------------------------------------------------------------------------
 int quant_amax_parts(int64_t rows, int64_t cols);
@@ -76,6 +76,11 @@ struct GemmArgs {
   void* out;         // bf16 [M_cap, N]
   float* amax_out;   // L1: per-workgroup max |h| slots [MEGAMOE_L1_AMAX_PARTS]; NULL for L2
   int clear_other;   // L1: the other tile class is not launched; this kernel zeroes its slots
+  // L1 only, optional: write h as NVFP4 with this global scale (codes [M_cap, N/2], scales
+  // [M_cap, N/16]) instead of bf16 h into `out`.
+  const float* q_gs = nullptr;
+  uint8_t* q_codes = nullptr;
+  uint8_t* q_scales = nullptr;
 };
 // Which tile classes a call may contain, from the routing override and the caller's row bound.
 struct GemmClasses {

@@ -1,6 +1,7 @@
-// Device code of the NVFP4 activation quantizer shared by quant.hip and the fused decode
-// kernel in route.hip: block scale and element code rules (bit-exact with the real-number
-// definition, see quant.hip), one 16-element block, and the single-launch small-tensor form.
+// Device code of the NVFP4 activation quantizer shared by quant.hip, the fused decode kernel in
+// route.hip and the GEMM epilogues that write NVFP4 h (gemm.hip): block scale and element code
+// rules (bit-exact with the real-number definition, see quant.hip), one 16-element block, and the
+// single-launch small-tensor forms.
 #pragma once
 
 #include "device_common.h"
@@ -59,11 +60,10 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t xbits, float gs, const fl
   return ((xbits >> 12) & 8u) | mag;
 }
 
-// Quantize one 16-element block b of the tensor (row-major blocks) with global scale gs.
-__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int64_t b, float gs,
-                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const u32x4 v0 = *reinterpret_cast<const u32x4*>(x + b * 16);
-  const u32x4 v1 = *reinterpret_cast<const u32x4*>(x + b * 16 + 8);
+// Quantize 16 bf16 elements (v0: elements 0-7, v1: 8-15, two per word, the lower element in the
+// low half) with global scale gs: returns the E4M3 scale code; codes[0..1] receive the 8 code
+// bytes (element 2i in the low nibble of byte i).
+__device__ __forceinline__ uint32_t quant16(u32x4 v0, u32x4 v1, float gs, uint32_t (&out)[2]) {
   uint32_t bmax = bf16_abs_max8(v0);
   const uint32_t bm1 = bf16_abs_max8(v1);
   bmax = bmax > bm1 ? bmax : bm1;
@@ -72,7 +72,7 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int6
   const float s = e4m3_value(sc);
   const float t[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
   const bool zs = sc == 0;
-  uint32_t out[2] = {0u, 0u};
+  out[0] = out[1] = 0u;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t w = j < 4 ? v0[j] : v1[j - 4];
@@ -80,6 +80,16 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int6
     const uint32_t c1 = e2m1_code(w >> 16, gs, t, zs);
     out[j >> 2] |= (c0 | (c1 << 4)) << (8 * (j & 3));
   }
+  return sc;
+}
+
+// Quantize one 16-element block b of the tensor (row-major blocks) with global scale gs.
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int64_t b, float gs,
+                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const u32x4 v0 = *reinterpret_cast<const u32x4*>(x + b * 16);
+  const u32x4 v1 = *reinterpret_cast<const u32x4*>(x + b * 16 + 8);
+  uint32_t out[2];
+  const uint32_t sc = quant16(v0, v1, gs, out);
   *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{out[0], out[1]};
   scales[b] = (uint8_t)sc;
 }
@@ -95,6 +105,14 @@ __device__ __forceinline__ float global_scale_of(float amax) {
 constexpr int kQuantSmallThreads = 1024;
 constexpr int kQuantSmallLoads = 8;
 constexpr int64_t kQuantSmallElems = (int64_t)kQuantSmallThreads * kQuantSmallLoads * 8;
+
+// Workgroup `wg` of the single-launch form with a caller-given global scale: one block per thread.
+__device__ __forceinline__ void quant_gs_small_body(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                    float gs, uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales, int wg) {
+  const int64_t b = (int64_t)wg * kQuantSmallThreads + threadIdx.x;
+  if (b < rows * (cols / 16)) quant_block(x, b, gs, codes, scales);
+}
 
 // Workgroup `wg` of the small-tensor quantizer (1024 threads); red: [kQuantSmallThreads / kWave].
 __device__ __forceinline__ void quant_small_body(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,

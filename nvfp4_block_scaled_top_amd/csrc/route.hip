@@ -235,14 +235,15 @@ __global__ __launch_bounds__(kRouteChunk) void route_small_kernel(const int32_t*
 }
 
 // Decode: routing (workgroup 0) and the quantization of x (workgroups 1..) in one launch; they
-// are independent, so one kernel replaces two launches and the two run side by side.
+// are independent, so one kernel replaces two launches and the two run side by side.  gs_in:
+// NULL = global scale from the amax of x (written to gs_out), else the caller's scale.
 static_assert(kQuantSmallThreads == kRouteChunk, "both parts use 1024-thread workgroups");
 __global__ __launch_bounds__(kRouteChunk) void route_quant_small_kernel(
     const int32_t* __restrict__ ids, int32_t n, int32_t k, int32_t e0, int32_t E, int32_t P, int32_t bm_override,
     int32_t* __restrict__ counts, int32_t* __restrict__ eoff, int32_t* __restrict__ poff,
     int32_t* __restrict__ row_token, int64_t M_cap, int32_t* __restrict__ token_rows, int32_t* __restrict__ sched,
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ gs_out) {
+    uint8_t* __restrict__ scales, float* __restrict__ gs_out, const float* __restrict__ gs_in) {
   extern __shared__ int32_t wcnt[];  // [kWaves][E]
   __shared__ Scan4 wtot[kRouteChunk / kWave];
   __shared__ int s_poff[kMaxExperts];
@@ -250,6 +251,8 @@ __global__ __launch_bounds__(kRouteChunk) void route_quant_small_kernel(
   if (blockIdx.x == 0)
     route_small_body(ids, n, k, e0, E, P, bm_override, counts, eoff, poff, row_token, M_cap, token_rows, sched, wcnt,
                      wtot, s_poff);
+  else if (gs_in)
+    quant_gs_small_body(x, rows, cols, *gs_in, codes, scales, (int)blockIdx.x - 1);
   else
     quant_small_body(x, rows, cols, nullptr, codes, scales, gs_out, (int)blockIdx.x - 1, red);
 }
@@ -262,13 +265,13 @@ hipError_t launch_route_quant_small(const int32_t* topk_ids, int32_t T, int32_t 
                                     int32_t block_m_override, int32_t* counts, int32_t* eoff, int32_t* poff,
                                     int32_t* row_token, int64_t M_cap, int32_t* token_rows, int32_t* sched,
                                     const uint16_t* x, int64_t H, uint8_t* codes, uint8_t* scales, float* gs,
-                                    hipStream_t stream) {
+                                    const float* gs_in, hipStream_t stream) {
   const size_t wcnt_bytes = (size_t)(kRouteChunk / kWave) * E * sizeof(int32_t);
   const int64_t nblk = (int64_t)T * (H / 16);
   const int qgrid = (int)((nblk + kQuantSmallThreads - 1) / kQuantSmallThreads);
   hipLaunchKernelGGL(route_quant_small_kernel, dim3(1 + (qgrid > 0 ? qgrid : 1)), dim3(kRouteChunk), wcnt_bytes, stream,
                      topk_ids, T * k, k, e0, E, P, block_m_override, counts, eoff, poff, row_token, M_cap, token_rows,
-                     sched, x, (int64_t)T, H, codes, scales, gs);
+                     sched, x, (int64_t)T, H, codes, scales, gs, gs_in);
   return hipGetLastError();
 }
 

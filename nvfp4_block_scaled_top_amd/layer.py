@@ -145,13 +145,15 @@ class MoELayer:
                             self.padded_offsets, self.row_token, self.token_rows, self.sched, self.route_ws,
                             block_m_override=self.block_m_override, stream=stream)
 
-    def route_quantize(self, topk_ids: torch.Tensor, x_bf16: torch.Tensor, stream=None) -> None:
-        """Route/permute and quantize x in one call (one launch at decode sizes)."""
-        self._gs_x = self.x_gs
+    def route_quantize(self, topk_ids: torch.Tensor, x_bf16: torch.Tensor, stream=None,
+                       gs: Optional[torch.Tensor] = None) -> None:
+        """Route/permute and quantize x in one call (one launch at decode sizes); gs given: the
+        calibrated quantizer with that global scale."""
+        self._gs_x = self.x_gs if gs is None else gs
         mm.moe_route_quantize(topk_ids, self.expert_begin, self.E, self.P, self.counts, self.expert_offsets,
                               self.padded_offsets, self.row_token, self.token_rows, self.sched, self.route_ws,
                               x_bf16, self._rows(self.x_codes, self.T), self._rows(self.x_scales, self.T), self.x_gs,
-                              self.x_ws, block_m_override=self.block_m_override, stream=stream)
+                              self.x_ws, block_m_override=self.block_m_override, stream=stream, x_gs_in=gs)
 
     def quantize_x(self, x_bf16: torch.Tensor, stream=None, gs: Optional[torch.Tensor] = None) -> None:
         """gs given (float32 [1] on the device): the calibrated quantizer with that global scale."""
@@ -168,6 +170,15 @@ class MoELayer:
                                     self.counts, self.sched, w.w13_codes, w.w13_scales, w.w13_gs,
                                     self._rows(self.h, self.M_cap), self.h_amax, self.block_m_override,
                                     self.T, stream=stream)
+
+    def l1_nvfp4(self, w: MoEWeights, gs: torch.Tensor, stream=None) -> None:
+        """L1 writing h as NVFP4 with the calibrated global scale gs (no bf16 h, no quantize_h)."""
+        self._gs_h = gs
+        mm.moe_grouped_gemm_l1_silu_nvfp4(self.x_codes, self.x_scales, self._gs_x, self.row_token,
+                                          self.padded_offsets, self.counts, self.sched, w.w13_codes, w.w13_scales,
+                                          w.w13_gs, gs, self._rows(self.h_codes, self.M_cap),
+                                          self._rows(self.h_scales, self.M_cap), self.h_amax, self.block_m_override,
+                                          self.T, stream=stream)
 
     def quantize_h(self, stream=None, gs: Optional[torch.Tensor] = None) -> None:
         """gs given (float32 [1] on the device): the calibrated quantizer with that global scale."""
@@ -201,14 +212,14 @@ class MoELayer:
         """x_bf16 int16-viewed bf16 [T, H], topk_ids int32 [T, k], topk_weights float32 [T, k].
         x_gs / h_gs (float32 [1] on the device): calibrated global scales for x and h (e.g. the
         x_gs / h_gs buffers of a warm-up forward) instead of ones derived from this call's amax.
-        shared: a shared expert (E = 1) whose output is added in the combine."""
-        if x_gs is None:
-            self.route_quantize(topk_ids, x_bf16, stream)
+        shared: a shared expert (E = 1) whose output is added in the combine.
+        With h_gs, L1 writes h as NVFP4 itself (no bf16 h and no separate quantization of h)."""
+        self.route_quantize(topk_ids, x_bf16, stream, gs=x_gs)
+        if h_gs is None:
+            self.l1(w, stream)
+            self.quantize_h(stream)
         else:
-            self.route(topk_ids, stream)
-            self.quantize_x(x_bf16, stream, gs=x_gs)
-        self.l1(w, stream)
-        self.quantize_h(stream, gs=h_gs)
+            self.l1_nvfp4(w, h_gs, stream)
         self.l2(w, stream)
         if shared is not None:
             self.shared_expert(shared, stream)

@@ -39,7 +39,9 @@ SIGNATURES = {
     "moe_route_logits": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _SZ, _P]),
     "moe_route_quantize": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _I64,
-                                  _P, _P, _P, _P, _SZ, _P]),
+                                  _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_grouped_gemm_l1_silu_nvfp4": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32,
+                                              _I32, _P, _P, _P, _P, _P]),
     "moe_route_permute": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_quantize_act_gs": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -150,14 +152,16 @@ def moe_route_permute(topk_ids, expert_begin, num_experts, pad_multiple, counts,
 
 def moe_route_quantize(topk_ids, expert_begin, num_experts, pad_multiple, counts, expert_offsets, padded_offsets,
                        row_token, token_rows, sched, route_workspace, x_bf16, x_codes, x_scales, x_global_scale,
-                       quant_workspace, block_m_override=0, stream=None):
+                       quant_workspace, block_m_override=0, stream=None, x_gs_in=None):
+    """x_gs_in (float32 [1] on the device): calibrated global scale; x_global_scale and
+    quant_workspace are then not used (may be None)."""
     T, k = topk_ids.shape
     H = x_bf16.shape[1]
     _check("moe_route_quantize", lib().moe_route_quantize(
         _ptr(topk_ids), T, k, expert_begin, num_experts, pad_multiple, block_m_override, _ptr(counts),
         _ptr(expert_offsets), _ptr(padded_offsets), _ptr(row_token), _ptr(token_rows), _ptr(sched),
-        _ptr(route_workspace), _nbytes(route_workspace), _ptr(x_bf16), H, _ptr(x_codes), _ptr(x_scales),
-        _ptr(x_global_scale), _ptr(quant_workspace), _nbytes(quant_workspace), _stream(stream)))
+        _ptr(route_workspace), _nbytes(route_workspace), _ptr(x_bf16), H, _ptr(x_gs_in), _ptr(x_codes),
+        _ptr(x_scales), _ptr(x_global_scale), _ptr(quant_workspace), _nbytes(quant_workspace), _stream(stream)))
 
 
 def nvfp4_quantize_act(x_bf16, codes, scales, global_scale, workspace=None, row_valid=None, amax_in=None,
@@ -186,6 +190,19 @@ def moe_grouped_gemm_l1_silu(x_codes, x_scales, x_gs, row_token, padded_offsets,
         _ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts), _ptr(sched),
         _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), E, 2 * Hh, I2 // 2, M_cap, block_m_override,
         max_rows_per_expert, _ptr(h_bf16), _ptr(h_amax_parts), _stream(stream)))
+
+
+def moe_grouped_gemm_l1_silu_nvfp4(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes,
+                                   w13_scales, w13_gs, h_gs, h_codes, h_scales, h_amax_parts, block_m_override=0,
+                                   max_rows_per_expert=0, stream=None):
+    E, I2, Hh = w13_codes.shape
+    M_cap = h_codes.shape[0]
+    if h_amax_parts.numel() < L1_AMAX_PARTS:
+        raise MegaMoEError(f"h_amax_parts needs {L1_AMAX_PARTS} floats")
+    _check("moe_grouped_gemm_l1_silu_nvfp4", lib().moe_grouped_gemm_l1_silu_nvfp4(
+        _ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts), _ptr(sched),
+        _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), E, 2 * Hh, I2 // 2, M_cap, block_m_override,
+        max_rows_per_expert, _ptr(h_gs), _ptr(h_codes), _ptr(h_scales), _ptr(h_amax_parts), _stream(stream)))
 
 
 def moe_grouped_gemm_l2(h_codes, h_scales, h_gs, padded_offsets, counts, sched, w2_codes, w2_scales, w2_gs, y_bf16,

@@ -95,15 +95,18 @@ def test_router_rejects_bad_args(lib):
 
     h = lib.moe_route_quantize
     r = [FAKE] * 6 + [FAKE, 1 << 20]
-    assert h(FAKE, 4, 0, 0, 48, 1, 0, *r, FAKE, 7168, FAKE, FAKE, FAKE, FAKE, 4096, None) == -2    # k < 1
-    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, FAKE, 48, FAKE, FAKE, FAKE, FAKE, 4096, None) == -2      # H % 32
-    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 4096, None) == -2       # H 0
-    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, None, 7168, FAKE, FAKE, FAKE, FAKE, 4096, None) == -1    # x NULL
-    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, FAKE, 7168, FAKE, FAKE, None, FAKE, 4096, None) == -1    # scale NULL
-    assert h(FAKE, 4, 6, 0, 48, 1, 0, *[FAKE] * 6, FAKE, 4, FAKE, 7168, FAKE, FAKE, FAKE, FAKE, 4096,
+    assert h(FAKE, 4, 0, 0, 48, 1, 0, *r, FAKE, 7168, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == -2    # k < 1
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, FAKE, 48, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == -2      # H % 32
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == -2       # H 0
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, None, 7168, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == -1    # x NULL
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, FAKE, 7168, None, FAKE, FAKE, None, FAKE, 4096, None) == -1    # scale NULL
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *[FAKE] * 6, FAKE, 4, FAKE, 7168, None, FAKE, FAKE, FAKE, FAKE, 4096,
              None) == -3                                                                         # route ws
-    assert h(FAKE, 100000, 6, 0, 48, 1, 0, *r, FAKE, 7168, FAKE, FAKE, FAKE, FAKE, 64, None) == -3  # quant ws
-    assert h(FAKE, 100000, 6, 0, 48, 1, 0, *r, FAKE, 7168, FAKE, FAKE, FAKE, None, 4096, None) == -1
+    # calibrated scale given: x_global_scale and the quantizer workspace are not needed
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, FAKE, 48, FAKE, FAKE, FAKE, None, None, 0, None) == -2  # H % 32
+    assert h(FAKE, 4, 6, 0, 48, 1, 0, *r, None, 7168, FAKE, FAKE, FAKE, None, None, 0, None) == -1  # x NULL
+    assert h(FAKE, 100000, 6, 0, 48, 1, 0, *r, FAKE, 7168, None, FAKE, FAKE, FAKE, FAKE, 64, None) == -3  # quant ws
+    assert h(FAKE, 100000, 6, 0, 48, 1, 0, *r, FAKE, 7168, None, FAKE, FAKE, FAKE, None, 4096, None) == -1
 
 
 def test_quant_rejects_bad_args(lib):
@@ -129,6 +132,11 @@ def test_gemm_rejects_bad_args(lib):
     assert l1(*p10, 8, 256, 128, 64, 0, -1, FAKE, FAKE, None) == -2     # negative row bound
     assert l1(*p10, 8, 256, 128, 64, 0, 0, FAKE, None, None) == -1      # h_amax NULL
     assert l1(None, *p10[1:], 8, 256, 128, 64, 0, 0, FAKE, FAKE, None) == -1
+    q = lib.moe_grouped_gemm_l1_silu_nvfp4
+    assert q(*p10, 8, 384, 128, 64, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == -2   # H not a multiple of 256
+    assert q(*p10, 8, 256, 128, 64, 0, 0, None, FAKE, FAKE, FAKE, None) == -1   # h_gs NULL
+    assert q(*p10, 8, 256, 128, 64, 0, 0, FAKE, None, FAKE, FAKE, None) == -1   # h_codes NULL
+    assert q(*p10, 8, 256, 128, 64, 0, 0, FAKE, FAKE, FAKE, None, None) == -1   # h_amax NULL
     p9 = [FAKE] * 9
     assert l2(*p9, 8, 256, 100, 64, 0, 0, FAKE, None) == -2
     assert l2(*p9, 8, 128, 128, 64, 0, 0, FAKE, None) == -2

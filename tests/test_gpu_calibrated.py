@@ -82,3 +82,70 @@ def test_layer_calibrated(i, T):
     err = rel_frob(out, ref["out"])
     log(f"[calibrated] layer {wl.name} T={T}: rel_frob {err:.2e}")
     assert err <= 1e-2
+
+
+MID = synth.Workload("mid_zipf_e24", 32, 4, 512, 256, (300,), 0, 24, 1, zipf=True)
+
+
+@pytest.mark.parametrize("wl,T", [(synth.WORKLOADS[0], 16), (synth.WORKLOADS[1], 8), (MID, 300),
+                                  (synth.WORKLOADS[2], 512)], ids=["tiny", "decode_t8", "mid", "t512_pad128"])
+def test_l1_nvfp4_equals_l1_then_quantizer(wl, T):
+    """moe_grouped_gemm_l1_silu_nvfp4 (h quantized in the GEMM epilogue) gives, on every row that
+    holds an assignment, the bits nvfp4_quantize_act_gs writes for the bf16 h of the plain L1; the
+    other rows are left alone; the amax slots are those of the plain L1.  Scales: the amax-derived
+    one, and 4x it (saturating blocks)."""
+    s = make_setup(wl, T)
+    x, ids, _ = s.dev_inputs()
+    L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
+                       expert_begin=wl.expert_begin, device=DEV)
+    L.route_quantize(ids, x)
+    L.l1(s.gpu_w)
+    L.quantize_h()
+    torch.cuda.synchronize()
+    M, I = L.M_cap, wl.intermediate
+    valid = np_i32(L.row_token[:M]) >= 0
+    amax_plain = L.h_amax.clone()
+    for factor in (1.0, 4.0):
+        gs = L.h_gs * factor
+        ref_c = torch.empty(M, I // 2, dtype=torch.uint8, device=DEV)
+        ref_s = torch.empty(M, I // 16, dtype=torch.uint8, device=DEV)
+        mm.nvfp4_quantize_act_gs(L.h[:M], gs, ref_c, ref_s, row_valid=L.row_token[:M])
+        codes = torch.full((M, I // 2), 0xAB, dtype=torch.uint8, device=DEV)
+        scales = torch.full((M, I // 16), 0xCD, dtype=torch.uint8, device=DEV)
+        amax = torch.full((mm.L1_AMAX_PARTS,), -1.0, dtype=torch.float32, device=DEV)
+        mm.moe_grouped_gemm_l1_silu_nvfp4(L.x_codes, L.x_scales, L.x_gs, L.row_token, L.padded_offsets, L.counts,
+                                          L.sched, s.gpu_w.w13_codes, s.gpu_w.w13_scales, s.gpu_w.w13_gs, gs, codes,
+                                          scales, amax, max_rows_per_expert=T)
+        torch.cuda.synchronize()
+        c, sc = np_i32(codes), np_i32(scales)
+        assert np.array_equal(c[valid], np_i32(ref_c)[valid]) and np.array_equal(sc[valid], np_i32(ref_s)[valid])
+        assert np.all(c[~valid] == 0xAB) and np.all(sc[~valid] == 0xCD)
+        assert torch.equal(amax, amax_plain)
+        log(f"[calibrated] fused L1 {wl.name} T={T} x{factor}: {int(valid.sum())} rows bit-exact, "
+            f"{int((sc[valid] == 0x7E).sum())} saturated blocks")
+
+
+@pytest.mark.parametrize("T,H", [(8, 7168), (1, 7168), (300, 2048)])
+def test_route_quantize_with_scale(T, H):
+    """moe_route_quantize with a calibrated scale (one launch at decode sizes, two calls above)
+    equals moe_route_permute + nvfp4_quantize_act_gs, bit for bit, and leaves x_global_scale alone."""
+    rng = np.random.default_rng(T + 3)
+    k, E = 6, 48
+    ids = np.array([rng.permutation(384)[:k] for _ in range(T)], np.int32)
+    x = O.bf16_round(rng.standard_normal((T, H)) * 0.09)
+    xd, idd = np2bf16_t(x), torch.from_numpy(ids).to(DEV)
+    gs = torch.tensor([float(O.global_scale(float(np.abs(x).max())) * 2.0)], dtype=torch.float32, device=DEV)
+    La = layer.MoELayer(T, k, E, H, 128, 1, device=DEV)
+    Lb = layer.MoELayer(T, k, E, H, 128, 1, device=DEV)
+    La.x_gs.fill_(-5.0)
+    La.route_quantize(idd, xd, gs=gs)
+    Lb.route(idd)
+    Lb.quantize_x(xd, gs=gs)
+    torch.cuda.synchronize()
+    assert La.x_gs.item() == -5.0
+    for name in ("counts", "expert_offsets", "padded_offsets", "sched"):
+        assert torch.equal(getattr(La, name), getattr(Lb, name)), name
+    assert torch.equal(La.row_token[:La.M_cap], Lb.row_token[:Lb.M_cap])
+    assert torch.equal(La.x_codes[:T], Lb.x_codes[:T]) and torch.equal(La.x_scales[:T], Lb.x_scales[:T])
+    ref_c, ref_s = O.quantize_rows_with_global_scale(x, np.float32(gs.item()))
+    assert np.array_equal(np_i32(La.x_codes[:T]), ref_c) and np.array_equal(np_i32(La.x_scales[:T]), ref_s)

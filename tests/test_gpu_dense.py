@@ -27,7 +27,8 @@ def quantized(rng, rows, K, std):
 
 
 @pytest.mark.parametrize("M,K,N", [(0, 2048, 256), (1, 2048, 7168), (5, 128, 256), (16, 7168, 2048),
-                                   (17, 2048, 7168), (300, 7168, 2048), (1000, 256, 512)])
+                                   (17, 2048, 7168), (300, 7168, 2048), (1000, 256, 512), (8, 640, 512),
+                                   (3, 1152, 256), (12, 1024, 768)])
 def test_linear(M, K, N):
     rng = np.random.default_rng(M + K + N)
     ac, as_, ag = quantized(rng, M, K, 0.09)
@@ -46,7 +47,7 @@ def test_linear(M, K, N):
 
 
 @pytest.mark.parametrize("M,K,I", [(1, 7168, 2048), (7, 256, 128), (16, 2048, 256), (40, 7168, 2048),
-                                   (513, 2048, 1024)])
+                                   (513, 2048, 1024), (3, 1024, 640)])
 def test_gate_up_silu(M, K, I):
     rng = np.random.default_rng(M * 7 + K + I)
     ac, as_, ag = quantized(rng, M, K, 0.09)

@@ -25,6 +25,9 @@ MID_PAD = synth.Workload("mid_zipf_e16_pad128", 32, 4, 512, 256, (150,), 8, 16, 
 # K of at least 4 chunks of 256 in both GEMMs (hidden 2048, intermediate 1024): the 16-row tile
 # kernels take the path with weight scales staged in LDS; Zipf routing leaves both tile classes.
 MID_K = synth.Workload("mid_k_e12", 24, 4, 2048, 1024, (160,), 4, 12, 1, zipf=True)
+# L2 reduction length 640 = five 128-element chunks (the 16-row kernel's 128-chunk path with its
+# weight scales read from HBM; staged scales cover whole 256-element chunks only).
+ODD_K = synth.Workload("odd_k640_e16", 128, 6, 1024, 640, (8,), 0, 16, 1)
 TINY = synth.WORKLOADS[0]
 DECODE = synth.WORKLOADS[1]
 
@@ -63,8 +66,8 @@ def check_tables(L, ref):
     assert sched[1] == small.sum() and sched[2] == large.sum()
 
 
-@pytest.mark.parametrize("wl,T", [(TINY, 16), (MID, 300), (MID_PAD, 150), (MID_K, 160)],
-                         ids=["tiny", "mid", "mid_pad128", "mid_k2048"])
+@pytest.mark.parametrize("wl,T", [(TINY, 16), (MID, 300), (MID_PAD, 150), (MID_K, 160), (ODD_K, 8)],
+                         ids=["tiny", "mid", "mid_pad128", "mid_k2048", "odd_k640"])
 def test_layer_end_to_end_and_stages(wl, T):
     s = setup_for(wl, T)
     log(f"[run] {wl.name} T={T}: GPU layer")
