@@ -395,7 +395,9 @@ def traffic_pass(which: str) -> None:
 
 def trace_steps(n: int) -> None:
     """Launch sequence for a rocprofv3 kernel trace: for the prefill (T=8192) and decode (T=1, 4, 8)
-    workloads in turn, quantize the weights, then run n eager layer forwards (no timing)."""
+    workloads in turn, quantize the weights, run n eager layer forwards, quantize expert 0 once
+    more (a separator in the trace), then n forwards with calibrated scales (those of the first
+    forwards).  No timing."""
     import torch
     from nvfp4_block_scaled_top_amd import layer, synth
 
@@ -411,7 +413,12 @@ def trace_steps(n: int) -> None:
         for i in range(n):
             L.forward(x, idd, wtd, Ws[i % copies])
         torch.cuda.synchronize()
-        log(f"[trace-steps] {wl.name} T={T}: {n} forwards")
+        gx, gh = L.x_gs.clone(), L.h_gs.clone()
+        build_weights(wl, [0], 1, "cuda")
+        for i in range(n):
+            L.forward(x, idd, wtd, Ws[i % copies], x_gs=gx, h_gs=gh)
+        torch.cuda.synchronize()
+        log(f"[trace-steps] {wl.name} T={T}: {n} forwards, {n} calibrated")
         del Ws, L
 
 

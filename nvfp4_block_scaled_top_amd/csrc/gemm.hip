@@ -132,6 +132,9 @@ __device__ __forceinline__ float silu_f32(float g) {
 #ifndef MEGAMOE_SMALL_OCC
 #define MEGAMOE_SMALL_OCC 2
 #endif
+#ifndef MEGAMOE_SMALL_STAGED
+#define MEGAMOE_SMALL_STAGED 1
+#endif
 template <bool kL1>
 constexpr int small_nb() { return kL1 ? MEGAMOE_SMALL_NB_L1 : MEGAMOE_SMALL_NB_L2; }  // blocks per group
 constexpr int kSDepth = MEGAMOE_SMALL_DEPTH;  // ring slots (chunks in flight per wave)
@@ -142,7 +145,7 @@ constexpr int kSmallGrid = 256 * kSOcc;       // small class: resident workgroup
 constexpr int kAmaxSmallSlots = MEGAMOE_L1_AMAX_PARTS - kLargeGrid;  // slots [kLargeGrid, PARTS)
 // Dynamic LDS of the small class: the per-expert tables, then 3 staged scale buffers if kStaged.
 // With kSOcc = 2 a workgroup may use 80 KB; the static arrays take about 21 KB of it.
-constexpr size_t kSmallDynMaxLds = 58 * 1024;
+constexpr size_t kSmallDynMaxLds = 160 * 1024 / kSOcc - 22 * 1024;
 static_assert(kSmallGrid <= kAmaxSmallSlots, "one amax slot per small workgroup");
 static_assert(kSmallGrid % kXcds == 0 && (kSmallGrid / kXcds) % kSOcc == 0, "grid split");
 
@@ -241,7 +244,7 @@ struct BoolTag {
 // least), so 3 buffers suffice; every wave has issued at least kSDepth steps of loads after its
 // copy of group q+1 when group q ends, so vmcnt <= kSDepth * (loads per step) there (before the
 // group's barrier) means the copy has landed.
-template <bool kL1, int CH, bool kStaged>
+template <bool kL1, int CH, bool kStaged, bool kQOut>
 __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArgs p) {
   static_assert(!kStaged || CH == 256, "staged scales copy whole 16-byte pieces: one per 256-element chunk");
   constexpr int kSNb = small_nb<kL1>();
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
   int* s_tiny = reinterpret_cast<int*>(s_inv + E);    // experts whose one m-tile is tiny
   uint8_t* s_scl = s_dyn + small_table_bytes(E);      // [3][scale buffer] if kStaged
   const float gs_a = *p.a_gs;
-  const bool quant_out = kL1 && p.q_codes != nullptr;  // L1: NVFP4 h instead of bf16 h
+  constexpr bool quant_out = kL1 && kQOut;  // L1: NVFP4 h (q_codes, q_scales) instead of bf16 h
   const float gs_q = quant_out ? *p.q_gs : 1.0f;
   {
     const int32_t* __restrict__ pref = p.sched + sched_pref_small(E);
@@ -399,27 +402,35 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
             out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + rc] = (uint16_t)f32_to_bf16_bits(r * inv);
         }
       }
-      if (kL1 && quant_out) {
-        // NVFP4 h: the 16 columns 16b.. of row `row` are blocks j = 2b, 2b+1 in lanes 16g + 0..7;
-        // lane 16g gathers them and quantizes the block (groups hold whole blocks: I % 16 == 0).
+      if constexpr (quant_out) {
+        // NVFP4 h: the 16 columns 16b.. of row `row` are blocks j = 2b, 2b+1, element e in lane
+        // 16g + e % 8, register 2b + e / 8 (groups hold whole blocks: I % 16 == 0).  The 8 lanes
+        // reduce the block's amax, each derives the block scale and codes its own 2 elements
+        // (the quantizer's block_scale / e2m1_code), and lane 16g assembles and stores the block.
 #pragma unroll
         for (int b = 0; b < kSNb / 2; ++b) {
-          const uint32_t pair = (hq[2 * b] & 0xFFFFu) | (hq[2 * b + 1] << 16);
-          uint32_t w[8];
+          const uint32_t e0 = hq[2 * b] & 0xFFFFu, e1 = hq[2 * b + 1] & 0xFFFFu;  // elements r16, 8 + r16
+          uint32_t m = (e0 & 0x7FFFu) > (e1 & 0x7FFFu) ? (e0 & 0x7FFFu) : (e1 & 0x7FFFu);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) w[i] = __shfl(pair, (lane & ~15) + i, kWave);
+          for (int o = 1; o < 8; o <<= 1) {
+            const uint32_t t = __shfl_xor(m, o, kWave);
+            m = m > t ? m : t;
+          }
+          float th[7];
+          const uint32_t sc = block_scale(m, gs_q, th);
+          const uint32_t cc = e2m1_code(e0, gs_q, th, sc == 0) | (e2m1_code(e1, gs_q, th, sc == 0) << 8);
+          // even lane 2i: byte i (elements 2i, 2i+1) in bits 0-7, byte i + 4 in bits 8-15
+          const uint32_t pr = cc | (__shfl_xor(cc, 1, kWave) << 4);
+          const int base = lane & ~15;
+          const uint32_t p1 = __shfl(pr, base + 2, kWave), p2 = __shfl(pr, base + 4, kWave),
+                         p3 = __shfl(pr, base + 6, kWave);
           if (r16 == 0 && row < cg.rows_left) {
-            u32x4 v0, v1;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v0[q] = (w[2 * q] & 0xFFFFu) | (w[2 * q + 1] << 16);
-              v1[q] = (w[2 * q] >> 16) | (w[2 * q + 1] & 0xFFFF0000u);
-            }
-            uint32_t c[2];
-            const uint32_t sc = quant16(v0, v1, gs_q, c);
+            const uint32_t lo = (pr & 0xFFu) | ((p1 & 0xFFu) << 8) | ((p2 & 0xFFu) << 16) | ((p3 & 0xFFu) << 24);
+            const uint32_t hi = ((pr >> 8) & 0xFFu) | (((p1 >> 8) & 0xFFu) << 8) | (((p2 >> 8) & 0xFFu) << 16) |
+                                (((p3 >> 8) & 0xFFu) << 24);
             const int64_t orow = cg.row0 + row;
             const int col = cg.j0 + 16 * b;
-            *reinterpret_cast<u32x2*>(p.q_codes + orow * (p.N / 2) + col / 2) = u32x2{c[0], c[1]};
+            *reinterpret_cast<u32x2*>(p.q_codes + orow * (p.N / 2) + col / 2) = u32x2{lo, hi};
             p.q_scales[orow * (p.N / 16) + col / 16] = (uint8_t)sc;
           }
         }
@@ -784,7 +795,7 @@ __device__ __forceinline__ void wait_stage(int stages_after) {
 }
 
 // One output tile of shape S: expert e, m-tile rows [row0, row0 + min(rows_left, BM)), n-tile nt.
-template <bool kL1, class S>
+template <bool kL1, bool kQ, class S>
 __device__ __forceinline__ void large_tile(const GemmArgs& p, uint8_t* smem, int e, int row0, int rows_left, int nt,
                                            float gs_a, uint32_t& amax_bits) {
   constexpr int BM = S::kBm, BN = S::kBn;
@@ -984,7 +995,7 @@ __device__ __forceinline__ void large_tile(const GemmArgs& p, uint8_t* smem, int
     }
   }
   __syncthreads();
-  if (kL1 && p.q_codes != nullptr) {
+  if constexpr (kL1 && kQ) {
     // NVFP4 h: one thread per 16-column block of a staged row (quantized with the given scale)
     constexpr int cols = BN / 2, nb = cols / 16;
     const int nrows = rows_left < BM ? rows_left : BM;
@@ -1016,7 +1027,7 @@ __device__ __forceinline__ void large_tile(const GemmArgs& p, uint8_t* smem, int
   __syncthreads();  // staging reads done before the next tile's DMA refills the ring
 }
 
-template <bool kL1>
+template <bool kL1, bool kQ>
 __global__ __launch_bounds__(kLThreads, 1) void gemm_large_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLLdsBytes];
   __shared__ int s_tpref[kMaxExperts + 1];  // exclusive prefix of tiles per expert
@@ -1068,8 +1079,8 @@ __global__ __launch_bounds__(kLThreads, 1) void gemm_large_kernel(GemmArgs p) {
     const int mt = local < nfull ? local / ntn_full : nm - 1;
     const int row0 = p.padded_offsets[e] + kBlockMLarge * mt;
     const int rows_left = p.counts[e] - kBlockMLarge * mt;
-    if (local < nfull) large_tile<kL1, LFull>(p, smem, e, row0, rows_left, local - mt * ntn_full, gs_a, amax_bits);
-    else large_tile<kL1, LTail>(p, smem, e, row0, rows_left, local - nfull, gs_a, amax_bits);
+    if (local < nfull) large_tile<kL1, kQ, LFull>(p, smem, e, row0, rows_left, local - mt * ntn_full, gs_a, amax_bits);
+    else large_tile<kL1, kQ, LTail>(p, smem, e, row0, rows_left, local - nfull, gs_a, amax_bits);
   }
   if (kL1) {
     amax_bits = wave_max_u32(amax_bits);
@@ -1087,11 +1098,13 @@ __global__ __launch_bounds__(kLThreads, 1) void gemm_large_kernel(GemmArgs p) {
 
 // Launch the tile classes the call may contain.  When only one class runs, its kernel also
 // zeroes the other class's amax slots (clear_other), so every slot is written on every call.
-template <bool kL1>
+// kQ: L1 writing NVFP4 h (a.q_codes set); a separate instantiation, so the plain kernels carry
+// none of its code.
+template <bool kL1, bool kQ>
 static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
   a.clear_other = !(c.large && c.small);
   if (c.large) {
-    hipLaunchKernelGGL(gemm_large_kernel<kL1>, dim3(kLargeGrid), dim3(kLThreads), 0, stream, a);
+    hipLaunchKernelGGL((gemm_large_kernel<kL1, kQ>), dim3(kLargeGrid), dim3(kLThreads), 0, stream, a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -1102,21 +1115,25 @@ static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
     const int ch = a.K % 256 == 0 ? 256 : 128;
     const size_t tables = small_table_bytes(a.E);
     const size_t bufs = 3 * small_scale_buf_bytes(small_nb<kL1>(), a.K);
-    const bool staged = ch == 256 && a.K / ch >= kSWaves && tables + bufs <= kSmallDynMaxLds;
+    const bool staged = MEGAMOE_SMALL_STAGED && ch == 256 && a.K / ch >= kSWaves && tables + bufs <= kSmallDynMaxLds;
     const size_t dyn = tables + (staged ? bufs : 0);
     if (staged)
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true, kQ>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
     else if (ch == 256)
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, false>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, false, kQ>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
     else
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 128, false>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 128, false, kQ>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
-hipError_t launch_gemm_l1(const GemmArgs& a, GemmClasses c, hipStream_t stream) { return launch_gemm<true>(a, c, stream); }
+hipError_t launch_gemm_l1(const GemmArgs& a, GemmClasses c, hipStream_t stream) {
+  return a.q_codes ? launch_gemm<true, true>(a, c, stream) : launch_gemm<true, false>(a, c, stream);
+}
 
-hipError_t launch_gemm_l2(const GemmArgs& a, GemmClasses c, hipStream_t stream) { return launch_gemm<false>(a, c, stream); }
+hipError_t launch_gemm_l2(const GemmArgs& a, GemmClasses c, hipStream_t stream) {
+  return launch_gemm<false, false>(a, c, stream);
+}
 
 }  // namespace megamoe

@@ -60,6 +60,22 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t xbits, float gs, const fl
   return ((xbits >> 12) & 8u) | mag;
 }
 
+// Block scale of a 16-element block whose largest magnitude has bf16 bits bmax: returns the E4M3
+// code and fills the element thresholds t (the E2M1 midpoints times the scale value).
+__device__ __forceinline__ uint32_t block_scale(uint32_t bmax, float gs, float (&t)[7]) {
+  const double q = ((double)bf16_bits_to_f32(bmax) * (double)gs) / 6.0;
+  const uint32_t sc = e4m3_code_rne(q);
+  const float s = e4m3_value(sc);
+  t[0] = 0.25f * s;
+  t[1] = 0.75f * s;
+  t[2] = 1.25f * s;
+  t[3] = 1.75f * s;
+  t[4] = 2.5f * s;
+  t[5] = 3.5f * s;
+  t[6] = 5.0f * s;
+  return sc;
+}
+
 // Quantize 16 bf16 elements (v0: elements 0-7, v1: 8-15, two per word, the lower element in the
 // low half) with global scale gs: returns the E4M3 scale code; codes[0..1] receive the 8 code
 // bytes (element 2i in the low nibble of byte i).
@@ -67,10 +83,8 @@ __device__ __forceinline__ uint32_t quant16(u32x4 v0, u32x4 v1, float gs, uint32
   uint32_t bmax = bf16_abs_max8(v0);
   const uint32_t bm1 = bf16_abs_max8(v1);
   bmax = bmax > bm1 ? bmax : bm1;
-  const double q = ((double)bf16_bits_to_f32(bmax) * (double)gs) / 6.0;
-  const uint32_t sc = e4m3_code_rne(q);
-  const float s = e4m3_value(sc);
-  const float t[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
+  float t[7];
+  const uint32_t sc = block_scale(bmax, gs, t);
   const bool zs = sc == 0;
   out[0] = out[1] = 0u;
 #pragma unroll
