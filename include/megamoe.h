@@ -349,6 +349,22 @@ int32_t nvfp4_linear_gate_up_silu(const uint8_t* a_codes, const uint8_t* a_scale
                                   size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * nvfp4_linear_gate_up_silu_nvfp4 - nvfp4_linear_gate_up_silu with h written as NVFP4 under a
+ * calibrated global scale, in the GEMM's epilogue (as moe_grouped_gemm_l1_silu_nvfp4 for the
+ * single group: CURRENT_BUG.md@2e65594, "Test Plan" Phase 1; CURRENT_BUG.md@2fc81cc, "Root
+ * Cause").  h_codes/h_scales equal bit for bit those nvfp4_quantize_act_gs writes for the bf16 h
+ * of nvfp4_linear_gate_up_silu with the same h_gs, on every row.
+ * h_gs         float [1] on the device.   h_codes uint8 [M, I/2];   h_scales uint8 [M, I/16].
+ * Other arguments, workspace and limits as for nvfp4_linear_gate_up_silu.
+ * ---------------------------------------------------------------------------------------- */
+int32_t nvfp4_linear_gate_up_silu_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                        int64_t M, int32_t K, const uint8_t* w13_codes,
+                                        const uint8_t* w13_scales, const float* w13_gs, int32_t I,
+                                        const float* h_gs, uint8_t* h_codes, uint8_t* h_scales,
+                                        float* h_amax_parts, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * moe_combine - routing-weighted combine of the expert outputs back into token order.
  *
  * The routing weight of each (token, expert) is applied exactly once, here:

@@ -345,4 +345,28 @@ int32_t nvfp4_linear_gate_up_silu(const uint8_t* a_codes, const uint8_t* a_scale
   return launch_status(launch_gemm_l1(ga, cls, s));
 }
 
+int32_t nvfp4_linear_gate_up_silu_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                        int64_t M, int32_t K, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                        const float* w13_gs, int32_t I, const float* h_gs, uint8_t* h_codes,
+                                        uint8_t* h_scales, float* h_amax_parts, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (!gemm_shape_ok(1, K, I, M)) return MEGAMOE_ERR_SHAPE;
+  if (!a_gs || !w13_codes || !w13_scales || !w13_gs || !h_gs || !h_amax_parts || !workspace) return MEGAMOE_ERR_NULL;
+  if (M > 0 && (!a_codes || !a_scales || !h_codes || !h_scales)) return MEGAMOE_ERR_NULL;
+  if (workspace_bytes < megamoe_dense_workspace_bytes(M)) return MEGAMOE_ERR_WORKSPACE;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* ws = static_cast<int32_t*>(workspace);
+  const int32_t r = launch_status(launch_dense_setup((int32_t)M, ws, true, s));
+  if (r != MEGAMOE_OK) return r;
+  const GemmClasses cls{M <= kSmallClassMaxTokens, M > kSmallClassMaxTokens};  // exactly the group's class
+  GemmArgs ga{a_codes, a_scales, a_gs, ws + kDenseHeader, ws + kDensePoff, ws + kDenseCounts, ws + kDenseSched,
+              w13_codes, w13_scales, w13_gs, 1, K, I, nullptr, h_amax_parts, 0};
+  ga.q_gs = h_gs;
+  ga.q_codes = h_codes;
+  ga.q_scales = h_scales;
+  return launch_status(launch_gemm_l1(ga, cls, s));
+}
+
 }  // extern "C"

@@ -117,16 +117,27 @@ class MoELayer:
         self.sh_y = torch.empty(T, H, dtype=torch.int16, device=dev)
         self.sh_ws = torch.empty(mm.megamoe_dense_workspace_bytes(self.T), dtype=torch.uint8, device=dev)
 
-    def shared_expert(self, shared: MoEWeights, stream=None) -> None:
-        """Dense gate+up+SiLU on the x codes, requantize its h (own amax), dense down: sh_y [T, H]."""
+    def shared_expert(self, shared: MoEWeights, stream=None, h_gs: Optional[torch.Tensor] = None) -> None:
+        """Dense gate+up+SiLU on the x codes, requantize its h (own amax), dense down: sh_y [T, H].
+        h_gs given: a calibrated global scale for its h, written as NVFP4 by the gate+up GEMM."""
         self._shared_buffers(shared)
         T = self.T
-        mm.nvfp4_linear_gate_up_silu(self._rows(self.x_codes, T), self._rows(self.x_scales, T), self._gs_x,
-                                     shared.w13_codes[0], shared.w13_scales[0], shared.w13_gs[0:1],
-                                     self._rows(self.sh_h, T), self.sh_h_amax, self.sh_ws, stream=stream)
-        mm.nvfp4_quantize_act(self._rows(self.sh_h, T), self._rows(self.sh_h_codes, T),
-                              self._rows(self.sh_h_scales, T), self.sh_h_gs, amax_in=self.sh_h_amax, stream=stream)
-        mm.nvfp4_linear(self._rows(self.sh_h_codes, T), self._rows(self.sh_h_scales, T), self.sh_h_gs,
+        if h_gs is None:
+            mm.nvfp4_linear_gate_up_silu(self._rows(self.x_codes, T), self._rows(self.x_scales, T), self._gs_x,
+                                         shared.w13_codes[0], shared.w13_scales[0], shared.w13_gs[0:1],
+                                         self._rows(self.sh_h, T), self.sh_h_amax, self.sh_ws, stream=stream)
+            mm.nvfp4_quantize_act(self._rows(self.sh_h, T), self._rows(self.sh_h_codes, T),
+                                  self._rows(self.sh_h_scales, T), self.sh_h_gs, amax_in=self.sh_h_amax,
+                                  stream=stream)
+            gs = self.sh_h_gs
+        else:
+            mm.nvfp4_linear_gate_up_silu_nvfp4(self._rows(self.x_codes, T), self._rows(self.x_scales, T),
+                                               self._gs_x, shared.w13_codes[0], shared.w13_scales[0],
+                                               shared.w13_gs[0:1], h_gs, self._rows(self.sh_h_codes, T),
+                                               self._rows(self.sh_h_scales, T), self.sh_h_amax, self.sh_ws,
+                                               stream=stream)
+            gs = h_gs
+        mm.nvfp4_linear(self._rows(self.sh_h_codes, T), self._rows(self.sh_h_scales, T), gs,
                         shared.w2_codes[0], shared.w2_scales[0], shared.w2_gs[0:1], self._rows(self.sh_y, T),
                         self.sh_ws, stream=stream)
 
@@ -208,11 +219,12 @@ class MoELayer:
 
     def forward(self, x_bf16: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, w: MoEWeights,
                 stream=None, x_gs: Optional[torch.Tensor] = None, h_gs: Optional[torch.Tensor] = None,
-                shared: Optional[MoEWeights] = None) -> torch.Tensor:
+                shared: Optional[MoEWeights] = None, shared_h_gs: Optional[torch.Tensor] = None) -> torch.Tensor:
         """x_bf16 int16-viewed bf16 [T, H], topk_ids int32 [T, k], topk_weights float32 [T, k].
         x_gs / h_gs (float32 [1] on the device): calibrated global scales for x and h (e.g. the
         x_gs / h_gs buffers of a warm-up forward) instead of ones derived from this call's amax.
-        shared: a shared expert (E = 1) whose output is added in the combine.
+        shared: a shared expert (E = 1) whose output is added in the combine; shared_h_gs: a
+        calibrated global scale for the shared expert's h.
         With h_gs, L1 writes h as NVFP4 itself (no bf16 h and no separate quantization of h)."""
         self.route_quantize(topk_ids, x_bf16, stream, gs=x_gs)
         if h_gs is None:
@@ -222,7 +234,7 @@ class MoELayer:
             self.l1_nvfp4(w, h_gs, stream)
         self.l2(w, stream)
         if shared is not None:
-            self.shared_expert(shared, stream)
+            self.shared_expert(shared, stream, h_gs=shared_h_gs)
         self.combine(topk_weights, stream, shared=shared is not None)
         return self._rows(self.out, self.T)
 

@@ -53,6 +53,8 @@ SIGNATURES = {
     "megamoe_dense_workspace_bytes": (_SZ, [_I64]),
     "nvfp4_linear": (_I32, [_P, _P, _P, _I64, _I32, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "nvfp4_linear_gate_up_silu": (_I32, [_P, _P, _P, _I64, _I32, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "nvfp4_linear_gate_up_silu_nvfp4": (_I32, [_P, _P, _P, _I64, _I32, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _SZ,
+                                               _P]),
 }
 
 
@@ -253,3 +255,15 @@ def nvfp4_linear_gate_up_silu(a_codes, a_scales, a_gs, w13_codes, w13_scales, w1
     _check("nvfp4_linear_gate_up_silu", lib().nvfp4_linear_gate_up_silu(
         _ptr(a_codes), _ptr(a_scales), _ptr(a_gs), M, 2 * Kh, _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), I,
         _ptr(h_bf16), _ptr(h_amax_parts), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def nvfp4_linear_gate_up_silu_nvfp4(a_codes, a_scales, a_gs, w13_codes, w13_scales, w13_gs, h_gs, h_codes, h_scales,
+                                    h_amax_parts, workspace, stream=None):
+    M, Kh = a_codes.shape
+    I = w13_codes.shape[0] // 2
+    if h_amax_parts.numel() < L1_AMAX_PARTS:
+        raise MegaMoEError(f"h_amax_parts needs {L1_AMAX_PARTS} floats")
+    _check("nvfp4_linear_gate_up_silu_nvfp4", lib().nvfp4_linear_gate_up_silu_nvfp4(
+        _ptr(a_codes), _ptr(a_scales), _ptr(a_gs), M, 2 * Kh, _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), I,
+        _ptr(h_gs), _ptr(h_codes), _ptr(h_scales), _ptr(h_amax_parts), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))

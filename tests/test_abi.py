@@ -149,3 +149,13 @@ def test_combine_rejects_bad_args(lib):
     assert f(FAKE, FAKE, FAKE, 4, 0, 256, FAKE, None) == -2
     assert f(FAKE, FAKE, FAKE, 4, 6, 12, FAKE, None) == -2
     assert f(None, FAKE, FAKE, 4, 6, 256, FAKE, None) == -1
+
+
+def test_dense_nvfp4_rejects_bad_args(lib):
+    f = lib.nvfp4_linear_gate_up_silu_nvfp4
+    need = mm.megamoe_dense_workspace_bytes(4)
+    assert f(FAKE, FAKE, FAKE, 4, 200, FAKE, FAKE, FAKE, 128, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == -2  # K
+    assert f(FAKE, FAKE, FAKE, 4, 256, FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == -2  # I
+    assert f(FAKE, FAKE, FAKE, 4, 256, FAKE, FAKE, FAKE, 128, None, FAKE, FAKE, FAKE, FAKE, need, None) == -1  # h_gs
+    assert f(FAKE, FAKE, FAKE, 4, 256, FAKE, FAKE, FAKE, 128, FAKE, None, FAKE, FAKE, FAKE, need, None) == -1  # codes
+    assert f(FAKE, FAKE, FAKE, 4, 256, FAKE, FAKE, FAKE, 128, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == -3

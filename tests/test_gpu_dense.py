@@ -125,3 +125,51 @@ def test_layer_with_shared_expert(i, T):
     err_sh = rel_frob(bf16_t2np(L.sh_y[:T]), ref["y_shared"])
     log(f"[dense] layer {wl.name} T={T} with a shared expert: out rel_frob {err:.2e}, shared y {err_sh:.2e}")
     assert err <= 1e-2 and err_sh <= 1e-2
+
+
+@pytest.mark.parametrize("M,K,I", [(1, 7168, 2048), (7, 256, 128), (40, 7168, 2048), (513, 2048, 1024)])
+def test_gate_up_silu_nvfp4_equals_gate_up_then_quantizer(M, K, I):
+    """nvfp4_linear_gate_up_silu_nvfp4 (h quantized in the epilogue with a given scale) equals
+    nvfp4_linear_gate_up_silu followed by nvfp4_quantize_act_gs, bit for bit on every row; the
+    amax slots are those of the plain call."""
+    rng = np.random.default_rng(M * 5 + K + I)
+    ac, as_, ag = quantized(rng, M, K, 0.09)
+    wc, ws, wg = quantized(rng, 2 * I, K, 0.02)
+    wsp = torch.empty(mm.megamoe_dense_workspace_bytes(M), dtype=torch.uint8, device=DEV)
+    h = torch.empty(M, I, dtype=torch.int16, device=DEV)
+    amax = torch.empty(mm.L1_AMAX_PARTS, dtype=torch.float32, device=DEV)
+    mm.nvfp4_linear_gate_up_silu(u8(ac), u8(as_), f32(ag), u8(wc), u8(ws), f32(wg), h, amax, wsp)
+    torch.cuda.synchronize()
+    gs = f32(O.global_scale(float(np.abs(bf16_t2np(h)).max())) * np.float32(2.0))  # some blocks saturate
+    ref_c = torch.empty(M, I // 2, dtype=torch.uint8, device=DEV)
+    ref_s = torch.empty(M, I // 16, dtype=torch.uint8, device=DEV)
+    mm.nvfp4_quantize_act_gs(h, gs, ref_c, ref_s)
+    codes = torch.full((M, I // 2), 0xAB, dtype=torch.uint8, device=DEV)
+    scales = torch.full((M, I // 16), 0xCD, dtype=torch.uint8, device=DEV)
+    amax2 = torch.full((mm.L1_AMAX_PARTS,), -1.0, dtype=torch.float32, device=DEV)
+    mm.nvfp4_linear_gate_up_silu_nvfp4(u8(ac), u8(as_), f32(ag), u8(wc), u8(ws), f32(wg), gs, codes, scales, amax2,
+                                       wsp)
+    torch.cuda.synchronize()
+    assert torch.equal(codes, ref_c) and torch.equal(scales, ref_s) and torch.equal(amax2, amax)
+    log(f"[dense] gate_up_silu_nvfp4 M={M} K={K} I={I}: bit-exact, "
+        f"{int((np_i32(scales) == 0x7E).sum())} saturated blocks")
+
+
+@pytest.mark.parametrize("i,T", [(0, 16), (1, 8)], ids=["tiny", "decode_t8"])
+def test_layer_with_calibrated_shared_expert(i, T):
+    """The layer with a shared expert and calibrated scales everywhere (x, routed h, shared h):
+    the scales the uncalibrated forward derived, passed back in, give the same bits."""
+    wl = synth.WORKLOADS[i]
+    s = make_setup(wl, T)
+    x, ids, wts = s.dev_inputs()
+    sh = layer.MoEWeights.empty(1, wl.hidden, wl.intermediate, device=DEV)
+    w13, w2 = synth.expert_weights(wl, 100000, device=DEV)
+    layer.quantize_expert_into(sh, 0, w13, w2)
+    L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
+                       expert_begin=wl.expert_begin, device=DEV)
+    base = L.forward(x, ids, wts, s.gpu_w, shared=sh).clone()
+    torch.cuda.synchronize()
+    gx, gh, gsh = L.x_gs.clone(), L.h_gs.clone(), L.sh_h_gs.clone()
+    same = L.forward(x, ids, wts, s.gpu_w, shared=sh, x_gs=gx, h_gs=gh, shared_h_gs=gsh).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(same, base)

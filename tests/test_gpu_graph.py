@@ -35,3 +35,33 @@ def test_graph_replays_match_eager(wl, T):
         assert np.array_equal(np_i32(L.out[:T].view(torch.int16)), eager), r
         valid = np_i32(L.row_token[:L.M_cap]) >= 0
         assert np.array_equal(np_i32(L.h[:L.M_cap].view(torch.int16))[valid], eager_h[valid]), r
+
+
+@pytest.mark.parametrize("wl,T", [(MID, 300), (synth.WORKLOADS[1], 8)], ids=["mid", "decode_t8"])
+def test_graph_replays_calibrated(wl, T):
+    """The calibrated forward (x quantized in the routing launch, h written as NVFP4 by L1)
+    captured once: every replay equals the eager result, with h's codes poisoned in between."""
+    s = make_setup(wl, T)
+    x, ids, wts = s.dev_inputs()
+    L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
+                       expert_begin=wl.expert_begin, device=DEV)
+    L.forward(x, ids, wts, s.gpu_w)
+    torch.cuda.synchronize()
+    gx, gh = L.x_gs.clone(), L.h_gs.clone()
+    L.forward(x, ids, wts, s.gpu_w, x_gs=gx, h_gs=gh)
+    torch.cuda.synchronize()
+    eager = np_i32(L.out[:T].view(torch.int16)).copy()
+    valid = np_i32(L.row_token[:L.M_cap]) >= 0
+    eager_hc = np_i32(L.h_codes[:L.M_cap])[valid].copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.forward(x, ids, wts, s.gpu_w, x_gs=gx, h_gs=gh)
+    for r in range(4):
+        L.out.fill_(0x7FC0)
+        L.h_codes.fill_(0xEE)
+        L.x_codes.fill_(0xEE)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np_i32(L.out[:T].view(torch.int16)), eager), r
+        assert np.array_equal(np_i32(L.h_codes[:L.M_cap])[valid], eager_hc), r
