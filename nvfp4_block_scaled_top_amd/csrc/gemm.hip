@@ -802,7 +802,8 @@ __device__ __forceinline__ void large_tile(const GemmArgs& p, uint8_t* smem, int
   const int K = p.K, Kh = K / 2, Ks = K / 16;
   const int Nw = kL1 ? 2 * p.N : p.N;
   const int nks = K / kLKs;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  // wave index as a scalar: the LDS destinations of the DMA (M0) are then computed in SGPRs
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = lane_id();
   const int wm = wave / S::kWN, wn = wave % S::kWN;
   const int p32 = lane & 31, h2 = lane >> 5;
 
