@@ -469,6 +469,63 @@ def summarize_traffic(paths: list) -> None:
     print("\n".join(out))
 
 
+TRACE_WORKLOADS = ("prefill T=8192", "prefill T=8192 (calibrated scales)", "decode T=1",
+                   "decode T=1 (calibrated scales)", "decode T=4", "decode T=4 (calibrated scales)",
+                   "decode T=8", "decode T=8 (calibrated scales)")
+
+
+def summarize_trace(path: str) -> None:
+    """Per-step kernel durations from the kernel-trace CSV of a `--trace-steps N` run.  A layer step
+    runs from a routing kernel to the combine; library quantization kernels outside a step (weight
+    quantization) separate the workloads, in the order of trace_steps().  Prints, per workload, the
+    median over steps of each kernel's duration per step and of their sum."""
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+
+    def short(name):
+        n = name.replace("void ", "").split("(")[0]
+        return n.replace("megamoe::", "")
+
+    segments, steps, cur, in_step = [], [], None, False
+    for t0, t1, name in rows:
+        if "megamoe::" not in name:
+            continue
+        k = short(name)
+        if k.startswith("route_") and not in_step:  # route_*, not the router
+            in_step, cur = True, {}
+        if in_step:
+            cur.setdefault(k, []).append((t1 - t0) / 1000.0)
+            if k.startswith("combine"):
+                steps.append({n: sum(v) for n, v in cur.items()})
+                in_step = False
+        elif k.startswith("quant") and steps:
+            segments.append(steps)
+            steps = []
+    if steps:
+        segments.append(steps)
+
+    def med(v):
+        v = sorted(v)
+        return v[len(v) // 2]
+
+    out = []
+    for label, seg in zip(TRACE_WORKLOADS, segments):
+        names = []
+        for st in seg:
+            names += [n for n in st if n not in names]
+        out.append(f"{label}: {len(seg)} layer steps, median kernel duration per step (us)")
+        for n in names:
+            v = [st.get(n, 0.0) for st in seg]
+            out.append(f"  {n:44s} {med(v):8.2f}   (min {min(v):.2f}, max {max(v):.2f})")
+        tot = [sum(st.values()) for st in seg]
+        out.append(f"  {'(sum of kernels)':44s} {med(tot):8.2f}   (min {min(tot):.2f}, max {max(tot):.2f})")
+    print("\n".join(out))
+
+
 def recorded_traffic(which: str):
     """Bytes per L1 call recorded in TRAFFIC_FILE, or None if absent or taken on other kernel code."""
     try:
@@ -501,7 +558,12 @@ def main():
                     help="launch sequence for a rocprofv3 kernel trace: N forwards per workload (no timing)")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="CSV",
                     help="prefill FETCH_SIZE, prefill WRITE_SIZE, decode FETCH_SIZE, decode WRITE_SIZE counter CSVs")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="kernel-trace CSV of a --trace-steps run: per-workload medians of kernel time per step")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic)
         return
