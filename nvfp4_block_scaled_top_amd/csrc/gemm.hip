@@ -1077,11 +1077,27 @@ __global__ __launch_bounds__(kLThreads, 1) void gemm_large_kernel(GemmArgs p) {
     const int local = t - s_tpref[e];
     const int nm = s_mt[e] >> 1, tail = s_mt[e] & 1;
     const int nfull = (nm - tail) * ntn_full;
-    const int mt = local < nfull ? local / ntn_full : nm - 1;
+    // Full tiles of an expert go in bands of kBand m-tiles, n-tile major within a band: the
+    // consecutive tiles an XCD runs at once share a few m-tiles' A rows and a few n-tiles' weight
+    // rows (instead of one m-tile and all of the expert's weights), so fewer weight bytes are
+    // fetched again for every m-tile.
+    constexpr int kBand = 4;
+    int mt, ntile;
+    if (local < nfull) {
+      const int band = local / (kBand * ntn_full);
+      const int rem = (nm - tail) - band * kBand;
+      const int h = rem < kBand ? rem : kBand;  // m-tiles in this band
+      const int r = local - band * kBand * ntn_full;
+      ntile = r / h;
+      mt = band * kBand + (r - ntile * h);
+    } else {
+      mt = nm - 1;
+      ntile = local - nfull;
+    }
     const int row0 = p.padded_offsets[e] + kBlockMLarge * mt;
     const int rows_left = p.counts[e] - kBlockMLarge * mt;
-    if (local < nfull) large_tile<kL1, kQ, LFull>(p, smem, e, row0, rows_left, local - mt * ntn_full, gs_a, amax_bits);
-    else large_tile<kL1, kQ, LTail>(p, smem, e, row0, rows_left, local - nfull, gs_a, amax_bits);
+    if (local < nfull) large_tile<kL1, kQ, LFull>(p, smem, e, row0, rows_left, ntile, gs_a, amax_bits);
+    else large_tile<kL1, kQ, LTail>(p, smem, e, row0, rows_left, ntile, gs_a, amax_bits);
   }
   if (kL1) {
     amax_bits = wave_max_u32(amax_bits);
