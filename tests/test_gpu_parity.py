@@ -4,8 +4,8 @@ Bars: bit-exact for routing tables, FP4 codes, E4M3 scales and global scales; re
 <= 1e-3 for h (L1) and y (L2) when fed the same quantized inputs; <= 1e-2 with cosine >= 0.9999
 end to end.  Workloads: the tiny workload, three medium workloads that mix both tile classes with
 ragged tails, non-local ids, a zero-token expert and padding to 128 (one with hidden 2048 and
-intermediate 1024, long enough in K for the staged-scale path of the 16-row kernels), and the
-decode workload at its full size (48 local experts of 384, hidden 7168, intermediate 2048,
+intermediate 1024, long enough in K for the staged-scale path of the 16-row kernels), experts
+with up to 8 m-tiles of 256 rows (the large-tile kernels' tile order), and the decode workload at its full size (48 local experts of 384, hidden 7168, intermediate 2048,
 T = 1, 4, 8).
 """
 import numpy as np
@@ -28,6 +28,10 @@ MID_K = synth.Workload("mid_k_e12", 24, 4, 2048, 1024, (160,), 4, 12, 1, zipf=Tr
 # L2 reduction length 640 = five 128-element chunks (the 16-row kernel's 128-chunk path with its
 # weight scales read from HBM; staged scales cover whole 256-element chunks only).
 ODD_K = synth.Workload("odd_k640_e16", 128, 6, 1024, 640, (8,), 0, 16, 1)
+# Experts with many 256-row m-tiles (top-1 over 4 Zipf-biased experts, T=4000) and 4 n-tiles per
+# m-tile in both GEMMs (intermediate 512, hidden 1024): the large-tile kernels' bands of m-tiles,
+# whole and ragged, and tail tiles.
+MANY_MT = synth.Workload("many_mtiles_e4", 4, 1, 1024, 512, (4000,), 0, 4, 1, zipf=True)
 TINY = synth.WORKLOADS[0]
 DECODE = synth.WORKLOADS[1]
 
@@ -66,8 +70,8 @@ def check_tables(L, ref):
     assert sched[1] == small.sum() and sched[2] == large.sum()
 
 
-@pytest.mark.parametrize("wl,T", [(TINY, 16), (MID, 300), (MID_PAD, 150), (MID_K, 160), (ODD_K, 8)],
-                         ids=["tiny", "mid", "mid_pad128", "mid_k2048", "odd_k640"])
+@pytest.mark.parametrize("wl,T", [(TINY, 16), (MID, 300), (MID_PAD, 150), (MID_K, 160), (ODD_K, 8), (MANY_MT, 4000)],
+                         ids=["tiny", "mid", "mid_pad128", "mid_k2048", "odd_k640", "many_mtiles"])
 def test_layer_end_to_end_and_stages(wl, T):
     s = setup_for(wl, T)
     log(f"[run] {wl.name} T={T}: GPU layer")
