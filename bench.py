@@ -526,6 +526,25 @@ def summarize_trace(path: str) -> None:
     print("\n".join(out))
 
 
+def summarize_counters(path: str) -> None:
+    """Median per dispatch of every counter in a rocprofv3 --pmc CSV, for the library's kernels."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            if "megamoe::" not in name:
+                continue
+            vals.setdefault(name.replace("megamoe::", ""), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    for k, cs in vals.items():
+        parts = []
+        for c, v in sorted(cs.items()):
+            v = sorted(v)
+            parts.append(f"{c} {v[len(v) // 2]:.4g}")
+        print(f"{k:44s} dispatches {max(len(v) for v in cs.values()):3d}  " + "  ".join(parts))
+
+
 def recorded_traffic(which: str):
     """Bytes per L1 call recorded in TRAFFIC_FILE, or None if absent or taken on other kernel code."""
     try:
@@ -560,7 +579,12 @@ def main():
                     help="prefill FETCH_SIZE, prefill WRITE_SIZE, decode FETCH_SIZE, decode WRITE_SIZE counter CSVs")
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="kernel-trace CSV of a --trace-steps run: per-workload medians of kernel time per step")
+    ap.add_argument("--summarize-counters", metavar="CSV",
+                    help="rocprofv3 --pmc counter CSV: per-kernel medians of each counter")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
         return
