@@ -85,10 +85,13 @@ def test_layer_calibrated(i, T):
 
 
 MID = synth.Workload("mid_zipf_e24", 32, 4, 512, 256, (300,), 0, 24, 1, zipf=True)
+# experts with up to 10 m-tiles of 256 rows: the large-tile kernel's tile order with NVFP4 h
+MANY_MT = synth.Workload("many_mtiles_e4", 4, 1, 1024, 512, (4000,), 0, 4, 1, zipf=True)
 
 
 @pytest.mark.parametrize("wl,T", [(synth.WORKLOADS[0], 16), (synth.WORKLOADS[1], 8), (MID, 300),
-                                  (synth.WORKLOADS[2], 512)], ids=["tiny", "decode_t8", "mid", "t512_pad128"])
+                                  (synth.WORKLOADS[2], 512), (MANY_MT, 4000)],
+                         ids=["tiny", "decode_t8", "mid", "t512_pad128", "many_mtiles"])
 def test_l1_nvfp4_equals_l1_then_quantizer(wl, T):
     """moe_grouped_gemm_l1_silu_nvfp4 (h quantized in the GEMM epilogue) gives, on every row that
     holds an assignment, the bits nvfp4_quantize_act_gs writes for the bf16 h of the plain L1; the
