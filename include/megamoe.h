@@ -127,7 +127,9 @@ int32_t moe_route_logits(const float* logits, int32_t T, int32_t num_experts_glo
  * variable token counts per expert, padded to 128 in vLLM) and Phase 2 (48-expert EP share of
  * 384, zero-token experts, expert_offsets and padded_expert_offsets).
  *
- * topk_ids        int32 [T, k]  global expert id of each (token, slot).
+ * topk_ids        int32 [T, k]  global expert id of each (token, slot).  A token may list the
+ *                 same expert in several slots; each (token, slot) is then an assignment of its own
+ *                 (its own row), in ascending slot order.
  * expert_begin    first global expert held here; local expert e = id - expert_begin.
  * num_experts     E, local experts (1..MEGAMOE_MAX_EXPERTS).
  * pad_multiple    P >= 1: each expert's row block is padded to a multiple of P (zero stays 0).
@@ -247,10 +249,12 @@ int32_t nvfp4_quantize_act_gs(const void* x_bf16, int64_t rows, int64_t cols, co
  * E, H, I      E as given to moe_route_permute; H a multiple of 256, I a multiple of 128.
  * M_cap        rows of h: megamoe_row_capacity(T, k, E, P).
  * block_m_override  the value given to moe_route_permute (0, 16 or 256).
- * max_rows_per_expert  a bound on counts[e] known to the caller, or 0 if none.  T is always one
- *              (a token picks each expert at most once).  With block_m_override 0 and a bound of
- *              at most 16, every expert uses 16-row tiles and the 256-row tile kernel is not
- *              launched (one launch fewer at decode).  A wrong bound gives wrong results.
+ * max_rows_per_expert  a bound on counts[e] the caller expects, or 0 if none (e.g. T when no
+ *              token lists an expert twice).  It changes which kernels launch, never the results:
+ *              with block_m_override 0 and a bound of at most 16 only the 16-row tile kernel is
+ *              launched (one launch fewer at decode), and it then also computes, in 16-row tiles,
+ *              any expert whose count turns out to exceed the bound.  A bound that is too low
+ *              costs time only.
  * h_bf16       bf16 [M_cap, I].   h_amax_parts float [MEGAMOE_L1_AMAX_PARTS].
  * ---------------------------------------------------------------------------------------- */
 int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
@@ -367,7 +371,11 @@ int32_t nvfp4_linear_gate_up_silu_nvfp4(const uint8_t* a_codes, const uint8_t* a
 /* ------------------------------------------------------------------------------------------
  * moe_combine - routing-weighted combine of the expert outputs back into token order.
  *
- * The routing weight of each (token, expert) is applied exactly once, here:
+ * The last step of the layer: the runner receives topk_weights with the top-k ids
+ * (CURRENT_BUG.md@2e65594, "Test Plan" Phase 1) and the routed experts' outputs are summed back
+ * per token, each weighted by its routing weight, with the tokens that have no local expert in
+ * the 48-of-384 expert-parallel share giving zero ("Test Plan" Phase 2).  The routing weight of
+ * each (token, expert) is applied exactly once, here:
  *   out[t, :] = bf16( sum over j = 0..k-1 ascending, token_rows[t*k+j] >= 0, of
  *                     topk_weights[t, j] * y[token_rows[t*k+j], :] )    (FP32 accumulation)
  * Tokens with no local assignment get +0.

@@ -239,11 +239,15 @@ struct BoolTag {
 // Weight scales staged in LDS (kStaged): a group's rows of weight block scales (row-contiguous in
 // HBM) are copied by full-line direct-to-LDS loads when the loader enters the group, into buffer
 // (group index) % 3, rows padded by 16 bytes so that the 4-byte reads of 16 rows x 4 lanes hit
-// distinct banks.  The steady state then issues no scale loads for the weights.  With a ring of
-// kSDepth steps the loader runs at most 2 groups ahead of the compute (one step per group at
-// least), so 3 buffers suffice; every wave has issued at least kSDepth steps of loads after its
-// copy of group q+1 when group q ends, so vmcnt <= kSDepth * (loads per step) there (before the
-// group's barrier) means the copy has landed.
+// distinct banks.  The steady state then issues no scale loads for the weights.  The loader runs
+// kSDepth = 2 steps ahead of the compute and enters group g right after loading the last chunk of
+// group g-1, i.e. while the compute is at step C*g - 3 for a wave with C chunks per group: in group
+// g-1 or g-2 when C >= 2.  Buffer g % 3 was last read in group g-3, whose barrier every wave has
+// passed by then, so 3 buffers suffice -- only if every wave has at least 2 chunks per group (with
+// C = 1 the copy of group g would land during group g-3's compute); the launch enables staging only
+// then.  Every wave has issued at least kSDepth steps of loads after its copy of group q+1 when
+// group q ends, so vmcnt <= kSDepth * (loads per step) there (before the group's barrier) means the
+// copy has landed.
 template <bool kL1, int CH, bool kStaged, bool kQOut>
 __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArgs p) {
   static_assert(!kStaged || CH == 256, "staged scales copy whole 16-byte pieces: one per 256-element chunk");
@@ -270,11 +274,17 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
   const float gs_q = quant_out ? *p.q_gs : 1.0f;
   {
     const int32_t* __restrict__ pref = p.sched + sched_pref_small(E);
+    const int32_t* __restrict__ bm = p.sched + sched_block_m(E);
     for (int j = threadIdx.x; j < E; j += blockDim.x) {
+      const int cnt = p.counts[j];
       s_poff[j] = p.padded_offsets[j];
-      s_cnt[j] = p.counts[j];
-      s_inv[j] = (float)(1.0 / ((double)gs_a * (double)p.w_gs[j]));
-      s_pref[j] = pref[j + 1] - pref[j];  // small m-tiles of expert j (scanned below)
+      s_cnt[j] = cnt;
+      // small m-tiles of expert j (scanned below); when the 256-row kernel is not launched, an
+      // expert the routing step gave 256-row tiles is covered here in 16-row m-tiles
+      int nt = pref[j + 1] - pref[j];
+      if (p.small_covers_large && bm[j] == kBlockMLarge) nt = (cnt + kBlockMSmall - 1) / kBlockMSmall;
+      s_pref[j] = nt;
+      s_inv[j] = nt > 0 ? (float)(1.0 / ((double)gs_a * (double)p.w_gs[j])) : 0.0f;
     }
     __syncthreads();
     if (threadIdx.x < kWave) {  // wave 0: split the small m-tiles into tiny and regular
@@ -1120,6 +1130,7 @@ __global__ __launch_bounds__(kLThreads, 1) void gemm_large_kernel(GemmArgs p) {
 template <bool kL1, bool kQ>
 static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
   a.clear_other = !(c.large && c.small);
+  a.small_covers_large = c.small && !c.large;  // a row bound that was too low costs time only
   if (c.large) {
     hipLaunchKernelGGL((gemm_large_kernel<kL1, kQ>), dim3(kLargeGrid), dim3(kLThreads), 0, stream, a);
     const hipError_t err = hipGetLastError();
@@ -1127,12 +1138,14 @@ static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
   }
   if (c.small) {
     // Staged weight scales need whole 16-byte scale pieces per chunk (K a multiple of 256: a
-    // staged row of K/16 bytes is K/256 whole pieces), every wave on K (K >= 4 chunks) and 3
+    // staged row of K/16 bytes is K/256 whole pieces), at least 2 chunks of K for every wave (so
+    // the loader never copies into the buffer of a group still being computed, see above) and 3
     // buffers beside the tables.
     const int ch = a.K % 256 == 0 ? 256 : 128;
     const size_t tables = small_table_bytes(a.E);
     const size_t bufs = 3 * small_scale_buf_bytes(small_nb<kL1>(), a.K);
-    const bool staged = MEGAMOE_SMALL_STAGED && ch == 256 && a.K / ch >= kSWaves && tables + bufs <= kSmallDynMaxLds;
+    const bool staged =
+        MEGAMOE_SMALL_STAGED && ch == 256 && a.K / ch >= 2 * kSWaves && tables + bufs <= kSmallDynMaxLds;
     const size_t dyn = tables + (staged ? bufs : 0);
     if (staged)
       hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true, kQ>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);

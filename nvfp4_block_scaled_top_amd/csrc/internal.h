@@ -76,6 +76,9 @@ struct GemmArgs {
   void* out;         // bf16 [M_cap, N]
   float* amax_out;   // L1: per-workgroup max |h| slots [MEGAMOE_L1_AMAX_PARTS]; NULL for L2
   int clear_other;   // L1: the other tile class is not launched; this kernel zeroes its slots
+  // The 256-row kernel is not launched: the 16-row kernel also takes experts the routing step gave
+  // 256-row tiles (in 16-row m-tiles), so a caller's row bound below a real count is still correct.
+  int small_covers_large = 0;
   // L1 only, optional: write h as NVFP4 with this global scale (codes [M_cap, N/2], scales
   // [M_cap, N/16]) instead of bf16 h into `out`.
   const float* q_gs = nullptr;

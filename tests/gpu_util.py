@@ -15,6 +15,7 @@ import torch
 
 from nvfp4_block_scaled_top_amd import layer, synth
 from oracle import nvfp4_oracle as O
+from oracle import nvfp4_ref as R
 
 DEV = "cuda:0"
 
@@ -27,6 +28,11 @@ def log(msg: str) -> None:
 def bf16_t2np(t: torch.Tensor) -> np.ndarray:
     """int16-viewed bf16 torch tensor -> float64 numpy."""
     return O.bf16_from_bits(t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def bf16_bits_of(t: torch.Tensor) -> np.ndarray:
+    """bf16 (or int16-viewed bf16) torch tensor -> uint16 bit patterns on the host."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
 def np2bf16_t(a: np.ndarray, device=DEV) -> torch.Tensor:
@@ -67,10 +73,12 @@ class Setup:
                 torch.from_numpy(self.wts).to(DEV))
 
     def oracle_quantize(self, e: int) -> tuple:
+        """The oracle's NVFP4 quantization of expert e's raw weights (the C form of the oracle's
+        quantizer, pinned against brute force and the NumPy form)."""
         if e not in self.oracle_w:
             w13, w2 = self.raw_dev[e]
-            c13 = O.quantize_nvfp4(bf16_t2np(w13.view(torch.int16)))
-            c2 = O.quantize_nvfp4(bf16_t2np(w2.view(torch.int16)))
+            c13 = R.quantize_bits(bf16_bits_of(w13))
+            c2 = R.quantize_bits(bf16_bits_of(w2))
             self.oracle_w[e] = c13 + c2
         return self.oracle_w[e]
 

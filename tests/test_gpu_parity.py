@@ -32,6 +32,11 @@ ODD_K = synth.Workload("odd_k640_e16", 128, 6, 1024, 640, (8,), 0, 16, 1)
 # m-tile in both GEMMs (intermediate 512, hidden 1024): the large-tile kernels' bands of m-tiles,
 # whole and ragged, and tail tiles.
 MANY_MT = synth.Workload("many_mtiles_e4", 4, 1, 1024, 512, (4000,), 0, 4, 1, zipf=True)
+# Many 16-row m-tiles with a short L2 reduction (intermediate 1024 = four 256-element chunks, one
+# per wave of the 16-row kernel) and hidden 7168: with block_m 16 forced, 40 m-tiles x 224 L2 groups
+# put ~17 groups on every workgroup of the 16-row L2 kernel (the weight-scale copies of its loader
+# run ahead of the compute across group boundaries).
+SMALL_K1024 = synth.Workload("small_k1024_e4", 4, 2, 7168, 1024, (320,), 0, 4, 1)
 TINY = synth.WORKLOADS[0]
 DECODE = synth.WORKLOADS[1]
 
@@ -219,6 +224,56 @@ def test_quantizer_edge_cases():
     mm.nvfp4_quantize_act(z, codes, scales, gs, workspace=ws)
     torch.cuda.synchronize()
     assert gs.item() == 1.0 and int(scales.sum()) == 0 and int(codes.sum()) == 0
+
+
+def test_quantizer_hand_built_bytes():
+    """The GPU quantizer writes the bytes worked out by hand from the format definition
+    (tests/golden/nvfp4_layout_literal.txt: exact ties, -0, a zero block, scales 448/112/224/0)."""
+    import os
+
+    g = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "nvfp4_layout_literal.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                key, *vals = line.split()
+                g[key] = [float(v) for v in vals] if key[0] in "xg" else [int(v, 16) for v in vals]
+    x = np.array([g["x0"], g["x1"]])
+    codes = torch.empty(2, 16, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(2, 2, dtype=torch.uint8, device=DEV)
+    gs = torch.empty(1, dtype=torch.float32, device=DEV)
+    ws = torch.empty(mm.megamoe_quant_workspace_bytes(2, 32), dtype=torch.uint8, device=DEV)
+    mm.nvfp4_quantize_act(np2bf16_t(x), codes, scales, gs, workspace=ws)
+    torch.cuda.synchronize()
+    assert gs.item() == g["gs"][0]
+    assert np_i32(codes).tolist() == [g["codes0"], g["codes1"]]
+    assert np_i32(scales).tolist() == [g["scales0"], g["scales1"]]
+
+
+def test_small_class_many_groups_short_k():
+    """16-row kernels only (block_m 16 forced), L2 with K = 1024 and ~17 groups per workgroup:
+    every stage against the oracle (h, y within 1e-3; end to end 1e-2 / 0.9999)."""
+    s = setup_for(SMALL_K1024, 320)
+    ref = oracle_chain(s)
+    L = run_gpu(s, block_m_override=16)
+    check_tables(L, ref)
+    sched = np_i32(L.sched)
+    assert sched[1] >= 40 and sched[2] == 0  # >= 40 small m-tiles, no large ones
+    valid = ref["row_token"] >= 0
+    err_h = rel_frob(bf16_t2np(L.h[:L.M_cap])[valid], ref["h"][valid])
+    # L2 on the oracle's quantized h
+    hq = torch.from_numpy(ref["h_codes"]).to(DEV)
+    hs = torch.from_numpy(ref["h_scales"]).to(DEV)
+    hg = torch.tensor([float(ref["gs_h"])], dtype=torch.float32, device=DEV)
+    y = torch.empty_like(L.y[:L.M_cap])
+    w = s.gpu_w
+    mm.moe_grouped_gemm_l2(hq, hs, hg, L.padded_offsets, L.counts, L.sched, w.w2_codes, w.w2_scales, w.w2_gs, y,
+                           16, 0)
+    torch.cuda.synchronize()
+    err_y = rel_frob(bf16_t2np(y)[valid], ref["y"][valid])
+    out = bf16_t2np(L.out[:L.T])
+    err, cos = rel_frob(out, ref["out"]), cosine(out, ref["out"])
+    log(f"[small k1024] l1 {err_h:.2e} l2 {err_y:.2e} e2e {err:.2e} cos {cos:.7f}")
+    assert err_h <= STAGE_TOL and err_y <= STAGE_TOL and err <= E2E_TOL and cos >= E2E_COS
 
 
 def test_quantizer_random_global_scales():

@@ -101,6 +101,53 @@ def test_e2m1_decode_matches_bitfields():
         assert O.e2m1_value(c) == (-mag if s else mag)
 
 
+# ---------------------------------------------------------------------------
+# byte layout: literal bytes written out by hand (tests/golden/nvfp4_layout_literal.txt)
+# ---------------------------------------------------------------------------
+
+def read_layout_literal():
+    rows = {}
+    with open(os.path.join(GOLDEN, "nvfp4_layout_literal.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key.startswith("x"):
+                rows[key] = np.array([float(v) for v in vals])
+            elif key == "gs":
+                rows[key] = float(vals[0])
+            else:
+                rows[key] = [int(v, 16) for v in vals]
+    return rows
+
+
+def test_pack_nibbles_literal_bytes():
+    """The even element goes in the low nibble: codes (1, 2, 0xF, 0x8) are the bytes 0x21, 0x8F."""
+    assert O.pack_nibbles(np.array([[1, 2, 0xF, 0x8]], np.uint8)).tolist() == [[0x21, 0x8F]]
+    assert O.unpack_nibbles(np.array([[0x21, 0x8F]], np.uint8)).tolist() == [[1, 2, 0xF, 0x8]]
+    # a byte's low nibble is element 0 of the pair after decoding as well
+    assert O.dequantize_blocks(np.array([[0x71] + [0] * 7], np.uint8), np.array([[0x38]], np.uint8))[0, :2].tolist() \
+        == [0.5, 6.0]  # scale 0x38 = 1.0
+
+
+def test_hand_built_tensor_bytes():
+    """The quantizer reproduces bytes worked out by hand from the format's definition (codes with
+    exact ties, -0, a zero block, block scales 448 / 112 / 224 / 0, gs = 448)."""
+    g = read_layout_literal()
+    x = np.stack([g["x0"], g["x1"]])
+    assert np.signbit(x[0, 15]) and np.signbit(x[1, 31])  # "-0" is -0.0
+    codes, scales, gs = O.quantize_nvfp4(x)
+    assert float(gs) == g["gs"]
+    assert codes.tolist() == [g["codes0"], g["codes1"]]
+    assert scales.tolist() == [g["scales0"], g["scales1"]]
+    # decoding the bytes: row 0 lies on its blocks' grids, row 1's ties went to the even code
+    dec = O.dequantize_blocks(codes, scales) / float(gs)
+    assert np.array_equal(dec[0], x[0])
+    assert dec[1, :16].tolist() == [3, 1, 0.25, 0.75, -2, 0.5, 1, 0, 0.5, 2, 2, 0, -1, -0.5, 0.5, -3]
+    assert not dec[1, 16:].any()
+
+
 def test_decode_products_exact_in_f16_and_bf16():
     """Every E2M1 x finite E4M3 product is exact in fp16 and bf16 (why the GPU decodes to fp16)."""
     prods = (O.E2M1_MAGNITUDES[:, None] * O.E4M3_GRID[None, :]).ravel()
@@ -441,6 +488,55 @@ def test_nonlocal_tokens_are_plus_zero():
     none = np.all(r["token_rows"] < 0, axis=1)
     assert none.any()
     assert np.all(O.bf16_bits(r["out"][none]) == 0)
+
+
+@pytest.mark.parametrize("P", [3, 4, 128])
+def test_padded_layer_equals_unpadded(P):
+    """Padding each expert's rows to a multiple of P (padded_expert_offsets, CURRENT_BUG.md@2e65594
+    "Test Plan" Phase 2) moves rows, never values: with a local share starting at e0 > 0, out is
+    bitwise that of P = 1, every assignment's h and y row is the unpadded run's row, gs_h is the
+    same, and padded rows hold -1 / zero codes / zero scales."""
+    base = _tiny_layer_inputs(E=5, k=2, T=13, Eg=9, e0=2, seed=11)
+    r1 = O.moe_layer(**base)
+    rP = O.moe_layer(**dict(base, pad_multiple=P))
+    counts = rP["counts"]
+    assert np.array_equal(counts, r1["counts"]) and counts.sum() > 0
+    assert np.array_equal(rP["padded_offsets"], np.concatenate([[0], np.cumsum((counts + P - 1) // P * P)]))
+    assert not np.array_equal(rP["padded_offsets"], rP["expert_offsets"])  # padding is really there
+    assert np.array_equal(rP["out"], r1["out"])
+    assert float(rP["gs_h"]) == float(r1["gs_h"])
+    t1, tP = r1["token_rows"], rP["token_rows"]
+    assert np.array_equal(t1 >= 0, tP >= 0)
+    m = t1 >= 0
+    for key in ("h", "y", "h_codes", "h_scales"):
+        assert np.array_equal(rP[key][tP[m]], r1[key][t1[m]])
+    pad = rP["row_token"] < 0
+    assert pad.sum() == len(rP["row_token"]) - counts.sum()
+    assert not rP["h"][pad].any() and not rP["y"][pad].any()
+    assert not rP["h_codes"][pad].any() and not rP["h_scales"][pad].any()
+
+
+def test_padded_rows_are_never_read():
+    """L1 reads only rows padded_offsets[e] .. + counts[e] of each expert, through row_token, and
+    L2 only those rows of h: poisoning every padding row (NaN block scales, -1 tokens) changes
+    nothing."""
+    inp = _tiny_layer_inputs(E=5, k=2, T=13, Eg=9, e0=2, seed=12, P=8)
+    r = O.moe_layer(**inp)
+    pad = r["row_token"] < 0
+    assert pad.any()
+    hc, hs = r["h_codes"].copy(), r["h_scales"].copy()
+    hc[pad], hs[pad] = 0xFF, 0x7F
+    y = O.moe_l2(hc, hs, r["gs_h"], r["padded_offsets"], r["counts"], inp["w2_codes"], inp["w2_scales"],
+                 inp["w2_gs"])
+    assert np.array_equal(y, r["y"])
+    # padding rows of row_token pointed at a poisoned extra token row of x are not followed either
+    T = r["x_codes"].shape[0]
+    xc = np.concatenate([r["x_codes"], np.full((1, r["x_codes"].shape[1]), 0xFF, np.uint8)])
+    xs = np.concatenate([r["x_scales"], np.full((1, r["x_scales"].shape[1]), 0x7F, np.uint8)])
+    rt = np.where(pad, T, r["row_token"]).astype(np.int32)
+    h, amax = O.moe_l1(xc, xs, r["gs_x"], rt, r["padded_offsets"], r["counts"],
+                       inp["w13_codes"], inp["w13_scales"], inp["w13_gs"])
+    assert np.array_equal(h, r["h"]) and amax == r["amax_h"]
 
 
 def test_decode_t1_has_no_local_work():
