@@ -153,6 +153,29 @@ int32_t moe_route_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t
                           int32_t* row_token, int32_t* token_rows, int32_t* sched,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the static per-GPU scratch of moe_route_permute_noalloc (1 MiB). */
+#define MEGAMOE_ROUTE_NOALLOC_SCRATCH_BYTES (1 << 20)
+
+/* ------------------------------------------------------------------------------------------
+ * moe_route_permute_noalloc - moe_route_permute without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).
+ *
+ * Arguments and results as moe_route_permute, bit for bit, minus workspace / workspace_bytes.
+ * The scratch moe_route_permute keeps in its workspace (the per-chunk expert histograms) lives in
+ * a static array of MEGAMOE_ROUTE_NOALLOC_SCRATCH_BYTES bytes in device memory, one per GPU the
+ * library runs on, held until the process ends; the call allocates nothing.  Sizes whose
+ * megamoe_route_workspace_bytes(T, k, num_experts) exceeds that return MEGAMOE_ERR_WORKSPACE
+ * before any launch (with 384 experts: up to 698,368 assignments, e.g. T = 116,394 at k = 6).
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time on the same GPU
+ * (other streams, other host threads) race and must be ordered by the caller.  The first call on a
+ * device looks up the array's device address (MEGAMOE_ERR_LAUNCH if that fails).
+ * ---------------------------------------------------------------------------------------- */
+int32_t moe_route_permute_noalloc(const int32_t* topk_ids, int32_t T, int32_t k, int32_t expert_begin,
+                                  int32_t num_experts, int32_t pad_multiple, int32_t block_m_override,
+                                  int32_t* counts, int32_t* expert_offsets, int32_t* padded_offsets,
+                                  int32_t* row_token, int32_t* token_rows, int32_t* sched, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * moe_route_quantize - moe_route_permute and nvfp4_quantize_act of x in one call.
  *

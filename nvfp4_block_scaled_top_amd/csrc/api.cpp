@@ -61,12 +61,12 @@ extern "C" int64_t megamoe_row_capacity(int32_t T, int32_t k, int32_t num_expert
 
 namespace {
 
-// Checks of moe_route_permute's arguments (also made by moe_route_logits).
-int32_t route_args_ok(int32_t T, int32_t k, int32_t expert_begin, int32_t num_experts, int32_t pad_multiple,
-                      int32_t block_m_override, const int32_t* topk_ids, const int32_t* counts,
-                      const int32_t* expert_offsets, const int32_t* padded_offsets, const int32_t* row_token,
-                      const int32_t* token_rows, const int32_t* sched, const void* workspace,
-                      size_t workspace_bytes) {
+// Checks of moe_route_permute's arguments other than the workspace (also made by
+// moe_route_logits, moe_route_quantize and moe_route_permute_noalloc).
+int32_t route_args_ok_no_ws(int32_t T, int32_t k, int32_t expert_begin, int32_t num_experts, int32_t pad_multiple,
+                            int32_t block_m_override, const int32_t* topk_ids, const int32_t* counts,
+                            const int32_t* expert_offsets, const int32_t* padded_offsets, const int32_t* row_token,
+                            const int32_t* token_rows, const int32_t* sched) {
   if (T < 0 || k < 1 || k > 64 || num_experts < 1 || num_experts > MEGAMOE_MAX_EXPERTS || pad_multiple < 1 ||
       expert_begin < 0)
     return MEGAMOE_ERR_SHAPE;
@@ -78,6 +78,18 @@ int32_t route_args_ok(int32_t T, int32_t k, int32_t expert_begin, int32_t num_ex
   if (!counts || !expert_offsets || !padded_offsets || !sched) return MEGAMOE_ERR_NULL;
   if (M_cap > 0 && !row_token) return MEGAMOE_ERR_NULL;
   if (n > 0 && (!topk_ids || !token_rows)) return MEGAMOE_ERR_NULL;
+  return MEGAMOE_OK;
+}
+
+// All of moe_route_permute's checks, the workspace included.
+int32_t route_args_ok(int32_t T, int32_t k, int32_t expert_begin, int32_t num_experts, int32_t pad_multiple,
+                      int32_t block_m_override, const int32_t* topk_ids, const int32_t* counts,
+                      const int32_t* expert_offsets, const int32_t* padded_offsets, const int32_t* row_token,
+                      const int32_t* token_rows, const int32_t* sched, const void* workspace,
+                      size_t workspace_bytes) {
+  const int32_t rc = route_args_ok_no_ws(T, k, expert_begin, num_experts, pad_multiple, block_m_override, topk_ids,
+                                         counts, expert_offsets, padded_offsets, row_token, token_rows, sched);
+  if (rc != MEGAMOE_OK) return rc;
   const size_t need = megamoe_route_workspace_bytes(T, k, num_experts);
   if (workspace_bytes < need) return MEGAMOE_ERR_WORKSPACE;
   if (need > 0 && !workspace) return MEGAMOE_ERR_NULL;
@@ -156,6 +168,25 @@ int32_t moe_route_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t
   return launch_status(launch_route(topk_ids, T, k, expert_begin, num_experts, pad_multiple, block_m_override, counts,
                                     expert_offsets, padded_offsets, row_token, M_cap, token_rows, sched,
                                     static_cast<int32_t*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_route_permute_noalloc(const int32_t* topk_ids, int32_t T, int32_t k, int32_t expert_begin,
+                                  int32_t num_experts, int32_t pad_multiple, int32_t block_m_override,
+                                  int32_t* counts, int32_t* expert_offsets, int32_t* padded_offsets,
+                                  int32_t* row_token, int32_t* token_rows, int32_t* sched, void* stream) {
+  const int32_t rc = route_args_ok_no_ws(T, k, expert_begin, num_experts, pad_multiple, block_m_override, topk_ids,
+                                         counts, expert_offsets, padded_offsets, row_token, token_rows, sched);
+  if (rc != MEGAMOE_OK) return rc;
+  if (megamoe_route_workspace_bytes(T, k, num_experts) > (size_t)MEGAMOE_ROUTE_NOALLOC_SCRATCH_BYTES)
+    return MEGAMOE_ERR_WORKSPACE;
+  const int64_t M_cap = megamoe_row_capacity(T, k, num_experts, pad_multiple);
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  int32_t* scratch = nullptr;
+  if (route_noalloc_scratch(&scratch) != hipSuccess) return MEGAMOE_ERR_LAUNCH;
+  return launch_status(launch_route(topk_ids, T, k, expert_begin, num_experts, pad_multiple, block_m_override, counts,
+                                    expert_offsets, padded_offsets, row_token, M_cap, token_rows, sched, scratch,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_route_quantize(const int32_t* topk_ids, int32_t T, int32_t k, int32_t expert_begin, int32_t num_experts,

@@ -37,6 +37,10 @@ hipError_t launch_route(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e
                         int32_t* row_token, int64_t M_cap, int32_t* token_rows, int32_t* sched,
                         int32_t* ws, hipStream_t stream);
 
+// Device address of this GPU's static routing scratch (MEGAMOE_ROUTE_NOALLOC_SCRATCH_BYTES bytes),
+// looked up once per device; it takes the place of the workspace in moe_route_permute_noalloc.
+hipError_t route_noalloc_scratch(int32_t** addr);
+
 // ---- router ----------------------------------------------------------------------------------
 hipError_t launch_router(const float* logits, int32_t T, int32_t Eg, int32_t k, int32_t* ids, float* weights,
                          hipStream_t stream);

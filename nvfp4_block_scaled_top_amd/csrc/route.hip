@@ -15,6 +15,9 @@
 //   3. scatter: each chunk ranks its assignments among equal experts with wave ballots (a
 //               lane's rank = earlier lanes with the same expert) plus the counts of earlier
 //               waves, so rows inside an expert follow ascending (token, slot) order.
+#include <atomic>
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 #include "quant_device.h"
@@ -298,6 +301,44 @@ hipError_t launch_route(const int32_t* topk_ids, int32_t T, int32_t k, int32_t e
   hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(kRouteChunk), wcnt_bytes, stream, topk_ids, n, k, e0, E,
                      ws, poff, row_token, token_rows);
   return hipGetLastError();
+}
+
+// ---- scratch for the no-allocation entry point ----------------------------------------------------
+// moe_route_permute_noalloc serves callers that cannot allocate device memory: the per-chunk
+// histograms that moe_route_permute keeps in the caller's workspace live here instead, in one static
+// array per GPU (held until the process ends).  In host code `scratch` names a host-side stand-in,
+// not device memory, so its device address is looked up once per device (with that device current)
+// and only that address is used: it is what the kernels receive, like the workspace pointer.  Nothing
+// in it needs to start at zero: route_count writes every histogram entry before route_scan reads it.
+// Every call on a GPU shares that GPU's array, so calls that overlap in time on one GPU race.
+static __device__ __align__(256) int32_t scratch[MEGAMOE_ROUTE_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<int32_t*> g_scratch_addr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t route_noalloc_scratch(int32_t** addr) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  int32_t* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* a = nullptr;
+      err = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+      if (err != hipSuccess) return err;
+      if (a == nullptr) return hipErrorInvalidSymbol;
+      p = static_cast<int32_t*>(a);
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return hipSuccess;
 }
 
 }  // namespace megamoe

@@ -19,6 +19,9 @@ _lib = None
 #: Slots of per-workgroup h amax written by moe_grouped_gemm_l1_silu (MEGAMOE_L1_AMAX_PARTS).
 L1_AMAX_PARTS = 1280
 
+#: Bytes of the static per-GPU scratch of moe_route_permute_noalloc (MEGAMOE_ROUTE_NOALLOC_SCRATCH_BYTES).
+ROUTE_NOALLOC_SCRATCH_BYTES = 1 << 20
+
 ERRORS = {
     -1: "MEGAMOE_ERR_NULL",
     -2: "MEGAMOE_ERR_SHAPE",
@@ -43,6 +46,7 @@ SIGNATURES = {
     "moe_grouped_gemm_l1_silu_nvfp4": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32,
                                               _I32, _P, _P, _P, _P, _P]),
     "moe_route_permute": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_permute_noalloc": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]),
     "nvfp4_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_quantize_act_gs": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "moe_grouped_gemm_l1_silu": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
@@ -150,6 +154,16 @@ def moe_route_permute(topk_ids, expert_begin, num_experts, pad_multiple, counts,
         _ptr(topk_ids), T, k, expert_begin, num_experts, pad_multiple, block_m_override, _ptr(counts),
         _ptr(expert_offsets), _ptr(padded_offsets), _ptr(row_token), _ptr(token_rows), _ptr(sched),
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_route_permute_noalloc(topk_ids, expert_begin, num_experts, pad_multiple, counts, expert_offsets,
+                              padded_offsets, row_token, token_rows, sched, block_m_override=0, stream=None):
+    """moe_route_permute with the library's static per-GPU scratch instead of a workspace."""
+    T, k = topk_ids.shape
+    _check("moe_route_permute_noalloc", lib().moe_route_permute_noalloc(
+        _ptr(topk_ids), T, k, expert_begin, num_experts, pad_multiple, block_m_override, _ptr(counts),
+        _ptr(expert_offsets), _ptr(padded_offsets), _ptr(row_token), _ptr(token_rows), _ptr(sched),
+        _stream(stream)))
 
 
 def moe_route_quantize(topk_ids, expert_begin, num_experts, pad_multiple, counts, expert_offsets, padded_offsets,

@@ -77,6 +77,24 @@ def test_route_rejects_bad_args(lib):
     assert f(FAKE, 4, 6, 0, 48, 1, 0, *ok, FAKE, 4, None) == -3               # workspace too small
 
 
+def test_route_noalloc_rejects_bad_args_and_oversize(lib):
+    """The no-allocation routing entry point makes moe_route_permute's checks and rejects sizes whose
+    scratch would exceed its static per-GPU array, all before any HIP call."""
+    f = lib.moe_route_permute_noalloc
+    ok = [FAKE] * 6
+    assert f(FAKE, 4, 0, 0, 48, 1, 0, *ok, None) == -2             # k < 1
+    assert f(FAKE, 4, 6, 0, 48, 0, 0, *ok, None) == -2             # P < 1
+    assert f(None, 4, 6, 0, 48, 1, 0, *ok, None) == -1             # ids NULL
+    assert f(FAKE, 4, 6, 0, 48, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -1  # sched NULL
+    cap = mm.ROUTE_NOALLOC_SCRATCH_BYTES
+    assert re.search(rf"#define MEGAMOE_ROUTE_NOALLOC_SCRATCH_BYTES \(1 << 20\)", open(HEADER).read())
+    assert cap == 1 << 20
+    # 384 experts: 682 chunks of 1024 assignments fit (682 * 384 * 4 <= 1 MiB), 683 do not
+    assert mm.megamoe_route_workspace_bytes(682 * 1024 // 8, 8, 384) <= cap
+    assert mm.megamoe_route_workspace_bytes(683 * 1024 // 8, 8, 384) > cap
+    assert f(FAKE, 683 * 1024 // 8, 8, 0, 384, 1, 0, *ok, None) == -3  # scratch too small
+
+
 def test_router_rejects_bad_args(lib):
     f = lib.moe_router_topk
     assert f(FAKE, 4, 384, 0, FAKE, FAKE, None) == -2        # k < 1
