@@ -80,7 +80,9 @@ def _ulp_excess(got, ref):
 def test_block_m_override_changes_speed_only(bm):
     """Forcing one tile height (16-row MFMA blocks with K split across waves, or 256x256 LDS tiles)
     changes only the fp32 summation order: per stage on identical inputs, h and y agree to within
-    one bf16 step element by element and to 1e-4 in relative Frobenius norm (measured ~1e-6)."""
+    one bf16 step element by element and to 1e-5 in relative Frobenius norm.  (Measured: identical
+    bits.  Each product of two decoded NVFP4 values has at most 12 significant bits, so these fp32
+    partial sums round rarely, if ever.)"""
     from nvfp4_block_scaled_top_amd import megamoe as mm
 
     s = mid()
@@ -108,7 +110,7 @@ def test_block_m_override_changes_speed_only(bm):
     err = rel_frob(b, a)
     log(f"[block_m={bm}] h {err_h:.2e} ({ex_h} > 1 ulp), y {err_y:.2e} ({ex_y} > 1 ulp), out {err:.2e}")
     assert ex_h == 0 and ex_y == 0
-    assert err_h <= 1e-4 and err_y <= 1e-4 and err <= 1e-3
+    assert err_h <= 1e-5 and err_y <= 1e-5 and err <= 1e-4
     # the forced run is itself deterministic
     assert np.array_equal(out_bits(forced), out_bits(run_gpu(s, block_m_override=bm)))
 
