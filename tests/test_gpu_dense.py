@@ -131,7 +131,7 @@ def test_layer_with_shared_expert(i, T):
 def test_gate_up_silu_nvfp4_equals_gate_up_then_quantizer(M, K, I):
     """nvfp4_linear_gate_up_silu_nvfp4 (h quantized in the epilogue with a given scale) equals
     nvfp4_linear_gate_up_silu followed by nvfp4_quantize_act_gs, bit for bit on every row; the
-    amax slots are those of the plain call."""
+    max over the amax slots is that of the plain call."""
     rng = np.random.default_rng(M * 5 + K + I)
     ac, as_, ag = quantized(rng, M, K, 0.09)
     wc, ws, wg = quantized(rng, 2 * I, K, 0.02)
@@ -150,7 +150,8 @@ def test_gate_up_silu_nvfp4_equals_gate_up_then_quantizer(M, K, I):
     mm.nvfp4_linear_gate_up_silu_nvfp4(u8(ac), u8(as_), f32(ag), u8(wc), u8(ws), f32(wg), gs, codes, scales, amax2,
                                        wsp)
     torch.cuda.synchronize()
-    assert torch.equal(codes, ref_c) and torch.equal(scales, ref_s) and torch.equal(amax2, amax)
+    assert torch.equal(codes, ref_c) and torch.equal(scales, ref_s)
+    assert amax2.min().item() >= 0.0 and amax2.max().item() == amax.max().item()  # every slot written; same max |h|
     log(f"[dense] gate_up_silu_nvfp4 M={M} K={K} I={I}: bit-exact, "
         f"{int((np_i32(scales) == 0x7E).sum())} saturated blocks")
 
