@@ -735,8 +735,8 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
 // sustains ~97% of the fp16 peak on gfx950, the 16x16x32 shape only ~55%).
 //
 // Stage layout (per operand): codes row-major, kLRowBytes per tile row R, with the 16-byte chunk
-// c (elements 32c..32c+31 of the stage) stored in slot c ^ swizzle(R) so that the 16-byte
-// fragment reads of 8 consecutive rows hit distinct banks; a DMA instruction covers 1024 /
+// c (elements 32c..32c+31 of the stage) stored in slot c ^ lswz(R) so that the 16-byte fragment
+// reads of 16 consecutive rows hit distinct banks; a DMA instruction covers 1024 /
 // kLRowBytes rows with kLChunks lanes per row (row-contiguous global bytes).  Scales: the stage's 8
 // block scales of row R at R * 8 (lane half h reads the 4 bytes at R * 8 + 4h).
 // Lane (p = lane % 32, h = lane / 32) of a 32-row fragment owns elements [h * kLKs/2, +kLKs/2) of
@@ -759,7 +759,10 @@ constexpr int kLWaves = 8, kLThreads = kLWaves * kWave;
 constexpr int kLKs = 128;                                        // stage depth (K elements)
 constexpr int kLRowBytes = kLKs / 2;                             // code bytes of one row per stage
 constexpr int kLChunks = kLRowBytes / 16;                        // 16-byte chunks per row
-constexpr int kLSwzShift = 1;                                    // row bits that pick the swizzle
+// 16-byte chunk slot swizzle of tile row R: the fragment reads of 16 consecutive rows (16 lanes x
+// 16 B, one 256-byte LDS cycle) and of 8 consecutive rows both hit distinct slots.
+__device__ __forceinline__ constexpr int lswz(int R) { return ((R >> 1) ^ (R >> 3)) & 3; }
+static_assert(kLChunks == 4, "lswz permutes 4 chunks per row");
 constexpr int kLScaleRow = kLKs / 16;                            // scale bytes of one row per stage
 constexpr int kLSteps = kLKs / 16;                               // 32x32x16 MFMA steps per stage
 constexpr int kLMI = 2;                                          // 32-row MFMA blocks per wave
@@ -823,7 +826,7 @@ __device__ __forceinline__ void large_tile(const GemmArgs& p, uint8_t* smem, int
   };
   // ---- DMA sources of this lane ----------------------------------------------------------------
   // codes: instruction j covers tile rows base + j*rows_per + lane/kLChunks; lane%kLChunks picks
-  // the LDS slot and the global chunk (lane%kLChunks) ^ swizzle(row) goes there; scales:
+  // the LDS slot and the global chunk (lane%kLChunks) ^ lswz(row) goes there; scales:
   // instruction j covers rows base + 32j + lane/2, lane%2 picking the 4-byte half (LDS scale
   // layout: 8 bytes per row).
   auto a_row_of = [&](int R) -> int64_t {
@@ -841,13 +844,13 @@ __device__ __forceinline__ void large_tile(const GemmArgs& p, uint8_t* smem, int
 #pragma unroll
   for (int j = 0; j < S::kACodeDma; ++j) {
     const int R = S::kARows * wave + rows_per * j + lane / kLChunks;
-    const int chunk = (lane % kLChunks) ^ ((R >> kLSwzShift) & (kLChunks - 1));
+    const int chunk = (lane % kLChunks) ^ lswz(R);
     a_code_src[j] = p.a_codes + a_row_of(R) * Kh + 16 * chunk;
   }
 #pragma unroll
   for (int j = 0; j < S::kBCodeDma; ++j) {
     const int R = S::kBRows * wave + rows_per * j + lane / kLChunks;
-    const int chunk = (lane % kLChunks) ^ ((R >> kLSwzShift) & (kLChunks - 1));
+    const int chunk = (lane % kLChunks) ^ lswz(R);
     b_code_src[j] = p.w_codes + b_row_of(R) * Kh + 16 * chunk;
   }
   static_assert(kLScaleRow == 8, "scale DMA assumes 128-K stages");
@@ -891,8 +894,8 @@ __device__ __forceinline__ void large_tile(const GemmArgs& p, uint8_t* smem, int
     const uint8_t* b_codes = base + S::kAOpBytes;
     const uint8_t* b_scales = b_codes + S::kBCodeBytes;
     constexpr int CPL = kLChunks / 2;  // chunks per lane half
-    // rows 32i + p and brow_of(f) + p share (row >> shift) with p: offsets are multiples of 32
-    const int swz = (p32 >> kLSwzShift) & (kLChunks - 1);
+    // rows 32i + p and brow_of(f) + p have the swizzle of p: offsets are multiples of 32
+    const int swz = lswz(p32);
     // scale bytes of this lane half: 4 per row (128-K stages)
     auto scale_word = [&](const uint8_t* sp, int row) -> uint32_t {
       return *reinterpret_cast<const uint32_t*>(sp + row * kLScaleRow + 4 * h2);
