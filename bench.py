@@ -32,7 +32,10 @@ their own step times and fractions; the step time with calibrated global scales 
 with the scales of a warm-up forward: no amax pass); per-step p10/p50/p90; GEMM-only time (L1 + L2);
 the L2 large-tile kernel alone; the decode aggregate over 64 routing seeds (sum of weight bytes over
 sum of step times); and, as context only, a 1 GiB device copy and an 8192^3 fp16 GEMM from the vendor
-BLAS measured on the same GPU.
+BLAS measured on the same GPU, with this repository's own measurement kernels (csrc/probe.hip): the
+HBM read rate of plain loads at the decode weight size in three access orders, the CU placement of a
+two-per-CU launch, and the dense NVFP4 GEMM on random versus zero codes (the clock's dependence on
+the operand data).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-seeds N] [--no-cpu-baseline] [--quick]
 """
@@ -399,7 +402,131 @@ def measured_ceilings():
         out[name] = round(work * 10 / (e0.elapsed_time(e1) * 1e-3), 1)
     del src, dst, a, bm
     torch.cuda.synchronize()
+    out["hbm_read"] = hbm_read_ceilings()
+    out["workgroup_placement"] = placement_check()
+    out["dense_nvfp4_gemm_operand_data"] = dense_data_dependence()
     return out
+
+
+def probe_lib():
+    """bench.py's measurement kernels (csrc/probe.hip, built by __graft_entry__.build())."""
+    import ctypes
+
+    from nvfp4_block_scaled_top_amd import build_lib
+
+    if not os.path.exists(build_lib.PROBE_LIB_PATH):
+        raise RuntimeError(f"{build_lib.PROBE_LIB_PATH} is missing: run __graft_entry__.build()")
+    h = ctypes.CDLL(build_lib.PROBE_LIB_PATH)
+    h.megamoe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    h.megamoe_probe_read.restype = ctypes.c_int
+    h.megamoe_probe_placement.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    h.megamoe_probe_placement.restype = ctypes.c_int
+    return h
+
+
+# (name, order, grid, loads in flight per thread): order 0 = all workgroups read neighbouring bytes
+# at any moment, 1 = one contiguous slab per workgroup, 2 = one contiguous eighth per XCD.
+READ_ORDERS = (("global_order_2048wg", 0, 2048, 1), ("global_order_512wg", 0, 512, 4),
+               ("xcd_eighths_512wg", 2, 512, 4), ("workgroup_slabs_512wg", 1, 512, 4))
+
+
+def hbm_read_ceilings(nbytes=149 * 2 ** 20, copies=4, reps=100):
+    """HBM read rate (GB/s) of a plain 16-byte-load kernel over `nbytes` (the decode L1 weight bytes
+    at T=8), rotating over `copies` buffers so that the 256 MB last-level cache does not hold them,
+    in the access orders of READ_ORDERS."""
+    import torch
+
+    lib = probe_lib()
+    stream = torch.cuda.current_stream()
+    bufs = [torch.full((nbytes,), i + 1, dtype=torch.uint8, device="cuda") for i in range(copies)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    res = {"bytes": nbytes}
+    for name, order, grid, unroll in READ_ORDERS:
+        def run(i):
+            rc = lib.megamoe_probe_read(bufs[i % copies].data_ptr(), nbytes, order, grid, unroll, sink.data_ptr(),
+                                        ctypes_stream(stream))
+            if rc != 0:
+                raise RuntimeError(f"megamoe_probe_read failed ({rc})")
+        for i in range(3):
+            run(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            run(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name + "_GBps"] = round(nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+    log(f"[bench] HBM read ceilings: {res}")
+    del bufs
+    return res
+
+
+def ctypes_stream(stream):
+    return stream.cuda_stream
+
+
+def placement_check():
+    """Whether the two workgroups of a 512-workgroup, two-per-CU launch that share a CU are b and
+    b + 256 (the 16-row GEMM gives those neighbouring work ranges), read from HW_ID / XCC_ID."""
+    import torch
+
+    lib = probe_lib()
+    out = torch.zeros(2 * 512, dtype=torch.int32, device="cuda")
+    rc = lib.megamoe_probe_placement(out.data_ptr(), 512, ctypes_stream(torch.cuda.current_stream()))
+    if rc != 0:
+        raise RuntimeError(f"megamoe_probe_placement failed ({rc})")
+    torch.cuda.synchronize()
+    h = out.cpu().numpy().astype(np.uint32).reshape(512, 2)
+    hw, xcc = h[:, 0], h[:, 1]
+    # HW_ID: CU in bits 8-11, shader array bit 12, shader engine bits 13-15
+    cu_key = [(int(xcc[b]), int((hw[b] >> 13) & 7), int((hw[b] >> 12) & 1), int((hw[b] >> 8) & 15)) for b in range(512)]
+    by_cu = {}
+    for b, k in enumerate(cu_key):
+        by_cu.setdefault(k, []).append(b)
+    pairs_ok = all(len(v) == 2 and v[1] - v[0] == 256 for v in by_cu.values())
+    xcd_ok = all(int(xcc[b]) == b % 8 for b in range(512))
+    res = {"cus": len(by_cu), "xcd_is_b_mod_8": xcd_ok, "cu_pairs_are_b_and_b_plus_256": pairs_ok}
+    log(f"[bench] workgroup placement: {res}")
+    return res
+
+
+def dense_data_dependence(reps=200):
+    """The same dense NVFP4 GEMM (nvfp4_linear, M=8192, K=7168, N=4096) on random codes and on zero
+    codes (same scales): the matrix core does the same work, so the ratio shows how much the clock
+    (power) depends on the operand data.  TFLOP/s each, ~0.1 s of work per case."""
+    import torch
+    from nvfp4_block_scaled_top_amd import megamoe
+
+    M, K, N = 8192, 7168, 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    stream = torch.cuda.current_stream()
+    a_c = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    w_c = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    a_s = torch.randint(0x28, 0x40, (M, K // 16), dtype=torch.uint8, device="cuda", generator=g)
+    w_s = torch.randint(0x28, 0x40, (N, K // 16), dtype=torch.uint8, device="cuda", generator=g)
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    out = torch.empty(M, N, dtype=torch.int16, device="cuda")
+    ws = torch.empty(megamoe.megamoe_dense_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+    res = {"shape": [M, K, N]}
+    for name, ac, wc in (("random_codes_TFLOPs", a_c, w_c),
+                         ("zero_codes_TFLOPs", torch.zeros_like(a_c), torch.zeros_like(w_c))):
+        call = lambda: megamoe.nvfp4_linear(ac, a_s, one, wc, w_s, one, out, ws)
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = round(2.0 * M * K * N / (ms * 1e-3) / 1e12, 1)
+    log(f"[bench] dense NVFP4 GEMM, random vs zero codes: {res}")
+    return res
 
 
 def cpu_baseline(wl, T):
@@ -607,7 +734,10 @@ def summarize_trace(path: str) -> None:
 
 
 def summarize_counters(path: str) -> None:
-    """Median per dispatch of every counter in a rocprofv3 --pmc CSV, for the library's kernels."""
+    """Median per dispatch of every counter in a rocprofv3 --pmc CSV, for the library's kernels.
+    With GRBM_GUI_ACTIVE (summed over the 8 XCDs) also the clock the kernel ran at: GRBM_GUI_ACTIVE
+    / 8 / the dispatch's duration (its Start/End timestamps, ns), for dispatches of at least 0.5 ms
+    (the counter's window is wider than a short dispatch)."""
     import csv
     vals = {}
     with open(path) as f:
@@ -615,8 +745,12 @@ def summarize_counters(path: str) -> None:
             name = r["Kernel_Name"].split("(")[0].replace("void ", "")
             if "megamoe::" not in name:
                 continue
-            vals.setdefault(name.replace("megamoe::", ""), {}).setdefault(r["Counter_Name"], []).append(
-                float(r["Counter_Value"]))
+            cs = vals.setdefault(name.replace("megamoe::", ""), {})
+            cs.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and r.get("End_Timestamp"):
+                ns = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                if ns >= 5e5:
+                    cs.setdefault("clock_GHz", []).append(float(r["Counter_Value"]) / 8.0 / ns)
     for k, cs in vals.items():
         parts = []
         for c, v in sorted(cs.items()):
@@ -662,6 +796,8 @@ def main():
                     help="kernel-trace CSV of a --trace-steps run: per-workload medians of kernel time per step")
     ap.add_argument("--summarize-counters", metavar="CSV",
                     help="rocprofv3 --pmc counter CSV: per-kernel medians of each counter")
+    ap.add_argument("--ceilings-only", action="store_true",
+                    help="print the measured ceilings (context of the bench line) as JSON and exit")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
@@ -688,6 +824,9 @@ def main():
         return
     if args.trace_steps:
         trace_steps(args.trace_steps)
+        return
+    if args.ceilings_only:
+        print(json.dumps(measured_ceilings()))
         return
 
     pre_wl = synth.WORKLOADS[3]

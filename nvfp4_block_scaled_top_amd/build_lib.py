@@ -56,5 +56,25 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+PROBE_SOURCE = "probe.hip"
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libmegamoe_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the measurement kernels bench.py uses (csrc/probe.hip, not part of the layer) into
+    PROBE_LIB_PATH and return the path."""
+    tmp = PROBE_LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, os.path.join(CSRC, PROBE_SOURCE), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
+    os.replace(tmp, PROBE_LIB_PATH)
+    return PROBE_LIB_PATH
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))

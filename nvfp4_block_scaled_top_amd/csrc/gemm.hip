@@ -1032,10 +1032,12 @@ __device__ __forceinline__ void large_tile(const GemmArgs& p, uint8_t* smem, int
     const int nrows = rows_left < BM ? rows_left : BM;
     uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
     const int col0 = nt * cols;
+    // Non-temporal: the tile is read again only by the next kernel, and keeping it out of the
+    // cache keeps the weight and A rows other tiles re-read (measured: L2 -2.5%, L1 -1%).
     for (int idx = tid; idx < nrows * chunks; idx += kLThreads) {
       const int r = idx / chunks, c = idx - r * chunks;
       const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * pitch + 16 * c);
-      *reinterpret_cast<u32x4*>(out + (int64_t)(row0 + r) * p.N + col0 + 8 * c) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + (int64_t)(row0 + r) * p.N + col0 + 8 * c));
     }
   }
   __syncthreads();  // staging reads done before the next tile's DMA refills the ring

@@ -1,0 +1,100 @@
+// Measurement kernels for bench.py, built into their own library (libmegamoe_probe.so); the MoE
+// layer does not use them.  They give the ceilings the layer's kernels are compared with:
+//  * megamoe_probe_read: the HBM read rate of three access orders over a buffer of a given size
+//    (decode streams ~150 MB of weights per GEMM), each lane summing 16-byte loads;
+//  * megamoe_probe_placement: the CU each workgroup of a two-per-CU launch runs on (the 16-row
+//    GEMM gives the two workgroups of a CU neighbouring work ranges, assuming workgroups b and
+//    b + 256 share a CU).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace megamoe_probe {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+
+// order 0: grid-stride over the whole buffer (at any moment the workgroups read neighbouring
+//          4 KB pieces);
+// order 1: each workgroup reads its own contiguous slab;
+// order 2: the workgroups of XCD x (b % 8 == x) grid-stride over the x-th eighth of the buffer.
+// U loads are in flight per thread; every load is in bounds (the tail loop takes the remainder).
+template <int U>
+__global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ p, uint64_t n16, int order,
+                                                        uint32_t* sink) {
+  uint64_t begin = 0, end = n16, first, stride;
+  const uint64_t tid = threadIdx.x;
+  if (order == 0) {
+    first = (uint64_t)blockIdx.x * kThreads + tid;
+    stride = (uint64_t)gridDim.x * kThreads;
+  } else if (order == 1) {
+    const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    begin = (uint64_t)blockIdx.x * per;
+    end = begin + per < n16 ? begin + per : n16;
+    first = begin + tid;
+    stride = kThreads;
+  } else {
+    const uint64_t x = blockIdx.x % kXcds, per_x = gridDim.x / kXcds;
+    begin = n16 * x / kXcds;
+    end = n16 * (x + 1) / kXcds;
+    first = begin + (uint64_t)(blockIdx.x / kXcds) * kThreads + tid;
+    stride = per_x * kThreads;
+  }
+  uint32_t acc = 0;
+  uint64_t i = first;
+  for (; i + (U - 1) * stride < end; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < end; i += stride) {
+    const u32x4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads; practically never taken
+}
+
+// Two workgroups of 256 threads per CU (78 KB of LDS each, like the 16-row GEMM); thread 0 of each
+// records the HW_ID and XCC_ID registers, then the workgroup waits ~spin cycles so that all of
+// them are resident at once.
+constexpr int kPlaceLdsWords = 78 * 1024 / 4;
+__global__ __launch_bounds__(kThreads, 2) void placement_kernel(uint32_t* out, int spin) {
+  __shared__ uint32_t lds[kPlaceLdsWords];
+  lds[threadIdx.x] = threadIdx.x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = __builtin_amdgcn_s_getreg((31 << 11) | 4);                 // HW_ID
+    out[2 * blockIdx.x + 1] = __builtin_amdgcn_s_getreg((31 << 11) | 20) + lds[0];   // XCC_ID (+0)
+  }
+  const long long t0 = clock64();
+  while (clock64() - t0 < spin) __builtin_amdgcn_s_sleep(2);
+}
+
+}  // namespace megamoe_probe
+
+// Returns 0, or -1 for bad arguments (bytes not a positive multiple of 16, grid not a multiple of
+// 8 in [8, 65536], unroll not 1 or 4, order not 0..2, null pointers), or the HIP error code.
+extern "C" int megamoe_probe_read(const void* buf, uint64_t bytes, int32_t order, int32_t grid, int32_t unroll,
+                                  uint32_t* sink, void* stream) {
+  using namespace megamoe_probe;
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || grid < 8 || grid > 65536 || grid % kXcds != 0 ||
+      (unroll != 1 && unroll != 4) || order < 0 || order > 2)
+    return -1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const u32x4* p = static_cast<const u32x4*>(buf);
+  if (unroll == 1) hipLaunchKernelGGL(read_kernel<1>, dim3(grid), dim3(kThreads), 0, s, p, bytes / 16, order, sink);
+  else hipLaunchKernelGGL(read_kernel<4>, dim3(grid), dim3(kThreads), 0, s, p, bytes / 16, order, sink);
+  return (int)hipGetLastError();
+}
+
+// out: 2 * grid words (HW_ID, XCC_ID per workgroup).  grid <= 512 (two per CU on 256 CUs, so all
+// are resident at once).  Returns 0, -1 for bad arguments, or the HIP error code.
+extern "C" int megamoe_probe_placement(uint32_t* out, int32_t grid, void* stream) {
+  using namespace megamoe_probe;
+  if (!out || grid < 1 || grid > 512) return -1;
+  hipLaunchKernelGGL(placement_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), out, 100000);
+  return (int)hipGetLastError();
+}

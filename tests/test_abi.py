@@ -177,3 +177,24 @@ def test_dense_nvfp4_rejects_bad_args(lib):
     assert f(FAKE, FAKE, FAKE, 4, 256, FAKE, FAKE, FAKE, 128, None, FAKE, FAKE, FAKE, FAKE, need, None) == -1  # h_gs
     assert f(FAKE, FAKE, FAKE, 4, 256, FAKE, FAKE, FAKE, 128, FAKE, None, FAKE, FAKE, FAKE, need, None) == -1  # codes
     assert f(FAKE, FAKE, FAKE, 4, 256, FAKE, FAKE, FAKE, 128, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == -3
+
+
+def test_probe_lib_exports_and_rejects_bad_args():
+    """bench.py's measurement kernels (csrc/probe.hip): the library loads, exports both entry points
+    and rejects bad arguments before any launch (no GPU is touched)."""
+    from nvfp4_block_scaled_top_amd import build_lib
+
+    if not os.path.exists(build_lib.PROBE_LIB_PATH):
+        pytest.skip("libmegamoe_probe.so not built")
+    h = ctypes.CDLL(build_lib.PROBE_LIB_PATH)
+    h.megamoe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    h.megamoe_probe_placement.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    fake = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+    assert h.megamoe_probe_read(None, 1024, 0, 512, 1, fake, None) == -1        # null buffer
+    assert h.megamoe_probe_read(fake, 1000, 0, 512, 1, fake, None) == -1        # bytes % 16
+    assert h.megamoe_probe_read(fake, 1024, 3, 512, 1, fake, None) == -1        # order
+    assert h.megamoe_probe_read(fake, 1024, 0, 500, 1, fake, None) == -1        # grid % 8
+    assert h.megamoe_probe_read(fake, 1024, 0, 512, 2, fake, None) == -1        # unroll
+    assert h.megamoe_probe_placement(fake, 513, None) == -1                     # grid > 512
+    assert h.megamoe_probe_placement(None, 512, None) == -1
