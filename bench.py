@@ -486,8 +486,11 @@ def placement_check():
     for b, k in enumerate(cu_key):
         by_cu.setdefault(k, []).append(b)
     pairs_ok = all(len(v) == 2 and v[1] - v[0] == 256 for v in by_cu.values())
-    xcd_ok = all(int(xcc[b]) == b % 8 for b in range(512))
-    res = {"cus": len(by_cu), "xcd_is_b_mod_8": xcd_ok, "cu_pairs_are_b_and_b_plus_256": pairs_ok}
+    # the XCD of workgroup 0 depends on where the previous dispatch left the round-robin; what the
+    # tile mappings use is that workgroups with equal b mod 8 share an XCD
+    xcd_ok = all(int(xcc[b]) == int(xcc[b % 8]) for b in range(512)) and len({int(x) for x in xcc[:8]}) == 8
+    res = {"cus": len(by_cu), "xcd_of_b_depends_on_b_mod_8": xcd_ok, "xcd_of_workgroup_0": int(xcc[0]),
+           "cu_pairs_are_b_and_b_plus_256": pairs_ok}
     log(f"[bench] workgroup placement: {res}")
     return res
 
@@ -743,9 +746,9 @@ def summarize_counters(path: str) -> None:
     with open(path) as f:
         for r in csv.DictReader(f):
             name = r["Kernel_Name"].split("(")[0].replace("void ", "")
-            if "megamoe::" not in name:
+            if "megamoe::" not in name and "megamoe_probe::" not in name:
                 continue
-            cs = vals.setdefault(name.replace("megamoe::", ""), {})
+            cs = vals.setdefault(name.replace("megamoe::", "").replace("megamoe_probe::", "probe::"), {})
             cs.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
             if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and r.get("End_Timestamp"):
                 ns = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
