@@ -279,6 +279,8 @@ int32_t nvfp4_quantize_act_gs(const void* x_bf16, int64_t rows, int64_t cols, co
  *              any expert whose count turns out to exceed the bound.  A bound that is too low
  *              costs time only.
  * h_bf16       bf16 [M_cap, I].   h_amax_parts float [MEGAMOE_L1_AMAX_PARTS].
+ * With M_cap == 0 (e.g. T == 0) there are no rows: x_codes, x_scales, row_token and h_bf16 may
+ * be NULL, no table is read, and the call only sets every slot of h_amax_parts to 0.
  * ---------------------------------------------------------------------------------------- */
 int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
                                  const int32_t* row_token, const int32_t* padded_offsets,
@@ -305,6 +307,8 @@ int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales
  * Arguments as for moe_grouped_gemm_l1_silu, with h_bf16 replaced by
  * h_gs         float [1] on the device: the global scale of h (e.g. from a warm-up pass).
  * h_codes      uint8 [M_cap, I/2];   h_scales  uint8 [M_cap, I/16].
+ * With M_cap == 0, x_codes, x_scales, row_token, h_codes and h_scales may be NULL and the call
+ * only sets every slot of h_amax_parts to 0.
  * ---------------------------------------------------------------------------------------- */
 int32_t moe_grouped_gemm_l1_silu_nvfp4(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
                                        const int32_t* row_token, const int32_t* padded_offsets,
@@ -329,6 +333,7 @@ int32_t moe_grouped_gemm_l1_silu_nvfp4(const uint8_t* x_codes, const uint8_t* x_
  * w2_codes/w2_scales/w2_gs   [E, H, I/2], [E, H, I/16], [E].
  * block_m_override, max_rows_per_expert   as for moe_grouped_gemm_l1_silu.
  * y_bf16       bf16 [M_cap, H].
+ * With M_cap == 0, h_codes, h_scales and y_bf16 may be NULL and the call enqueues nothing.
  * ---------------------------------------------------------------------------------------- */
 int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs,
                             const int32_t* padded_offsets, const int32_t* counts, const int32_t* sched,

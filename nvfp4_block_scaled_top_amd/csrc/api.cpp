@@ -260,11 +260,13 @@ int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales
   GemmClasses cls;
   if (!gemm_shape_ok(E, H, I, M_cap) || !classes_of(block_m_override, max_rows_per_expert, &cls))
     return MEGAMOE_ERR_SHAPE;
-  if (!x_codes || !x_scales || !x_gs || !row_token || !padded_offsets || !counts || !sched || !w13_codes ||
-      !w13_scales || !w13_gs || !h_bf16 || !h_amax_parts)
+  if (!x_gs || !padded_offsets || !counts || !sched || !w13_codes || !w13_scales || !w13_gs || !h_amax_parts)
     return MEGAMOE_ERR_NULL;
+  if (M_cap > 0 && (!x_codes || !x_scales || !row_token || !h_bf16)) return MEGAMOE_ERR_NULL;
   const int32_t dev = check_device();
   if (dev != MEGAMOE_OK) return dev;
+  if (M_cap == 0)  // no rows: only the amax slots, all 0
+    return launch_status(launch_fill_f32(h_amax_parts, MEGAMOE_L1_AMAX_PARTS, 0.0f, static_cast<hipStream_t>(stream)));
   GemmArgs a{x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
              E, H, I, h_bf16, h_amax_parts, 0};
   return launch_status(launch_gemm_l1(a, cls, static_cast<hipStream_t>(stream)));
@@ -279,11 +281,14 @@ int32_t moe_grouped_gemm_l1_silu_nvfp4(const uint8_t* x_codes, const uint8_t* x_
   GemmClasses cls;
   if (!gemm_shape_ok(E, H, I, M_cap) || !classes_of(block_m_override, max_rows_per_expert, &cls))
     return MEGAMOE_ERR_SHAPE;
-  if (!x_codes || !x_scales || !x_gs || !row_token || !padded_offsets || !counts || !sched || !w13_codes ||
-      !w13_scales || !w13_gs || !h_gs || !h_codes || !h_scales || !h_amax_parts)
+  if (!x_gs || !padded_offsets || !counts || !sched || !w13_codes || !w13_scales || !w13_gs || !h_gs ||
+      !h_amax_parts)
     return MEGAMOE_ERR_NULL;
+  if (M_cap > 0 && (!x_codes || !x_scales || !row_token || !h_codes || !h_scales)) return MEGAMOE_ERR_NULL;
   const int32_t dev = check_device();
   if (dev != MEGAMOE_OK) return dev;
+  if (M_cap == 0)  // no rows: only the amax slots, all 0
+    return launch_status(launch_fill_f32(h_amax_parts, MEGAMOE_L1_AMAX_PARTS, 0.0f, static_cast<hipStream_t>(stream)));
   GemmArgs a{x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
              E, H, I, nullptr, h_amax_parts, 0};
   a.q_gs = h_gs;
@@ -300,11 +305,11 @@ int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, con
   GemmClasses cls;
   if (!gemm_shape_ok(E, H, I, M_cap) || !classes_of(block_m_override, max_rows_per_expert, &cls))
     return MEGAMOE_ERR_SHAPE;
-  if (!h_codes || !h_scales || !h_gs || !padded_offsets || !counts || !sched || !w2_codes || !w2_scales || !w2_gs ||
-      !y_bf16)
-    return MEGAMOE_ERR_NULL;
+  if (!h_gs || !padded_offsets || !counts || !sched || !w2_codes || !w2_scales || !w2_gs) return MEGAMOE_ERR_NULL;
+  if (M_cap > 0 && (!h_codes || !h_scales || !y_bf16)) return MEGAMOE_ERR_NULL;
   const int32_t dev = check_device();
   if (dev != MEGAMOE_OK) return dev;
+  if (M_cap == 0) return MEGAMOE_OK;  // no rows: nothing to compute or write
   GemmArgs a{h_codes, h_scales, h_gs, nullptr, padded_offsets, counts, sched, w2_codes, w2_scales, w2_gs,
              E, I, H, y_bf16, nullptr, 0};
   return launch_status(launch_gemm_l2(a, cls, static_cast<hipStream_t>(stream)));

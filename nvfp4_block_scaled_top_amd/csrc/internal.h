@@ -95,6 +95,8 @@ struct GemmClasses {
 };
 hipError_t launch_gemm_l1(const GemmArgs& a, GemmClasses c, hipStream_t stream);
 hipError_t launch_gemm_l2(const GemmArgs& a, GemmClasses c, hipStream_t stream);
+// n floats at p set to v on the stream (graph-safe: a kernel, no memset node).
+hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream);
 
 // ---- dense layers (one group of M rows) -------------------------------------------------------
 // int32 workspace layout: counts [1], padded offsets [2], tile table [sched_len(1)], then the

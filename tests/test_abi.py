@@ -160,6 +160,19 @@ def test_gemm_rejects_bad_args(lib):
     assert l2(*p9, 8, 128, 128, 64, 0, 0, FAKE, None) == -2
     assert l2(*p9, 8, 256, 128, 64, 32, 0, FAKE, None) == -2
     assert l2(*p9, 8, 256, 128, 64, 0, 0, None, None) == -1
+    # M_cap == 0: the row arrays may be NULL, the small fixed-size ones may not
+    pl1 = [FAKE] * 10
+    pl1[0] = pl1[1] = pl1[3] = None                                         # x_codes, x_scales, row_token
+    assert l1(*pl1, 8, 256, 128, 0, 0, 0, FAKE, None, None) == -1          # h_amax still required
+    assert l1(*pl1, 8, 256, 128, 64, 0, 0, FAKE, FAKE, None) == -1         # rows present: required
+    pnull_gs = [FAKE] * 10
+    pnull_gs[2] = None                                                      # x_gs
+    assert l1(*pnull_gs, 8, 256, 128, 0, 0, 0, None, FAKE, None) == -1
+    pl2 = [FAKE] * 9
+    pl2[0] = pl2[1] = None                                                  # h_codes, h_scales
+    assert l2(*pl2, 8, 256, 128, 64, 0, 0, None, None) == -1               # rows present: required
+    pl2[2] = None                                                           # h_gs
+    assert l2(*pl2, 8, 256, 128, 0, 0, 0, None, None) == -1
 
 
 def test_combine_rejects_bad_args(lib):

@@ -5,8 +5,9 @@ Bars: bit-exact for routing tables, FP4 codes, E4M3 scales and global scales; re
 end to end.  Workloads: the tiny workload, three medium workloads that mix both tile classes with
 ragged tails, non-local ids, a zero-token expert and padding to 128 (one with hidden 2048 and
 intermediate 1024, long enough in K for the staged-scale path of the 16-row kernels), experts
-with up to 8 m-tiles of 256 rows (the large-tile kernels' tile order), and the decode workload at its full size (48 local experts of 384, hidden 7168, intermediate 2048,
-T = 1, 4, 8).
+with up to 8 m-tiles of 256 rows (the large-tile kernels' tile order), a single expert with top-1
+routing, an empty input (T = 0), and the decode workload at its full size (48 local experts of 384,
+hidden 7168, intermediate 2048, T = 1, 4, 8).
 """
 import numpy as np
 import pytest
@@ -37,6 +38,9 @@ MANY_MT = synth.Workload("many_mtiles_e4", 4, 1, 1024, 512, (4000,), 0, 4, 1, zi
 # put ~17 groups on every workgroup of the 16-row L2 kernel (the weight-scale copies of its loader
 # run ahead of the compute across group boundaries).
 SMALL_K1024 = synth.Workload("small_k1024_e4", 4, 2, 7168, 1024, (320,), 0, 4, 1)
+# The degenerate routing: one expert, top-1 (every token's weight is 1), 40 tokens in one 256-row
+# tile whose rows 40..255 are padding, no tail tiles (intermediate 128, hidden 256).
+SINGLE = synth.Workload("single_expert_top1", 1, 1, 256, 128, (40,), 0, 1, 1)
 TINY = synth.WORKLOADS[0]
 DECODE = synth.WORKLOADS[1]
 
@@ -75,8 +79,9 @@ def check_tables(L, ref):
     assert sched[1] == small.sum() and sched[2] == large.sum()
 
 
-@pytest.mark.parametrize("wl,T", [(TINY, 16), (MID, 300), (MID_PAD, 150), (MID_K, 160), (ODD_K, 8), (MANY_MT, 4000)],
-                         ids=["tiny", "mid", "mid_pad128", "mid_k2048", "odd_k640", "many_mtiles"])
+@pytest.mark.parametrize("wl,T", [(TINY, 16), (MID, 300), (MID_PAD, 150), (MID_K, 160), (ODD_K, 8), (MANY_MT, 4000),
+                                  (SINGLE, 40)],
+                         ids=["tiny", "mid", "mid_pad128", "mid_k2048", "odd_k640", "many_mtiles", "single_expert"])
 def test_layer_end_to_end_and_stages(wl, T):
     s = setup_for(wl, T)
     log(f"[run] {wl.name} T={T}: GPU layer")
@@ -113,6 +118,18 @@ def test_layer_end_to_end_and_stages(wl, T):
     assert np.isfinite(out).all() and err <= E2E_TOL and cos >= E2E_COS
     none_local = np.all(ref["token_rows"] < 0, axis=1)
     assert np.all(np_i32(L.out[:T].view(torch.int16))[none_local] == 0)
+
+
+def test_layer_empty_input():
+    """T = 0: every launch of the forward runs with no work.  The routing tables are empty, both
+    global scales are the amax-zero value 1 (oracle.global_scale), and there is no output row."""
+    s = setup_for(TINY, 0)
+    L = run_gpu(s)
+    ref = oracle_chain(s)
+    assert np.array_equal(np_i32(L.counts), ref["counts"]) and ref["counts"].sum() == 0
+    assert L.x_gs.item() == float(ref["gs_x"]) == 1.0
+    assert L.h_gs.item() == float(ref["gs_h"]) == 1.0
+    assert L.out[:0].shape[0] == 0 and ref["out"].shape[0] == 0
 
 
 @pytest.mark.parametrize("wl,T", [(TINY, 16), (MID, 300), (MID_PAD, 150), (MID_K, 160)],
