@@ -1163,18 +1163,6 @@ static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
   return hipSuccess;
 }
 
-// n floats of p set to v (a kernel rather than a memset node, so that captured graphs replay it).
-__global__ __launch_bounds__(256) void fill_f32_kernel(float* p, int n, float v) {
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = v;
-}
-
-hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  const int grid = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
-  hipLaunchKernelGGL(fill_f32_kernel, dim3(grid), dim3(256), 0, stream, p, n, v);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm_l1(const GemmArgs& a, GemmClasses c, hipStream_t stream) {
   return a.q_codes ? launch_gemm<true, true>(a, c, stream) : launch_gemm<true, false>(a, c, stream);
 }

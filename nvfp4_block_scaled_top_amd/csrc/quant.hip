@@ -134,6 +134,18 @@ hipError_t launch_quant_gs(const uint16_t* x, int64_t rows, int64_t cols, const 
   return hipGetLastError();
 }
 
+// n floats of p set to v (e.g. the L1 amax slots of an empty layer) (a kernel rather than a memset node, so that captured graphs replay it).
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* p, int n, float v) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = v;
+}
+
+hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int grid = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(grid), dim3(256), 0, stream, p, n, v);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* row_valid,
                         const float* amax_in, int32_t amax_in_count, uint8_t* codes, uint8_t* scales, float* gs,
                         float* ws, hipStream_t stream) {
