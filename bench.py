@@ -92,7 +92,7 @@ def build_weights(wl, active, copies, dev):
     return [W] + [W.clone() for _ in range(copies - 1)]
 
 
-def time_workload(wl, T, steps, warmup, copies, use_graph):
+def time_workload(wl, T, steps, warmup, copies, use_graph, fused=False):
     import torch
     from nvfp4_block_scaled_top_amd import layer, megamoe, synth
 
@@ -153,30 +153,39 @@ def time_workload(wl, T, steps, warmup, copies, use_graph):
     spread = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
               "p90": float(np.percentile(per_step, 90))}
 
-    # Calibrated variant: the global scales of x and h given (those of the warm-up forward), so
-    # neither quantizer derives one from an amax.
-    calibrated_ms = None
-    if graphs is not None:
-        gx, gh = L.x_gs.clone(), L.h_gs.clone()
-        cgraphs = []
+    # Variants of the step, each captured per weight copy and replayed like the default one:
+    # calibrated (the global scales of x and h given, those of the warm-up forward, so neither
+    # quantizer derives one from an amax) and, at decode, the fused L1 -> requantize -> L2 launch
+    # with and without calibrated scales.
+    def variant_ms(**kw):
+        vgraphs = []
         for c in range(copies):
-            L.forward(x, ids_d, wts_d, Ws[c], x_gs=gx, h_gs=gh)
+            L.forward(x, ids_d, wts_d, Ws[c], **kw)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                L.forward(x, ids_d, wts_d, Ws[c], x_gs=gx, h_gs=gh)
-            cgraphs.append(g)
-        for g in cgraphs:
+                L.forward(x, ids_d, wts_d, Ws[c], **kw)
+            vgraphs.append(g)
+        for g in vgraphs:
             g.replay()
         torch.cuda.synchronize()
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record(stream)
         for i in range(steps):
-            cgraphs[i % copies].replay()
+            vgraphs[i % copies].replay()
         c1.record(stream)
         torch.cuda.synchronize()
-        calibrated_ms = c0.elapsed_time(c1) / steps
-        del cgraphs
+        return c0.elapsed_time(c1) / steps
+
+    calibrated_ms = fused_ms = fused_calibrated_ms = None
+    if graphs is not None:
+        gx, gh = L.x_gs.clone(), L.h_gs.clone()
+        calibrated_ms = variant_ms(x_gs=gx, h_gs=gh)
+        if fused:
+            fused_ms = variant_ms(fused=True)
+            fused_calibrated_ms = variant_ms(x_gs=gx, h_gs=gh, fused=True)
+            if L.ffn_sync_error():
+                raise RuntimeError("a wait inside the fused launch expired")
 
     # Per-stage durations: a short GPU spin ahead of each stage keeps the launch latency out of
     # the event pair that brackets it.
@@ -211,7 +220,8 @@ def time_workload(wl, T, steps, warmup, copies, use_graph):
     del Ws, graphs
     torch.cuda.synchronize()
     return dict(T=T, ms_per_step=ms_per_step, wall_s=wall, stage_ms=stage_ms, spread=spread,
-                calibrated_ms=calibrated_ms, assignments=assign,
+                calibrated_ms=calibrated_ms, fused_ms=fused_ms, fused_calibrated_ms=fused_calibrated_ms,
+                assignments=assign,
                 active_experts=len(active), flops=flops, weight_bytes=wbytes, w13_bytes=w13_bytes,
                 l1_flops=4.0 * wl.hidden * wl.intermediate * assign)
 
@@ -850,7 +860,8 @@ def main():
         dec_wl = synth.WORKLOADS[1]
         for Td in dec_wl.tokens:
             log(f"[bench] decode {dec_wl.name} T={Td}")
-            d = time_workload(dec_wl, Td, args.decode_steps, args.warmup, copies=4, use_graph=not args.no_graph)
+            d = time_workload(dec_wl, Td, args.decode_steps, args.warmup, copies=4, use_graph=not args.no_graph,
+                              fused=True)
             gbs = d["weight_bytes"] / (d["ms_per_step"] * 1e-3) / 1e9
             # at decode every expert has at most 16 tokens and the layer passes T as the row bound, so
             # moe_grouped_gemm_l1_silu launches exactly one kernel, the 16-row one: the stage time is
@@ -861,6 +872,9 @@ def main():
                 "ms_per_step_p10_p50_p90": [round(d["spread"][q], 5) for q in ("p10", "p50", "p90")],
                 "gemm_ms": round(d["stage_ms"]["l1"] + d["stage_ms"]["l2"], 5), "weight_GBps": round(gbs, 1),
                 "calibrated_gs_ms_per_step": None if d["calibrated_ms"] is None else round(d["calibrated_ms"], 5),
+                "fused_ffn_ms_per_step": None if d["fused_ms"] is None else round(d["fused_ms"], 5),
+                "fused_ffn_calibrated_gs_ms_per_step": (None if d["fused_calibrated_ms"] is None
+                                                        else round(d["fused_calibrated_ms"], 5)),
                 "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "TFLOPs": round(d["flops"] / (d["ms_per_step"] * 1e-3) / 1e12, 3),
                 "active_experts": d["active_experts"], "assignments": d["assignments"],
                 "weight_bytes": d["weight_bytes"], "stage_ms": {k: round(v, 5) for k, v in d["stage_ms"].items()},
@@ -869,7 +883,10 @@ def main():
                              "traffic": recorded_traffic(f"decode_t{Td}", L1_SMALL) if Td in (4, 8) else None,
                              "kernel": L1_SMALL, "algorithmic_bytes": d["w13_bytes"]},
             }
-            log(f"[bench] decode T={Td}: {d['ms_per_step'] * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+            log(f"[bench] decode T={Td}: {d['ms_per_step'] * 1e3:.1f} us/step, {gbs:.0f} GB/s; calibrated "
+                f"{d['calibrated_ms'] * 1e3:.1f}, fused {d['fused_ms'] * 1e3:.1f}, fused calibrated "
+                f"{d['fused_calibrated_ms'] * 1e3:.1f} us/step" if d["fused_ms"] is not None else
+                f"[bench] decode T={Td}: {d['ms_per_step'] * 1e3:.1f} us/step, {gbs:.0f} GB/s")
 
     prefill_configs = None
     if not args.quick:

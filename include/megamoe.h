@@ -65,6 +65,9 @@ extern "C" {
 /* Slots of the per-workgroup h amax written by moe_grouped_gemm_l1_silu (every slot, every call). */
 #define MEGAMOE_L1_AMAX_PARTS 1280
 
+/* Index of the error word in the sync workspace of moe_grouped_ffn_fused (uint32 words). */
+#define MEGAMOE_FFN_SYNC_ERROR_WORD 352
+
 /* ------------------------------------------------------------------------------------------
  * Host-side size helpers (no HIP calls; usable without a GPU).
  * ---------------------------------------------------------------------------------------- */
@@ -85,6 +88,10 @@ size_t megamoe_quant_workspace_bytes(int64_t rows, int64_t cols);
 /* Scratch bytes nvfp4_linear and nvfp4_linear_gate_up_silu need for M rows (0 if M is out of
  * range). */
 size_t megamoe_dense_workspace_bytes(int64_t M);
+
+/* Bytes of the sync workspace of moe_grouped_ffn_fused for num_experts experts (0 if out of
+ * range). */
+size_t megamoe_ffn_sync_bytes(int32_t num_experts);
 
 /* ------------------------------------------------------------------------------------------
  * moe_router_topk - router logits -> top-k expert ids and weights.
@@ -340,6 +347,56 @@ int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, con
                             const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
                             int32_t E, int32_t H, int32_t I, int64_t M_cap, int32_t block_m_override,
                             int32_t max_rows_per_expert, void* y_bf16, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_grouped_ffn_fused - L1 gate+up with SiLU(gate)*up, the requantization of h and L2 down in
+ * one persistent launch (experts taken in 16-row m-tiles: decode sizes).
+ *
+ * The layer's L1, requantize and L2 steps (CURRENT_BUG.md@2e65594, "Test Plan" Phase 1), with
+ * persistent scheduling across expert groups ("Architecture: DeepSeek-V4 MegaMoE"), as one
+ * launch instead of two or three, to cut the kernel boundaries of a decode step.  The global scale
+ * of h is either calibrated (CURRENT_BUG.md@2fc81cc, "What we've tried": a scale from a warm-up
+ * pass; h is then quantized in the L1 epilogue and an expert's L2 starts as soon as its own L1 is
+ * done) or the per-tensor amax scale of nvfp4_quantize_act (every L1 group must finish before h
+ * is quantized: a wait across the whole launch).  Work is claimed in order from a counter per XCD,
+ * so the launch never depends on all workgroups being resident at once.
+ *
+ * Results, bit for bit, are those of moe_grouped_gemm_l1_silu (or _nvfp4 with h_gs_in), then
+ * nvfp4_quantize_act of h with row_valid = row_token and amax_in = h_amax_parts (not with
+ * h_gs_in), then moe_grouped_gemm_l2, when those run every expert in 16-row m-tiles (as they do
+ * when every expert has at most 16 rows, or with block_m_override 16).  Any routing is accepted;
+ * experts with more rows are covered in 16-row m-tiles too (correct, but slow beyond decode).
+ *
+ * x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_*   as for
+ *              moe_grouped_gemm_l1_silu.      w2_*   as for moe_grouped_gemm_l2.
+ * E, H, I, M_cap   as for the grouped GEMMs.
+ * h_gs_in      NULL: the global scale of h is derived from its amax and written to h_gs_out [1];
+ *              h_bf16 (bf16 [M_cap, I]) receives the unquantized h.  Non-NULL (float [1] on the
+ *              device): a calibrated scale; h_gs_out and h_bf16 are then not used and may be NULL.
+ * h_amax_parts float [MEGAMOE_L1_AMAX_PARTS]: as written by moe_grouped_gemm_l1_silu (every slot,
+ *              max over them = max |h| over the valid rows).
+ * h_codes, h_scales   uint8 [M_cap, I/2], [M_cap, I/16]: NVFP4 h.  Without h_gs_in, rows holding
+ *              no assignment are set to zero; with h_gs_in they are not written.
+ * y_bf16       bf16 [M_cap, H]; rows holding no assignment are not written.
+ * sync         device memory of at least megamoe_ffn_sync_bytes(E) bytes, all zero before the
+ *              first call (e.g. from a zeroing allocation).  Every call leaves its counters at zero
+ *              again.  Word MEGAMOE_FFN_SYNC_ERROR_WORD becomes non-zero, and stays so, if a wait
+ *              inside the launch ever expired (about 0.25 s): results of that call are undefined.
+ *              Calls that share one sync buffer must not overlap in time (one stream).
+ * With M_cap == 0 nothing is computed: the call only sets every slot of h_amax_parts to 0 and,
+ * without h_gs_in, writes 1.0 to h_gs_out.
+ * Errors: MEGAMOE_ERR_SHAPE as for the grouped GEMMs; MEGAMOE_ERR_NULL for a missing pointer;
+ * MEGAMOE_ERR_WORKSPACE if sync_bytes is too small.
+ * ---------------------------------------------------------------------------------------- */
+int32_t moe_grouped_ffn_fused(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                              const int32_t* row_token, const int32_t* padded_offsets,
+                              const int32_t* counts, const int32_t* sched, const uint8_t* w13_codes,
+                              const uint8_t* w13_scales, const float* w13_gs, const uint8_t* w2_codes,
+                              const uint8_t* w2_scales, const float* w2_gs, int32_t E, int32_t H,
+                              int32_t I, int64_t M_cap, const float* h_gs_in, void* h_bf16,
+                              float* h_amax_parts, uint8_t* h_codes, uint8_t* h_scales,
+                              float* h_gs_out, void* y_bf16, void* sync, size_t sync_bytes,
+                              void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * nvfp4_linear - dense NVFP4 linear layer: the L2 GEMM with one group holding every row.

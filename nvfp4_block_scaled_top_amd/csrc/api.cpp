@@ -336,6 +336,54 @@ int32_t moe_combine_shared(const void* y_bf16, const int32_t* token_rows, const 
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t megamoe_ffn_sync_bytes(int32_t num_experts) {
+  if (num_experts < 1 || num_experts > MEGAMOE_MAX_EXPERTS) return 0;
+  return (size_t)(kFfnSyncHeader + (int64_t)num_experts * kFfnSyncStride) * sizeof(uint32_t);
+}
+
+int32_t moe_grouped_ffn_fused(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                              const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
+                              const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                              const float* w13_gs, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                              const float* w2_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap,
+                              const float* h_gs_in, void* h_bf16, float* h_amax_parts, uint8_t* h_codes,
+                              uint8_t* h_scales, float* h_gs_out, void* y_bf16, void* sync, size_t sync_bytes,
+                              void* stream) {
+  if (!gemm_shape_ok(E, H, I, M_cap)) return MEGAMOE_ERR_SHAPE;
+  if (!x_gs || !padded_offsets || !counts || !sched || !w13_codes || !w13_scales || !w13_gs || !w2_codes ||
+      !w2_scales || !w2_gs || !h_amax_parts || !sync)
+    return MEGAMOE_ERR_NULL;
+  if (!h_gs_in && !h_gs_out) return MEGAMOE_ERR_NULL;
+  if (M_cap > 0 && (!x_codes || !x_scales || !row_token || !h_codes || !h_scales || !y_bf16)) return MEGAMOE_ERR_NULL;
+  if (M_cap > 0 && !h_gs_in && !h_bf16) return MEGAMOE_ERR_NULL;
+  if (sync_bytes < megamoe_ffn_sync_bytes(E)) return MEGAMOE_ERR_WORKSPACE;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M_cap == 0) {  // no rows: the amax slots (all 0) and, without a calibrated scale, gs_h = 1
+    const int32_t r = launch_status(launch_fill_f32(h_amax_parts, MEGAMOE_L1_AMAX_PARTS, 0.0f, s));
+    if (r != MEGAMOE_OK || h_gs_in) return r;
+    return launch_status(launch_fill_f32(h_gs_out, 1, 1.0f, s));
+  }
+  FfnArgs a{};
+  a.l1 = GemmArgs{x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
+                  E, H, I, h_gs_in ? nullptr : h_bf16, h_amax_parts, 0};
+  if (h_gs_in) {
+    a.l1.q_gs = h_gs_in;
+    a.l1.q_codes = h_codes;
+    a.l1.q_scales = h_scales;
+  }
+  a.l2 = GemmArgs{h_codes, h_scales, h_gs_in ? h_gs_in : h_gs_out, nullptr, padded_offsets, counts, sched, w2_codes,
+                  w2_scales, w2_gs, E, I, H, y_bf16, nullptr, 0};
+  a.sync = static_cast<uint32_t*>(sync);
+  a.row_valid = row_token;
+  a.M_cap = M_cap;
+  a.hq_codes = h_codes;
+  a.hq_scales = h_scales;
+  a.h_gs = h_gs_out;
+  return launch_status(launch_ffn_small(a, s));
+}
+
 size_t megamoe_dense_workspace_bytes(int64_t M) {
   if (M < 0 || M >= ((int64_t)1 << 31)) return 0;
   return (size_t)(kDenseHeader + M) * sizeof(int32_t);

@@ -26,6 +26,8 @@
 // code bytes of its row (elements chunk + (CH/4)*(l/16) ..) and feeds element group st of them to
 // MFMA step st (instead of the MFMA's natural 8*(l/16) within each 32-K step).  A and B use the
 // same permutation, so each dot product is unchanged; it lets a lane read contiguous bytes.
+#include <atomic>
+
 #include "device_common.h"
 #include "internal.h"
 #include "quant_device.h"
@@ -248,74 +250,154 @@ struct BoolTag {
 // then.  Every wave has issued at least kSDepth steps of loads after its copy of group q+1 when
 // group q ends, so vmcnt <= kSDepth * (loads per step) there (before the group's barrier) means the
 // copy has landed.
-template <bool kL1, int CH, bool kStaged, bool kQOut>
-__global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArgs p) {
+// LDS of the small class, owned by the kernels and handed to the passes: the per-expert tables
+// (dynamic LDS, identical for L1 and L2 since both walk the routing step's m-tiles) and the
+// group-end reduction buffers.
+template <int NB>
+struct SmallLds {
+  int* pref;     // [E+1] exclusive prefix of regular small m-tiles
+  int* poff;     // [E] first padded row
+  int* cnt;      // [E] tokens
+  int* tiny;     // experts whose one m-tile is tiny
+  int* ntiny;    // [1] their number
+  uint8_t* scl;  // [3][scale buffer] if staged
+  f32x4 (*red)[kSWaves][NB][kWave];  // [2] partial blocks at a group end (by group parity)
+  f16x8 (*afrag)[kWave];             // [kSWaves] tiny phase: the chunk's decoded A pieces
+};
+
+// Device-scope (every XCD) accesses.  The fused kernel below hands h from the workgroups that
+// compute it to those that read it within one launch; the 8 XCDs' L2 caches are not coherent with
+// each other, so those stores and loads are relaxed atomics at agent scope (gfx950: the sc1 bit;
+// no cache-wide write-back or invalidate).
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev_u16(const uint8_t* p) {
+  return __hip_atomic_load(reinterpret_cast<const uint16_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev_u8(const uint8_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4 ld_dev_x4(const uint8_t* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until the device-scope counter *c reaches target (wave-uniform; every lane of the wave
+// calls it).  Bounded: after about a quarter of a second it sets *err and returns, so a broken
+// dependency shows as an error word instead of a hang.
+constexpr int kSpinLimit = 1 << 18;
+__device__ __forceinline__ void wait_count(const uint32_t* c, uint32_t target, uint32_t* err) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    if (__builtin_amdgcn_readfirstlane(ld_dev(c)) >= target) return;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  st_dev(err, 1u);
+}
+
+// The part of one phase's group list that work item `part` of `nparts` takes.
+__device__ __forceinline__ void phase_part(int64_t part, int64_t nparts, int64_t groups, int64_t& begin,
+                                           int64_t& end) {
+  begin = part * groups / nparts;
+  end = (part + 1) * groups / nparts;
+}
+
+// Fills the per-expert tables from the routing step's table and inv[e] = 1 / (gs_a * gs_w[e]) for
+// the experts with small m-tiles (and inv2 likewise with gs_a2 and w_gs2 when inv2 is given).
+// Small m-tiles are split into tiny ones (the expert's only m-tile, at most 512/CH rows) and
+// regular ones.  Ends with a workgroup barrier.
+template <int CH, int NB>
+__device__ __forceinline__ void small_tables(const GemmArgs& p, const SmallLds<NB>& L, float* inv, float gs_a,
+                                             float* inv2 = nullptr, float gs_a2 = 0.0f,
+                                             const float* w_gs2 = nullptr) {
+  constexpr int kTinyRows = kWave / (CH / 8);
+  const int E = p.E;
+  const int32_t* __restrict__ pref = p.sched + sched_pref_small(E);
+  const int32_t* __restrict__ bm = p.sched + sched_block_m(E);
+  for (int j = threadIdx.x; j < E; j += blockDim.x) {
+    const int cnt = p.counts[j];
+    L.poff[j] = p.padded_offsets[j];
+    L.cnt[j] = cnt;
+    // small m-tiles of expert j (scanned below); when the 256-row kernel is not launched, an
+    // expert the routing step gave 256-row tiles is covered here in 16-row m-tiles
+    int nt = pref[j + 1] - pref[j];
+    if (p.small_covers_large && bm[j] == kBlockMLarge) nt = (cnt + kBlockMSmall - 1) / kBlockMSmall;
+    L.pref[j] = nt;
+    inv[j] = nt > 0 ? (float)(1.0 / ((double)gs_a * (double)p.w_gs[j])) : 0.0f;
+    if (inv2) inv2[j] = nt > 0 ? (float)(1.0 / ((double)gs_a2 * (double)w_gs2[j])) : 0.0f;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {  // wave 0: split the small m-tiles into tiny and regular
+    const int lane = lane_id();
+    int reg_carry = 0, tiny_carry = 0;
+    for (int c = 0; c < E; c += kWave) {
+      const int e = c + lane;
+      const int nt = e < E ? L.pref[e] : 0;
+      const int cnt = e < E ? L.cnt[e] : 0;
+      const bool tiny = nt == 1 && cnt <= kTinyRows;
+      const int reg = tiny ? 0 : nt;
+      int incl = reg;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+      }
+      const uint64_t mask = __ballot(tiny);
+      const int tpos = tiny_carry + __popcll(mask & ((1ull << lane) - 1));
+      if (e < E) L.pref[e] = reg_carry + incl - reg;
+      if (tiny) L.tiny[tpos] = e;
+      reg_carry += __shfl(incl, kWave - 1, kWave);
+      tiny_carry += __popcll(mask);
+    }
+    if (lane == 0) {
+      L.pref[E] = reg_carry;
+      *L.ntiny = tiny_carry;
+    }
+  }
+  __syncthreads();
+}
+
+// What the fused kernel adds to a pass.  L2 (ready != NULL): before a group's A rows (h) are
+// loaded, wait until the L1 groups of its expert are done (ready[e * kSyncStride] counts them;
+// gm1 L1 groups per m-tile).  kDev: h is read (L2) or written (L1) with device-scope accesses.
+constexpr int kSyncStride = kFfnSyncStride;  // words between per-expert counters (a 128-byte line)
+struct SmallSync {
+  const uint32_t* ready = nullptr;
+  int gm1 = 0;
+  uint32_t* err = nullptr;
+};
+
+// One pass of the small class over part `part` of `nparts` of its group lists (tiny m-tiles,
+// then regular ones), for one workgroup.  inv: the pass's 1 / (gs_a * gs_w[e]).
+template <bool kL1, int CH, bool kStaged, bool kQOut, bool kDev>
+__device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<small_nb<kL1>()>& L, const float* inv,
+                                           int64_t part, int64_t nparts, uint32_t& amax_bits, int& parity,
+                                           const SmallSync& sync) {
   static_assert(!kStaged || CH == 256, "staged scales copy whole 16-byte pieces: one per 256-element chunk");
   constexpr int kSNb = small_nb<kL1>();
   constexpr int kQ = CH / 128;
   constexpr int kLaneBytes = CH / 8, kLaneScales = CH / 64;
   constexpr int kPieces = CH / 8;               // 8-element pieces per row and chunk
   constexpr int kTinyRows = kWave / kPieces;    // rows of a dense A chunk (2 or 4)
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
-  __shared__ f32x4 s_red[2][kSWaves][kSNb][kWave];
-  __shared__ f16x8 s_afrag[kSWaves][kWave];  // tiny phase: this chunk's decoded A pieces
-  __shared__ uint32_t s_amax[kSWaves];
-  __shared__ int s_ntiny;
+  constexpr bool kDevA = kDev && !kL1;          // A (h) written by other workgroups of this launch
+  constexpr bool kDevOut = kDev && kL1;         // h read by other workgroups of this launch
   const int E = p.E;
-  // Per-expert tables (LDS; reading them inside the loop must not wait on the weight stream):
-  int* s_pref = reinterpret_cast<int*>(s_dyn);  // [E+1] exclusive prefix of regular small m-tiles
-  int* s_poff = s_pref + E + 1;                 // [E] first padded row
-  int* s_cnt = s_poff + E;                      // [E] tokens
-  float* s_inv = reinterpret_cast<float*>(s_cnt + E);  // [E] 1 / (gs_a * gs_w[e])
-  int* s_tiny = reinterpret_cast<int*>(s_inv + E);    // experts whose one m-tile is tiny
-  uint8_t* s_scl = s_dyn + small_table_bytes(E);      // [3][scale buffer] if kStaged
-  const float gs_a = *p.a_gs;
+  const int* s_pref = L.pref;
+  const int* s_poff = L.poff;
+  const int* s_cnt = L.cnt;
+  const int* s_tiny = L.tiny;
+  uint8_t* s_scl = L.scl;
   constexpr bool quant_out = kL1 && kQOut;  // L1: NVFP4 h (q_codes, q_scales) instead of bf16 h
   const float gs_q = quant_out ? *p.q_gs : 1.0f;
-  {
-    const int32_t* __restrict__ pref = p.sched + sched_pref_small(E);
-    const int32_t* __restrict__ bm = p.sched + sched_block_m(E);
-    for (int j = threadIdx.x; j < E; j += blockDim.x) {
-      const int cnt = p.counts[j];
-      s_poff[j] = p.padded_offsets[j];
-      s_cnt[j] = cnt;
-      // small m-tiles of expert j (scanned below); when the 256-row kernel is not launched, an
-      // expert the routing step gave 256-row tiles is covered here in 16-row m-tiles
-      int nt = pref[j + 1] - pref[j];
-      if (p.small_covers_large && bm[j] == kBlockMLarge) nt = (cnt + kBlockMSmall - 1) / kBlockMSmall;
-      s_pref[j] = nt;
-      s_inv[j] = nt > 0 ? (float)(1.0 / ((double)gs_a * (double)p.w_gs[j])) : 0.0f;
-    }
-    __syncthreads();
-    if (threadIdx.x < kWave) {  // wave 0: split the small m-tiles into tiny and regular
-      const int lane = lane_id();
-      int reg_carry = 0, tiny_carry = 0;
-      for (int c = 0; c < E; c += kWave) {
-        const int e = c + lane;
-        const int nt = e < E ? s_pref[e] : 0;
-        const int cnt = e < E ? s_cnt[e] : 0;
-        const bool tiny = nt == 1 && cnt <= kTinyRows;
-        const int reg = tiny ? 0 : nt;
-        int incl = reg;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int t = __shfl_up(incl, o, kWave);
-          if (lane >= o) incl += t;
-        }
-        const uint64_t mask = __ballot(tiny);
-        const int tpos = tiny_carry + __popcll(mask & ((1ull << lane) - 1));
-        if (e < E) s_pref[e] = reg_carry + incl - reg;
-        if (tiny) s_tiny[tpos] = e;
-        reg_carry += __shfl(incl, kWave - 1, kWave);
-        tiny_carry += __popcll(mask);
-      }
-      if (lane == 0) {
-        s_pref[E] = reg_carry;
-        s_ntiny = tiny_carry;
-      }
-    }
-    __syncthreads();
-  }
   const int NU = p.N;  // units per m-tile: L1 h columns (I), L2 output columns (H)
   constexpr int GU = small_group_units<kL1>();
   const int Gm = (NU + GU - 1) / GU;  // groups per m-tile
@@ -326,15 +408,6 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
   const int nch = K / CH;
   const int ks = nch < kSWaves ? nch : kSWaves;  // waves sharing K (all 4 unless K < 4 chunks)
   const int c0 = wave < ks ? wave * nch / ks : 0, c1 = wave < ks ? (wave + 1) * nch / ks : 0;
-  uint32_t amax_bits = 0;
-  int parity = 0;  // s_red buffer of the next group end (continues across phases)
-
-  // This workgroup's position: workgroup b runs on XCD b % 8; the kSOcc workgroups of a CU (XCD-
-  // local indices i and i + 256/8) get neighbouring positions.
-  const int G = kSmallGrid, b = blockIdx.x;
-  constexpr int kPerXcd = kSmallGrid / kXcds, kCusPerXcd = kPerXcd / kSOcc;
-  const int xi = b / kXcds;
-  const int64_t lb = (int64_t)(b % kXcds) * kPerXcd + (xi % kCusPerXcd) * kSOcc + xi / kCusPerXcd;
 
   // Staged scales: buffer geometry (pieces of 16 bytes; P per padded row).
   const int P = Ks / 16 + 1, SRB = 16 * P;
@@ -346,10 +419,11 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
   auto run_phase = [&](auto tiny_tag) {
     constexpr bool kTiny = decltype(tiny_tag)::value;
     using Slot = SmallSlot<CH, kSNb, kTiny>;
-    constexpr int kLoadsPerStep = (kTiny ? 2 : kQ + 1) + kSNb * kQ + (kStaged ? 0 : kSNb);
-    const int nm = kTiny ? s_ntiny : s_pref[E];
-    const int64_t Gt = (int64_t)nm * Gm;
-    const int64_t g_begin = lb * Gt / G, g_end = (lb + 1) * Gt / G;
+    constexpr int kLoadsPerStep =
+        (kTiny ? 2 : (kDevA ? 2 * kQ : kQ) + 1) + kSNb * kQ + (kStaged ? 0 : kSNb);
+    const int nm = kTiny ? *L.ntiny : s_pref[E];
+    int64_t g_begin, g_end;
+    phase_part(part, nparts, (int64_t)nm * Gm, g_begin, g_end);
     const int ngroups = (int)(g_end - g_begin);
     if (ngroups == 0) return;
 
@@ -387,8 +461,8 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
     // End of a group: publish the partial blocks; after the barrier wave w adds accumulator row
     // w of every block in wave order and writes it out.
     auto group_epilogue = [&](const SmallGroup& cg) {
-      const float inv = s_inv[cg.e];
-      const float* red = reinterpret_cast<const float*>(&s_red[parity][0][0][0]);
+      const float invg = inv[cg.e];
+      const float* red = reinterpret_cast<const float*>(&L.red[parity][0][0][0]);
       uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
       const int row = 4 * g + wave;  // MFMA output row of accumulator element `wave`
       uint32_t hq[kSNb];             // L1: bf16 h of column 8j + r16 (lanes r16 < 8)
@@ -399,17 +473,21 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
         if (kL1) {
           const float up_raw = __shfl(r, lane + 8, kWave);  // column c+8 holds the up row of c
           const int hc = 8 * j + r16;
-          const uint32_t hb = f32_to_bf16_bits(silu_f32(r * inv) * (up_raw * inv));
+          const uint32_t hb = f32_to_bf16_bits(silu_f32(r * invg) * (up_raw * invg));
           hq[j] = hb;
           if (r16 < 8 && hc < cg.n && row < cg.rows_left) {
-            if (!quant_out) out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + hc] = (uint16_t)hb;
+            if (!quant_out) {
+              uint16_t* dst = out + (int64_t)(cg.row0 + row) * p.N + cg.j0 + hc;
+              if (kDevOut) st_dev(dst, (uint16_t)hb);
+              else *dst = (uint16_t)hb;
+            }
             const uint32_t mag = hb & 0x7FFFu;
             amax_bits = amax_bits > mag ? amax_bits : mag;
           }
         } else {
           const int rc = 16 * j + r16;
           if (rc < cg.n && row < cg.rows_left)
-            out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + rc] = (uint16_t)f32_to_bf16_bits(r * inv);
+            out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + rc] = (uint16_t)f32_to_bf16_bits(r * invg);
         }
       }
       if constexpr (quant_out) {
@@ -440,8 +518,15 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
                                 (((p3 >> 8) & 0xFFu) << 24);
             const int64_t orow = cg.row0 + row;
             const int col = cg.j0 + 16 * b;
-            *reinterpret_cast<u32x2*>(p.q_codes + orow * (p.N / 2) + col / 2) = u32x2{lo, hi};
-            p.q_scales[orow * (p.N / 16) + col / 16] = (uint8_t)sc;
+            uint8_t* cdst = p.q_codes + orow * (p.N / 2) + col / 2;
+            uint8_t* sdst = p.q_scales + orow * (p.N / 16) + col / 16;
+            if (kDevOut) {
+              st_dev(reinterpret_cast<uint64_t*>(cdst), (uint64_t)lo | ((uint64_t)hi << 32));
+              st_dev(sdst, (uint8_t)sc);
+            } else {
+              *reinterpret_cast<u32x2*>(cdst) = u32x2{lo, hi};
+              *sdst = (uint8_t)sc;
+            }
           }
         }
       }
@@ -465,6 +550,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
     // never consumed), so every step issues the same loads.
     Cursor lcur = cursor_at(g_begin);
     int lgrp = 0, lc = c0;
+    int ready_e = -1;  // fused L2: the last expert whose h is known to be complete
     const uint8_t* la_c = p.a_codes;
     const uint8_t* la_s = p.a_scales;
     const uint8_t* lb_c[kSNb];
@@ -498,6 +584,12 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
       const SmallGroup q = group_of(lcur);
       if (kStaged) stage_scales(q, lgrp % 3);
       ++lgrp;
+      if (kDevA && sync.ready != nullptr && q.e != ready_e) {
+        // the h rows of this expert are written by the L1 groups of its m-tiles
+        const int nmt = kTiny ? 1 : s_pref[q.e + 1] - s_pref[q.e];
+        wait_count(sync.ready + q.e * kSyncStride, (uint32_t)(sync.gm1 * nmt), sync.err);
+        ready_e = q.e;
+      }
       if (kTiny) {
         // dense A: lane -> (row lane / kPieces, piece lane % kPieces); rows past the m-tile read
         // row 0
@@ -552,17 +644,24 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
     };
     loader_enter();
     auto load_scale = [](const uint8_t* q) -> uint32_t {
+      if (kDevA) return kLaneScales == 4 ? ld_dev(reinterpret_cast<const uint32_t*>(q)) : ld_dev_u16(q);
       if (kLaneScales == 4) return *reinterpret_cast<const uint32_t*>(q);
       return *reinterpret_cast<const uint16_t*>(q);
     };
     auto load = [&](Slot& d) {
       const int64_t off = (int64_t)lc * (CH / 2), soff = (int64_t)lc * (CH / 16);
       if (kTiny) {
-        d.a[0].x = *reinterpret_cast<const uint32_t*>(la_c + off);
-        d.as = *(la_s + soff);
+        if (kDevA) {
+          d.a[0].x = ld_dev(reinterpret_cast<const uint32_t*>(la_c + off));
+          d.as = ld_dev_u8(la_s + soff);
+        } else {
+          d.a[0].x = *reinterpret_cast<const uint32_t*>(la_c + off);
+          d.as = *(la_s + soff);
+        }
       } else {
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) d.a[q] = *reinterpret_cast<const u32x4*>(la_c + off + 16 * q);
+        for (int q = 0; q < kQ; ++q)
+          d.a[q] = kDevA ? ld_dev_x4(la_c + off + 16 * q) : *reinterpret_cast<const u32x4*>(la_c + off + 16 * q);
         d.as = load_scale(la_s + soff);
       }
 #pragma unroll
@@ -612,11 +711,11 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
 #pragma unroll
         for (int j = 0; j < kSNb; ++j) sb[j][q] = e4m3x2_to_f16(bsw[j], q == 1);
       if (kTiny) {
-        s_afrag[wave][lane] = decode8(d.a[0].x, bcast_lo(e4m3x2_to_f16(d.as, false)));
+        L.afrag[wave][lane] = decode8(d.a[0].x, bcast_lo(e4m3x2_to_f16(d.as, false)));
 #pragma unroll
         for (int st = 0; st < CH / 32; ++st) {
           const int q = st / 4, w4 = st % 4;
-          const f16x8 a = s_afrag[wave][tsrc + st];
+          const f16x8 a = L.afrag[wave][tsrc + st];
 #pragma unroll
           for (int j = 0; j < kSNb; ++j) {
             const f16x8 w = decode8(d.b[j][q][w4], w4 < 2 ? bcast_lo(sb[j][q]) : bcast_hi(sb[j][q]));
@@ -645,7 +744,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
     auto group_end = [&](bool tail) {
 #pragma unroll
       for (int j = 0; j < kSNb; ++j) {
-        s_red[parity][wave][j][lane] = acc[j];
+        L.red[parity][wave][j][lane] = acc[j];
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       if (kStaged) {
@@ -700,8 +799,43 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
 
   run_phase(BoolTag<true>{});
   run_phase(BoolTag<false>{});
+}
+
+template <bool kL1, int CH, bool kStaged, bool kQOut>
+__global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArgs p) {
+  constexpr int kSNb = small_nb<kL1>();
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+  __shared__ f32x4 s_red[2][kSWaves][kSNb][kWave];
+  __shared__ f16x8 s_afrag[kSWaves][kWave];  // tiny phase: this chunk's decoded A pieces
+  __shared__ uint32_t s_amax[kSWaves];
+  __shared__ int s_ntiny;
+  const int E = p.E;
+  // Per-expert tables (LDS; reading them inside the loop must not wait on the weight stream).
+  SmallLds<kSNb> L;
+  L.pref = reinterpret_cast<int*>(s_dyn);
+  L.poff = L.pref + E + 1;
+  L.cnt = L.poff + E;
+  float* s_inv = reinterpret_cast<float*>(L.cnt + E);  // [E] 1 / (gs_a * gs_w[e])
+  L.tiny = reinterpret_cast<int*>(s_inv + E);
+  L.ntiny = &s_ntiny;
+  L.scl = s_dyn + small_table_bytes(E);
+  L.red = s_red;
+  L.afrag = s_afrag;
+  small_tables<CH>(p, L, s_inv, *p.a_gs);
+
+  // This workgroup's position: workgroup b runs on XCD b % 8; the kSOcc workgroups of a CU (XCD-
+  // local indices i and i + 256/8) get neighbouring positions.
+  const int G = kSmallGrid, b = blockIdx.x;
+  constexpr int kPerXcd = kSmallGrid / kXcds, kCusPerXcd = kPerXcd / kSOcc;
+  const int xi = b / kXcds;
+  const int64_t lb = (int64_t)(b % kXcds) * kPerXcd + (xi % kCusPerXcd) * kSOcc + xi / kCusPerXcd;
+
+  uint32_t amax_bits = 0;
+  int parity = 0;  // s_red buffer of the next group end (continues across phases)
+  small_pass<kL1, CH, kStaged, kQOut, false>(p, L, s_inv, lb, G, amax_bits, parity, SmallSync{});
 
   if (kL1) {
+    const int wave = threadIdx.x / kWave, lane = lane_id();
     amax_bits = wave_max_u32(amax_bits);
     if (lane == 0) s_amax[wave] = amax_bits;
     __syncthreads();
@@ -712,6 +846,216 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
       for (int j = b + G; j < kAmaxSmallSlots; j += G) p.amax_out[kLargeGrid + j] = 0.0f;
       if (p.clear_other)
         for (int j = b; j < kLargeGrid; j += G) p.amax_out[j] = 0.0f;
+    }
+  }
+}
+
+// ============================================================================================
+// L1 -> requantization of h -> L2 of the small class in one persistent launch (decode).
+//
+// The layer's S3, S4 and S5 (CURRENT_BUG.md@2e65594, "Test Plan" Phase 1) as one kernel, so that a
+// decode step pays one kernel boundary fewer with a calibrated global scale for h (S4 is then the
+// L1 epilogue) and two fewer without.  Work items, taken in order from a device-scope ticket
+// counter of the workgroup's XCD (each XCD takes a contiguous eighth of every kind of item):
+//  1. the L1 parts: the group lists of gemm_small_kernel cut into at most 512 parts, computed by
+//     the same pass (same groups, same K split and reduction order: bit-identical results);
+//  2. without a calibrated scale, the quantization parts of h: the global scale of h needs the
+//     amax of all of h, so they wait until every L1 part is done (the method's grid-wide barrier)
+//     and then quantize a share of h's rows each, as nvfp4_quantize_act does;
+//  3. the L2 parts.  With a calibrated scale a group waits only until the L1 groups of its expert
+//     are done (per-expert counters); otherwise until every quantization part is done.
+// A workgroup claims an item only while it runs, and only after finishing the previous one; an item
+// waits only for L1 (or quantization) items.  A workgroup of XCD x waits only once every L1 item
+// of x is claimed, by a running workgroup that will finish it without waiting, and the slots of XCD
+// y can hold only y's workgroups, which take y's L1 items before anything else: the launch needs no
+// co-residency (no cooperative launch) and cannot deadlock, as long as every XCD receives
+// workgroups (512 of them over the 8 XCDs of the GPU).  Claiming the next item while computing the
+// current one was slower: the items are as large as a workgroup's share of a GEMM, and workgroups
+// that started first took a second one.  h and the amax slots go from workgroup to
+// workgroup through device-scope stores and loads, after which the counters are incremented; the
+// waits are bounded (an expired wait sets the error word).  The sync words start at zero and the
+// last workgroup to leave sets them back to zero, so replays of a captured graph need no reset.
+// ============================================================================================
+// Sync words: the ticket counter of XCD x at 32x (x < 8), then the exit, L1-done and
+// quantization-done counters and the error word, each on a 128-byte line of its own; per-expert
+// counters from kSyncHeader on.
+constexpr int kSyncExit = 256, kSyncL1 = 288, kSyncQ = 320, kSyncHeader = kFfnSyncHeader;
+constexpr int kFfnQuantBlocks = 256;  // 16-element blocks of h per quantization part (one per thread)
+constexpr int kFfnMaxQuantParts = 512;
+static_assert(MEGAMOE_FFN_SYNC_ERROR_WORD == 352 && kSyncHeader >= 384, "sync word layout");
+
+// Bytes of the fused kernel's per-expert tables: those of the small class plus the L2 inv.
+__host__ __device__ inline size_t ffn_table_bytes(int E) { return (((size_t)6 * E + 1) * 4 + 15) / 16 * 16; }
+
+template <int CH, bool kStaged, bool kCal>
+__global__ __launch_bounds__(kGemmThreads, kSOcc) void ffn_small_kernel(FfnArgs a) {
+  constexpr int kSNb = small_nb<true>();
+  static_assert(small_nb<false>() == kSNb, "the two passes share the reduction buffers");
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+  __shared__ f32x4 s_red[2][kSWaves][kSNb][kWave];
+  __shared__ f16x8 s_afrag[kSWaves][kWave];
+  __shared__ uint32_t s_amax[kSWaves];
+  __shared__ int s_ntiny;
+  __shared__ uint32_t s_ticket;
+  uint32_t* const sync = a.sync;
+  uint32_t* const err = sync + MEGAMOE_FFN_SYNC_ERROR_WORD;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  // This workgroup's XCD (hardware register XCC_ID), among the nxcd of the device.
+  const int xcd = (int)((__builtin_amdgcn_s_getreg((31 << 11) | 20) & 0xFu) % (uint32_t)a.nxcd);
+  uint32_t* const ticket = sync + 32 * xcd;
+  uint32_t t_next = 0;
+  if (threadIdx.x == 0) t_next = add_dev(ticket, 1u);  // the first claim, while the tables load
+  const GemmArgs& p1 = a.l1;
+  const GemmArgs& p2 = a.l2;
+  const int E = p1.E;
+  SmallLds<kSNb> L;
+  L.pref = reinterpret_cast<int*>(s_dyn);
+  L.poff = L.pref + E + 1;
+  L.cnt = L.poff + E;
+  float* inv1 = reinterpret_cast<float*>(L.cnt + E);
+  L.tiny = reinterpret_cast<int*>(inv1 + E);
+  float* inv2 = reinterpret_cast<float*>(L.tiny + E);
+  L.ntiny = &s_ntiny;
+  L.scl = s_dyn + ffn_table_bytes(E);
+  L.red = s_red;
+  L.afrag = s_afrag;
+  if (kCal) small_tables<CH>(p1, L, inv1, *p1.a_gs, inv2, *p2.a_gs, p2.w_gs);
+  else small_tables<CH>(p1, L, inv1, *p1.a_gs);
+
+  // Item counts (every workgroup derives the same from the same tables).
+  const int mtiles = s_ntiny + L.pref[E];
+  const int gm1 = (p1.N + small_group_units<true>() - 1) / small_group_units<true>();
+  const int gm2 = (p2.N + small_group_units<false>() - 1) / small_group_units<false>();
+  const int64_t n1 = (int64_t)mtiles * gm1 < kSmallGrid ? (int64_t)mtiles * gm1 : kSmallGrid;
+  const int64_t n2 = (int64_t)mtiles * gm2 < kSmallGrid ? (int64_t)mtiles * gm2 : kSmallGrid;
+  const int64_t qblocks = a.M_cap * (p1.N / 16);
+  int64_t nq = 0;
+  if (!kCal) {
+    nq = (qblocks + kFfnQuantBlocks - 1) / kFfnQuantBlocks;
+    if (nq > kFfnMaxQuantParts) nq = kFfnMaxQuantParts;
+  }
+  // this XCD's share of each kind of item
+  const int nx = a.nxcd;
+  const int64_t b1 = n1 * xcd / nx, c1 = n1 * (xcd + 1) / nx - b1;
+  const int64_t bq = nq * xcd / nx, cq = nq * (xcd + 1) / nx - bq;
+  const int64_t b2 = n2 * xcd / nx, c2 = n2 * (xcd + 1) / nx - b2;
+  const int64_t total = c1 + cq + c2;
+
+  // amax slots no L1 part writes: zero (read only after the launch)
+  for (int j = blockIdx.x * kGemmThreads + threadIdx.x; j < MEGAMOE_L1_AMAX_PARTS; j += gridDim.x * kGemmThreads)
+    if (j < kLargeGrid || j >= kLargeGrid + n1) p1.amax_out[j] = 0.0f;
+
+  SmallSync l2sync;
+  if (kCal) {
+    l2sync.ready = sync + kSyncHeader;
+    l2sync.gm1 = gm1;
+    l2sync.err = err;
+  }
+  bool inv2_ready = kCal;
+  uint32_t amax_bits = 0;
+  int parity = 0;  // s_red buffer of the next group end (continues across items)
+  for (;;) {
+    if (threadIdx.x == 0) s_ticket = t_next;
+    __syncthreads();
+    const int64_t tx = s_ticket;
+    __syncthreads();
+    if (tx >= total) break;
+    // the global item: L1 part t < n1, quantization part t - n1 < nq, L2 part t - n1 - nq
+    const int64_t t = tx < c1 ? b1 + tx : tx < c1 + cq ? n1 + bq + (tx - c1) : n1 + nq + b2 + (tx - c1 - cq);
+    if (t < n1) {
+      small_pass<true, CH, kStaged, kCal, true>(p1, L, inv1, t, n1, amax_bits, parity, SmallSync{});
+      // Publish: this wave's h stores have completed (vmcnt counts stores), then the counts.
+      amax_bits = wave_max_u32(amax_bits);
+      if (lane == 0) s_amax[wave] = amax_bits;
+      amax_bits = 0;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint32_t m = s_amax[0];
+        for (int w = 1; w < kSWaves; ++w) m = m > s_amax[w] ? m : s_amax[w];
+        st_dev(p1.amax_out + kLargeGrid + t, bf16_bits_to_f32(m));
+        if (kCal) {
+          // per expert, the L1 groups of this part (both phases)
+          for (int ph = 0; ph < 2; ++ph) {
+            const int nm = ph == 0 ? s_ntiny : L.pref[E];
+            int64_t gb, ge;
+            phase_part(t, n1, (int64_t)nm * gm1, gb, ge);
+            while (gb < ge) {
+              const int mt = (int)(gb / gm1);
+              const int64_t hi = (int64_t)(mt + 1) * gm1 < ge ? (int64_t)(mt + 1) * gm1 : ge;
+              const int ex = ph == 0 ? L.tiny[mt] : find_expert(L.pref, E, 1, mt);
+              add_dev(sync + kSyncHeader + ex * kSyncStride, (uint32_t)(hi - gb));
+              gb = hi;
+            }
+          }
+        } else {
+          __builtin_amdgcn_s_waitcnt(0);  // the amax slot before the count
+          add_dev(sync + kSyncL1, 1u);
+        }
+      }
+    } else if (!kCal && t < n1 + nq) {
+      // Quantization part: wait for every L1 part, reduce the amax slots, quantize a share of h.
+      const int64_t s = t - n1;
+      if (threadIdx.x == 0) wait_count(sync + kSyncL1, (uint32_t)n1, err);
+      __syncthreads();
+      uint32_t am = 0;
+      for (int j = threadIdx.x; j < n1; j += kGemmThreads) {
+        const uint32_t v = ld_dev(reinterpret_cast<const uint32_t*>(p1.amax_out + kLargeGrid + j));
+        am = am > v ? am : v;  // non-negative floats: uint order is float order
+      }
+      am = wave_max_u32(am);
+      if (lane == 0) s_amax[wave] = am;
+      __syncthreads();
+      am = s_amax[0];
+      for (int w = 1; w < kSWaves; ++w) am = am > s_amax[w] ? am : s_amax[w];
+      const float gs = global_scale_of(__uint_as_float(am));
+      if (s == 0 && threadIdx.x == 0) st_dev(a.h_gs, gs);
+      int64_t bb, be;
+      phase_part(s, nq, qblocks, bb, be);
+      const int64_t bpr = p1.N / 16;
+      const uint8_t* hsrc = reinterpret_cast<const uint8_t*>(p1.out);
+      for (int64_t blk = bb + threadIdx.x; blk < be; blk += kGemmThreads) {
+        uint64_t* cd = reinterpret_cast<uint64_t*>(a.hq_codes + blk * 8);
+        uint8_t* sd = a.hq_scales + blk;
+        if (a.row_valid[blk / bpr] < 0) {
+          st_dev(cd, (uint64_t)0);
+          st_dev(sd, (uint8_t)0);
+          continue;
+        }
+        const u32x4 v0 = ld_dev_x4(hsrc + blk * 32), v1 = ld_dev_x4(hsrc + blk * 32 + 16);
+        uint32_t o[2];
+        const uint32_t sc = quant16(v0, v1, gs, o);
+        st_dev(cd, (uint64_t)o[0] | ((uint64_t)o[1] << 32));
+        st_dev(sd, (uint8_t)sc);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) add_dev(sync + kSyncQ, 1u);
+    } else {
+      if (!inv2_ready) {  // the first L2 part of this workgroup: h and its global scale are final
+        if (threadIdx.x == 0) wait_count(sync + kSyncQ, (uint32_t)nq, err);
+        __syncthreads();
+        const float gs_h = __uint_as_float(ld_dev(reinterpret_cast<const uint32_t*>(a.h_gs)));
+        for (int j = threadIdx.x; j < E; j += kGemmThreads)
+          inv2[j] = L.cnt[j] > 0 ? (float)(1.0 / ((double)gs_h * (double)p2.w_gs[j])) : 0.0f;
+        __syncthreads();
+        inv2_ready = true;
+      }
+      small_pass<false, CH, kStaged, false, true>(p2, L, inv2, t - n1 - nq, n2, amax_bits, parity, l2sync);
+    }
+    if (threadIdx.x == 0) t_next = add_dev(ticket, 1u);
+  }
+
+  // Leave; the last workgroup out sets the counters back to zero (everyone else is done with them).
+  if (threadIdx.x == 0) s_ticket = add_dev(sync + kSyncExit, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (s_ticket) {
+    for (int j = threadIdx.x; j < E; j += kGemmThreads) st_dev(sync + kSyncHeader + j * kSyncStride, 0u);
+    if (threadIdx.x < 8) st_dev(sync + 32 * threadIdx.x, 0u);
+    if (threadIdx.x == 0) {
+      st_dev(sync + kSyncExit, 0u);
+      st_dev(sync + kSyncL1, 0u);
+      st_dev(sync + kSyncQ, 0u);
     }
   }
 }
@@ -1161,6 +1505,50 @@ static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+// The fused small-class launch: CH and staging as launch_gemm would choose them for both GEMMs
+// (one CH for both, so that both passes split the m-tiles into tiny and regular alike).
+// XCDs of the current device: gfx950 has 32 CUs per XCD (a partitioned GPU shows fewer).
+static int device_xcds() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 1;
+  int n = dev < 64 ? cached[dev].load(std::memory_order_relaxed) : 0;
+  if (n == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    n = cus / 32 < 1 ? 1 : cus / 32 > kXcds ? kXcds : cus / 32;
+    if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+hipError_t launch_ffn_small(const FfnArgs& a0, hipStream_t stream) {
+  FfnArgs a = a0;
+  a.nxcd = device_xcds();
+  a.l1.small_covers_large = 1;
+  a.l2.small_covers_large = 1;
+  const bool cal = a.l1.q_codes != nullptr;
+  const int k1 = a.l1.K, k2 = a.l2.K;
+  const int ch = k1 % 256 == 0 && k2 % 256 == 0 ? 256 : 128;
+  const size_t tables = ffn_table_bytes(a.l1.E);
+  const size_t b1 = small_scale_buf_bytes(small_nb<true>(), k1), b2 = small_scale_buf_bytes(small_nb<false>(), k2);
+  const size_t bufs = 3 * (b1 > b2 ? b1 : b2);
+  const bool staged = MEGAMOE_SMALL_STAGED && ch == 256 && k1 / ch >= 2 * kSWaves && k2 / ch >= 2 * kSWaves &&
+                      tables + bufs <= kSmallDynMaxLds;
+  const size_t dyn = tables + (staged ? bufs : 0);
+  const dim3 grid(kSmallGrid), block(kGemmThreads);
+  if (cal) {
+    if (staged) hipLaunchKernelGGL((ffn_small_kernel<256, true, true>), grid, block, dyn, stream, a);
+    else if (ch == 256) hipLaunchKernelGGL((ffn_small_kernel<256, false, true>), grid, block, dyn, stream, a);
+    else hipLaunchKernelGGL((ffn_small_kernel<128, false, true>), grid, block, dyn, stream, a);
+  } else {
+    if (staged) hipLaunchKernelGGL((ffn_small_kernel<256, true, false>), grid, block, dyn, stream, a);
+    else if (ch == 256) hipLaunchKernelGGL((ffn_small_kernel<256, false, false>), grid, block, dyn, stream, a);
+    else hipLaunchKernelGGL((ffn_small_kernel<128, false, false>), grid, block, dyn, stream, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_l1(const GemmArgs& a, GemmClasses c, hipStream_t stream) {

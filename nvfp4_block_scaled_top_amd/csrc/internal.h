@@ -95,6 +95,23 @@ struct GemmClasses {
 };
 hipError_t launch_gemm_l1(const GemmArgs& a, GemmClasses c, hipStream_t stream);
 hipError_t launch_gemm_l2(const GemmArgs& a, GemmClasses c, hipStream_t stream);
+// L1, the requantization of h and L2 of the small class in one launch (moe_grouped_ffn_fused).
+// Sync words: per-XCD tickets, three counters and the error word in the first 384, then one
+// 32-word line per expert.
+constexpr int kFfnSyncHeader = 384, kFfnSyncStride = 32;
+struct FfnArgs {
+  GemmArgs l1;  // q_codes/q_scales/q_gs set: calibrated scale of h (NVFP4 h from the L1 epilogue);
+                // else out = bf16 h, requantized inside the launch
+  GemmArgs l2;  // a_codes/a_scales: NVFP4 h; a_gs: its global scale (written here when not given)
+  uint32_t* sync;             // MEGAMOE_FFN_SYNC words, zero before the launch (left zero)
+  const int32_t* row_valid;   // row_token: rows without an assignment get zero h codes
+  int64_t M_cap;
+  uint8_t* hq_codes;          // NVFP4 h written by the requantization parts (no calibrated scale)
+  uint8_t* hq_scales;
+  float* h_gs;                // global scale of h written by the first requantization part
+  int nxcd;                   // XCDs of the device (each has its own ticket counter)
+};
+hipError_t launch_ffn_small(const FfnArgs& a, hipStream_t stream);
 // n floats at p set to v on the stream (graph-safe: a kernel, no memset node).
 hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream);
 

@@ -208,6 +208,29 @@ class MoELayer:
                                w.w2_codes, w.w2_scales, w.w2_gs, self._rows(self.y, self.M_cap),
                                self.block_m_override, self.T, stream=stream)
 
+    def ffn_fused(self, w: MoEWeights, stream=None, h_gs: Optional[torch.Tensor] = None) -> None:
+        """L1, the requantization of h and L2 in one launch (every expert in 16-row m-tiles: for
+        decode).  h_gs given: a calibrated global scale for h; else h_gs is derived from the amax of
+        h inside the launch and written to self.h_gs.  Same bits as l1 / quantize_h / l2 with
+        16-row tiles."""
+        if getattr(self, "ffn_sync", None) is None:  # zero once; every call leaves it zero
+            self.ffn_sync = torch.zeros(mm.megamoe_ffn_sync_bytes(self.E) // 4, dtype=torch.int32,
+                                        device=self.out.device)
+        self._gs_h = self.h_gs if h_gs is None else h_gs
+        M = self.M_cap
+        mm.moe_grouped_ffn_fused(self.x_codes, self.x_scales, self._gs_x, self.row_token, self.padded_offsets,
+                                 self.counts, self.sched, w.w13_codes, w.w13_scales, w.w13_gs, w.w2_codes,
+                                 w.w2_scales, w.w2_gs, self.h_amax, self._rows(self.h_codes, M),
+                                 self._rows(self.h_scales, M), self._rows(self.y, M), self.ffn_sync,
+                                 h_gs_in=h_gs, h_bf16=None if h_gs is not None else self._rows(self.h, M),
+                                 h_gs_out=None if h_gs is not None else self.h_gs, stream=stream)
+
+    def ffn_sync_error(self) -> int:
+        """The fused launch's error word (non-zero once a wait inside it ever expired)."""
+        if getattr(self, "ffn_sync", None) is None:
+            return 0
+        return int(self.ffn_sync[mm.FFN_SYNC_ERROR_WORD].item())
+
     def combine(self, topk_weights: torch.Tensor, stream=None, shared: bool = False) -> None:
         if shared:
             mm.moe_combine_shared(self._rows(self.y, self.M_cap), self._rows(self.token_rows, self.T * self.k),
@@ -219,20 +242,25 @@ class MoELayer:
 
     def forward(self, x_bf16: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, w: MoEWeights,
                 stream=None, x_gs: Optional[torch.Tensor] = None, h_gs: Optional[torch.Tensor] = None,
-                shared: Optional[MoEWeights] = None, shared_h_gs: Optional[torch.Tensor] = None) -> torch.Tensor:
+                shared: Optional[MoEWeights] = None, shared_h_gs: Optional[torch.Tensor] = None,
+                fused: bool = False) -> torch.Tensor:
         """x_bf16 int16-viewed bf16 [T, H], topk_ids int32 [T, k], topk_weights float32 [T, k].
         x_gs / h_gs (float32 [1] on the device): calibrated global scales for x and h (e.g. the
         x_gs / h_gs buffers of a warm-up forward) instead of ones derived from this call's amax.
         shared: a shared expert (E = 1) whose output is added in the combine; shared_h_gs: a
         calibrated global scale for the shared expert's h.
-        With h_gs, L1 writes h as NVFP4 itself (no bf16 h and no separate quantization of h)."""
+        With h_gs, L1 writes h as NVFP4 itself (no bf16 h and no separate quantization of h).
+        fused: L1, the quantization of h and L2 as one launch (ffn_fused; for decode sizes)."""
         self.route_quantize(topk_ids, x_bf16, stream, gs=x_gs)
-        if h_gs is None:
-            self.l1(w, stream)
-            self.quantize_h(stream)
+        if fused:
+            self.ffn_fused(w, stream, h_gs=h_gs)
         else:
-            self.l1_nvfp4(w, h_gs, stream)
-        self.l2(w, stream)
+            if h_gs is None:
+                self.l1(w, stream)
+                self.quantize_h(stream)
+            else:
+                self.l1_nvfp4(w, h_gs, stream)
+            self.l2(w, stream)
         if shared is not None:
             self.shared_expert(shared, stream, h_gs=shared_h_gs)
         self.combine(topk_weights, stream, shared=shared is not None)

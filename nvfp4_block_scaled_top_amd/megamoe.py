@@ -19,6 +19,9 @@ _lib = None
 #: Slots of per-workgroup h amax written by moe_grouped_gemm_l1_silu (MEGAMOE_L1_AMAX_PARTS).
 L1_AMAX_PARTS = 1280
 
+#: Index of the error word in the sync buffer of moe_grouped_ffn_fused (MEGAMOE_FFN_SYNC_ERROR_WORD).
+FFN_SYNC_ERROR_WORD = 352
+
 #: Bytes of the static per-GPU scratch of moe_route_permute_noalloc (MEGAMOE_ROUTE_NOALLOC_SCRATCH_BYTES).
 ROUTE_NOALLOC_SCRATCH_BYTES = 1 << 20
 
@@ -55,6 +58,9 @@ SIGNATURES = {
     "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
     "moe_combine_shared": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P]),
     "megamoe_dense_workspace_bytes": (_SZ, [_I64]),
+    "megamoe_ffn_sync_bytes": (_SZ, [_I32]),
+    "moe_grouped_ffn_fused": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P,
+                                     _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_linear": (_I32, [_P, _P, _P, _I64, _I32, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "nvfp4_linear_gate_up_silu": (_I32, [_P, _P, _P, _I64, _I32, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "nvfp4_linear_gate_up_silu_nvfp4": (_I32, [_P, _P, _P, _I64, _I32, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _SZ,
@@ -229,6 +235,24 @@ def moe_grouped_gemm_l2(h_codes, h_scales, h_gs, padded_offsets, counts, sched, 
         _ptr(h_codes), _ptr(h_scales), _ptr(h_gs), _ptr(padded_offsets), _ptr(counts), _ptr(sched), _ptr(w2_codes),
         _ptr(w2_scales), _ptr(w2_gs), E, H, 2 * Ih, M_cap, block_m_override, max_rows_per_expert, _ptr(y_bf16),
         _stream(stream)))
+
+
+def megamoe_ffn_sync_bytes(num_experts: int) -> int:
+    return int(lib().megamoe_ffn_sync_bytes(num_experts))
+
+
+def moe_grouped_ffn_fused(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales,
+                          w13_gs, w2_codes, w2_scales, w2_gs, h_amax_parts, h_codes, h_scales, y_bf16, sync,
+                          h_gs_in=None, h_bf16=None, h_gs_out=None, stream=None):
+    E, I2, Hh = w13_codes.shape
+    M_cap = y_bf16.shape[0]
+    if h_amax_parts.numel() < L1_AMAX_PARTS:
+        raise MegaMoEError(f"h_amax_parts needs {L1_AMAX_PARTS} floats")
+    _check("moe_grouped_ffn_fused", lib().moe_grouped_ffn_fused(
+        _ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts), _ptr(sched),
+        _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), _ptr(w2_codes), _ptr(w2_scales), _ptr(w2_gs), E, 2 * Hh,
+        I2 // 2, M_cap, _ptr(h_gs_in), _ptr(h_bf16), _ptr(h_amax_parts), _ptr(h_codes), _ptr(h_scales),
+        _ptr(h_gs_out), _ptr(y_bf16), _ptr(sync), _nbytes(sync), _stream(stream)))
 
 
 def moe_combine(y_bf16, token_rows, topk_weights, out_bf16, stream=None):

@@ -175,6 +175,43 @@ def test_gemm_rejects_bad_args(lib):
     assert l2(*pl2, 8, 256, 128, 0, 0, 0, None, None) == -1
 
 
+def test_ffn_fused_rejects_bad_args(lib):
+    """moe_grouped_ffn_fused: shape, NULL and sync-size checks, all before any HIP call."""
+    f = lib.moe_grouped_ffn_fused
+    need = mm.megamoe_ffn_sync_bytes(8)
+    assert need == (384 + 8 * 32) * 4
+    assert mm.megamoe_ffn_sync_bytes(0) == 0 and mm.megamoe_ffn_sync_bytes(1025) == 0
+    p13 = [FAKE] * 13
+
+    def call(p=p13, E=8, H=256, I=128, M=64, gs_in=FAKE, hbf=None, amax=FAKE, codes=FAKE, scales=FAKE,
+             gs_out=None, y=FAKE, sync=FAKE, nbytes=need):
+        return f(*p, E, H, I, M, gs_in, hbf, amax, codes, scales, gs_out, y, sync, nbytes, None)
+
+    assert call(H=384) == -2                         # H not a multiple of 256
+    assert call(I=96) == -2                          # I not a multiple of 128
+    assert call(E=0) == -2
+    assert call(M=-1) == -2
+    assert call(nbytes=need - 1) == -3               # sync too small
+    assert call(sync=None) == -1
+    assert call(amax=None) == -1
+    assert call(gs_in=None) == -1                    # neither a calibrated scale nor h_gs_out
+    assert call(gs_in=None, gs_out=FAKE) == -1       # no calibrated scale: h_bf16 required
+    assert call(codes=None) == -1
+    assert call(y=None) == -1
+    pn = list(p13)
+    pn[10] = None                                    # w2_codes
+    assert call(p=pn) == -1
+    pr = list(p13)
+    pr[0] = pr[1] = pr[3] = None                     # x_codes, x_scales, row_token
+    assert call(p=pr) == -1                          # rows present: required
+    assert call(p=pr, M=0, codes=None, scales=None, y=None, sync=FAKE, amax=None) == -1  # amax still required
+
+
+def test_ffn_error_word_matches_header():
+    src = open(HEADER).read()
+    assert re.search(rf"#define MEGAMOE_FFN_SYNC_ERROR_WORD {mm.FFN_SYNC_ERROR_WORD}\b", src)
+
+
 def test_combine_rejects_bad_args(lib):
     f = lib.moe_combine
     assert f(FAKE, FAKE, FAKE, 4, 0, 256, FAKE, None) == -2
