@@ -11,6 +11,10 @@
 
 namespace megamoe {
 
+// Slots are taken 8 at a time: their rows and weights are loaded first, then the 8 output rows
+// together (two dependent round trips per 8 slots instead of two per slot), then added in slot order.
+constexpr int kCombineSlots = 8;
+
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ token_rows,
                                                       const float* __restrict__ w, int32_t T, int32_t k, int32_t H,
                                                       const uint16_t* __restrict__ y_shared,
@@ -20,15 +24,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   if (idx >= (int64_t)T * per) return;
   const int64_t t = idx / per, c8 = idx - t * per;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int32_t r = token_rows[t * k + j];
-    if (r < 0) continue;
-    const float wt = w[t * k + j];
-    const u32x4 v = *reinterpret_cast<const u32x4*>(y + (int64_t)r * H + c8 * 8);
+  for (int j0 = 0; j0 < k; j0 += kCombineSlots) {
+    int32_t r[kCombineSlots];
+    float wt[kCombineSlots];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = fmaf(wt, bf16_bits_to_f32(v[q] & 0xFFFFu), acc[2 * q]);
-      acc[2 * q + 1] = fmaf(wt, bf16_bits_to_f32(v[q] >> 16), acc[2 * q + 1]);
+    for (int u = 0; u < kCombineSlots; ++u) {
+      const int j = j0 + u;
+      r[u] = j < k ? token_rows[t * k + j] : -1;
+      wt[u] = j < k ? w[t * k + j] : 0.0f;
+    }
+    u32x4 v[kCombineSlots];
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u)
+      if (r[u] >= 0) v[u] = *reinterpret_cast<const u32x4*>(y + (int64_t)r[u] * H + c8 * 8);
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u) {
+      if (r[u] < 0) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(wt[u], bf16_bits_to_f32(v[u][q] & 0xFFFFu), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(wt[u], bf16_bits_to_f32(v[u][q] >> 16), acc[2 * q + 1]);
+      }
     }
   }
   if (y_shared != nullptr) {

@@ -248,3 +248,14 @@ def test_probe_lib_exports_and_rejects_bad_args():
     assert h.megamoe_probe_read(fake, 1024, 0, 512, 2, fake, None) == -1        # unroll
     assert h.megamoe_probe_placement(fake, 513, None) == -1                     # grid > 512
     assert h.megamoe_probe_placement(None, 512, None) == -1
+
+
+def test_build_spill_check_parses_remarks():
+    """The build refuses kernels that spill: it reads the compiler's resource-usage remarks."""
+    from nvfp4_block_scaled_top_amd import build_lib
+    text = ("a.hip:1:1: remark: Function Name: _Z1kv [-Rpass-analysis=kernel-resource-usage]\n"
+            "a.hip:1:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]\n"
+            "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 1028 [-Rpass-analysis=kernel-resource-usage]\n"
+            "b.hip:9:1: remark: Function Name: _Z1jv [-Rpass-analysis=kernel-resource-usage]\n"
+            "b.hip:9:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert build_lib.kernel_scratch(text) == {"_Z1kv": 1028, "_Z1jv": 0}
