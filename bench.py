@@ -294,10 +294,11 @@ def prefill_config_entry(wl, steps, warmup, use_graph):
             "gemm_ms": round(r["stage_ms"]["l1"] + r["stage_ms"]["l2"], 4)}
 
 
-def decode_seed_aggregate(wl, seeds, reps, copies=4):
+def decode_seed_aggregate(wl, seeds, reps, copies=4, **fwd_kw):
     """Decode over routing seeds 0..seeds-1 at every T of the workload: sum of algorithmic weight
     bytes over sum of step times (all 48 local experts quantized once, `copies` rotated copies;
-    one graph per seed and T holds `copies` layer forwards, one per weight copy)."""
+    one graph per seed and T holds `copies` layer forwards, one per weight copy).  fwd_kw: options
+    of the layer forward (fused=True: the L1 -> requantize -> L2 launch)."""
     import torch
     from nvfp4_block_scaled_top_amd import layer, synth
 
@@ -315,12 +316,12 @@ def decode_seed_aggregate(wl, seeds, reps, copies=4):
             nact = int(np.count_nonzero(counts))
             x = torch.from_numpy(synth.activations(wl, T, seed).view(np.int16)).to(dev)
             for c in range(copies):
-                L.forward(x, idd, wtd, Ws[c])
+                L.forward(x, idd, wtd, Ws[c], **fwd_kw)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for c in range(copies):
-                    L.forward(x, idd, wtd, Ws[c])
+                    L.forward(x, idd, wtd, Ws[c], **fwd_kw)
             g.replay()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -338,7 +339,8 @@ def decode_seed_aggregate(wl, seeds, reps, copies=4):
         res[f"T{T}"] = {"seeds": seeds, "weight_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                         "mean_us_per_step": round(tot_ms / seeds * 1e3, 2),
                         "mean_active_experts": round(tot_active / seeds, 3), "seeds_without_local_work": empty}
-        log(f"[bench] decode T={T} over {seeds} seeds: {gbs:.0f} GB/s, {tot_ms / seeds * 1e3:.1f} us/step")
+        log(f"[bench] decode T={T} over {seeds} seeds{' ' + str(fwd_kw) if fwd_kw else ''}: {gbs:.0f} GB/s, "
+            f"{tot_ms / seeds * 1e3:.1f} us/step")
         del L
     del Ws
     torch.cuda.synchronize()

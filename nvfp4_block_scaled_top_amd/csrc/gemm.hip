@@ -821,7 +821,6 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
   L.scl = s_dyn + small_table_bytes(E);
   L.red = s_red;
   L.afrag = s_afrag;
-  small_tables<CH>(p, L, s_inv, *p.a_gs);
 
   // This workgroup's position: workgroup b runs on XCD b % 8; the kSOcc workgroups of a CU (XCD-
   // local indices i and i + 256/8) get neighbouring positions.
@@ -832,7 +831,12 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
 
   uint32_t amax_bits = 0;
   int parity = 0;  // s_red buffer of the next group end (continues across phases)
-  small_pass<kL1, CH, kStaged, kQOut, false>(p, L, s_inv, lb, G, amax_bits, parity, SmallSync{});
+  // The m-tile totals of the routing step's table header: with none for this class (e.g. a decode
+  // step without a local token) the tables are not built and only the amax slots are written.
+  if (sload(p.sched, 1) + (p.small_covers_large ? sload(p.sched, 2) : 0) > 0) {
+    small_tables<CH>(p, L, s_inv, *p.a_gs);
+    small_pass<kL1, CH, kStaged, kQOut, false>(p, L, s_inv, lb, G, amax_bits, parity, SmallSync{});
+  }
 
   if (kL1) {
     const int wave = threadIdx.x / kWave, lane = lane_id();
@@ -903,11 +907,28 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void ffn_small_kernel(FfnArgs 
   // This workgroup's XCD (hardware register XCC_ID), among the nxcd of the device.
   const int xcd = (int)((__builtin_amdgcn_s_getreg((31 << 11) | 20) & 0xFu) % (uint32_t)a.nxcd);
   uint32_t* const ticket = sync + 32 * xcd;
-  uint32_t t_next = 0;
-  if (threadIdx.x == 0) t_next = add_dev(ticket, 1u);  // the first claim, while the tables load
   const GemmArgs& p1 = a.l1;
   const GemmArgs& p2 = a.l2;
   const int E = p1.E;
+  if (sload(p1.sched, 1) + sload(p1.sched, 2) == 0) {
+    // No m-tile (a decode step without a local token): no counter is touched.  The amax slots
+    // are zero; without a calibrated scale h's codes are zero on every row and gs_h = 1, as the
+    // quantizer writes them when no row is valid.
+    for (int j = blockIdx.x * kGemmThreads + threadIdx.x; j < MEGAMOE_L1_AMAX_PARTS; j += gridDim.x * kGemmThreads)
+      p1.amax_out[j] = 0.0f;
+    if (!kCal) {
+      const int64_t qblocks = a.M_cap * (p1.N / 16);
+      for (int64_t j = (int64_t)blockIdx.x * kGemmThreads + threadIdx.x; j < qblocks;
+           j += (int64_t)gridDim.x * kGemmThreads) {
+        *reinterpret_cast<u32x2*>(a.hq_codes + j * 8) = u32x2{0u, 0u};
+        a.hq_scales[j] = 0;
+      }
+      if (blockIdx.x == 0 && threadIdx.x == 0) *a.h_gs = 1.0f;
+    }
+    return;
+  }
+  uint32_t t_next = 0;
+  if (threadIdx.x == 0) t_next = add_dev(ticket, 1u);  // the first claim, while the tables load
   SmallLds<kSNb> L;
   L.pref = reinterpret_cast<int*>(s_dyn);
   L.poff = L.pref + E + 1;
