@@ -4,7 +4,7 @@ bit for bit: h codes and scales, the global scale of h, the amax slots' maximum 
 amax-derived scale (the launch waits for every L1 group before quantizing h) and with a calibrated
 one (an expert's L2 waits for its own L1 groups only).  Workloads: decode at T = 1, 4 and 8 on
 the 48-expert share, the tiny and odd-K shapes (128-element chunks), padded rows,
-experts of up to 50 rows (several 16-row m-tiles each) and a single expert.  The sync words are back
+experts of up to 50 rows (several 16-row m-tiles each), a single expert and 1024 local experts.  The sync words are back
 at zero after every call, no wait expired, a second call right after the first gives the same bits,
 the layer's fused forward matches the oracle's layer, and replays of a captured graph equal the
 eager result."""
@@ -23,11 +23,15 @@ MID = synth.Workload("mid_zipf_e24", 32, 4, 512, 256, (300,), 0, 24, 1, zipf=Tru
 MID_PAD = synth.Workload("mid_zipf_e16_pad128", 32, 4, 512, 256, (150,), 8, 16, 128, zipf=True)
 ODD_K = synth.Workload("odd_k640_e16", 128, 6, 1024, 640, (8,), 0, 16, 1)
 SINGLE = synth.Workload("single_expert_top1", 1, 1, 256, 128, (40,), 0, 1, 1)
+# the most local experts one call takes: 24.6 KB of per-expert tables in LDS, 1024 expert counters
+# in the sync buffer
+WIDE = synth.Workload("wide_e1024", 2048, 8, 512, 256, (24,), 512, 1024, 1)
 DEC = synth.WORKLOADS[1]
 
 CASES = [(synth.WORKLOADS[0], 16), (DEC, 1), (DEC, 4), (DEC, 8), (MID, 300), (MID_PAD, 150), (ODD_K, 8),
-         (SINGLE, 40)]
-IDS = ["tiny", "decode_t1", "decode_t4", "decode_t8", "mid", "mid_pad128", "odd_k640", "single_expert"]
+         (SINGLE, 40), (WIDE, 24)]
+IDS = ["tiny", "decode_t1", "decode_t4", "decode_t8", "mid", "mid_pad128", "odd_k640", "single_expert",
+       "wide_e1024"]
 
 
 def make_layer(wl, T):
