@@ -415,6 +415,7 @@ def measured_ceilings():
     del src, dst, a, bm
     torch.cuda.synchronize()
     out["hbm_read"] = hbm_read_ceilings()
+    out["decode_gemm_load_stream"] = gemm_stream_ceilings()
     out["workgroup_placement"] = placement_check()
     out["dense_nvfp4_gemm_operand_data"] = dense_data_dependence()
     return out
@@ -434,7 +435,44 @@ def probe_lib():
     h.megamoe_probe_read.restype = ctypes.c_int
     h.megamoe_probe_placement.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     h.megamoe_probe_placement.restype = ctypes.c_int
+    h.megamoe_probe_gemm_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    h.megamoe_probe_gemm_stream.restype = ctypes.c_int
     return h
+
+
+def gemm_stream_ceilings(experts=9, copies=4, reps=100):
+    """Read rate (GB/s) of the 16-row L1 GEMM's weight-code stream at decode T=8 (9 active experts'
+    W13 codes, 132 MB) with the kernel's launch shape and load structure but no arithmetic
+    (csrc/probe.hip, megamoe_probe_gemm_stream): in the kernel's own addressing and in a
+    workgroup-contiguous order; `copies` rotated buffers keep it out of the last-level cache."""
+    import torch
+
+    lib = probe_lib()
+    stream = torch.cuda.current_stream()
+    nbytes = experts * 4096 * 3584
+    bufs = [torch.full((nbytes,), 0x35 + i, dtype=torch.uint8, device="cuda") for i in range(copies)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    res = {"bytes": nbytes}
+    for name, pattern in (("gemm_addressing_GBps", 0), ("workgroup_contiguous_GBps", 1)):
+        def run(i):
+            rc = lib.megamoe_probe_gemm_stream(bufs[i % copies].data_ptr(), nbytes, experts, pattern,
+                                               sink.data_ptr(), ctypes_stream(stream))
+            if rc != 0:
+                raise RuntimeError(f"megamoe_probe_gemm_stream failed ({rc})")
+        for i in range(3):
+            run(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            run(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+    log(f"[bench] decode GEMM load stream without arithmetic: {res}")
+    del bufs
+    return res
 
 
 # (name, order, grid, loads in flight per thread): order 0 = all workgroups read neighbouring bytes

@@ -1,5 +1,7 @@
 // Measurement kernels for bench.py, built into their own library (libmegamoe_probe.so); the MoE
 // layer does not use them.  They give the ceilings the layer's kernels are compared with:
+//  * megamoe_probe_gemm_stream: the 16-row GEMM's weight stream at decode, its load structure
+//    without the arithmetic;
 //  * megamoe_probe_read: the HBM read rate of three access orders over a buffer of a given size
 //    (decode streams ~150 MB of weights per GEMM), each lane summing 16-byte loads;
 //  * megamoe_probe_placement: the CU each workgroup of a two-per-CU launch runs on (the 16-row
@@ -57,6 +59,63 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
   if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads; practically never taken
 }
 
+// The weight-code stream of the 16-row L1 GEMM at decode (experts x 4096 rows x 3584 code bytes, the
+// W13 codes of the active experts at H = 7168, I = 2048) with that kernel's launch shape and load
+// structure but no arithmetic between the loads: 512 workgroups of 4 waves, two per CU (80 KB of
+// LDS each), groups of 2 x 16 weight rows over the whole K cut into equal contiguous ranges, the 4
+// waves splitting the 28 K-chunks of 128 code bytes (7 steps per group), a 2-step register ring of
+// 4 x 16-byte loads per lane refilled after each step is consumed (XOR-ed into a sink).
+//   pattern 0: the GEMM's addressing: lane (r = lane % 16, g = lane / 16) of block j reads 32 bytes
+//              of row r at K offset 32 g; rows 0-7 of a block are gate rows, 8-15 the matching up
+//              rows 2048 rows later;
+//   pattern 1: workgroup-contiguous: the 4 KB a wave takes at step s of group G lie at
+//              ((G * 7 + s) * 4 + wave) * 4 KB (a layout permuted for the stream).
+constexpr int kGsRowBytes = 3584, kGsRowsPerExpert = 4096, kGsGroupsPerExpert = 128, kGsSteps = 7;
+constexpr int kGsLdsWords = 80 * 1024 / 4;
+
+template <int PATTERN>
+__global__ __launch_bounds__(kThreads, 2) void gemm_stream_kernel(const uint8_t* __restrict__ w, int groups,
+                                                                  uint32_t* sink) {
+  __shared__ uint32_t lds[kGsLdsWords];  // two workgroups per CU, as the GEMM
+  const int wave = threadIdx.x / 64, lane = threadIdx.x & 63;
+  const int g0 = (int)((int64_t)blockIdx.x * groups / gridDim.x);
+  const int g1 = (int)((int64_t)(blockIdx.x + 1) * groups / gridDim.x);
+  const int S = (g1 - g0) * kGsSteps;
+  const int r16 = lane & 15, gg = lane >> 4;
+  auto load = [&](u32x4 (&d)[4], int t) {
+    const int g = g0 + t / kGsSteps, s = t % kGsSteps;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int64_t off;
+      if (PATTERN == 1) {
+        off = ((int64_t)(g * kGsSteps + s) * 4 + wave) * 4096 + k * 1024 + lane * 16;
+      } else {
+        const int j = k >> 1, q = k & 1, e = g / kGsGroupsPerExpert, gi = g % kGsGroupsPerExpert;
+        const int hc = gi * 16 + 8 * j + (r16 & 7);
+        const int row = e * kGsRowsPerExpert + (r16 < 8 ? hc : kGsRowsPerExpert / 2 + hc);
+        off = (int64_t)row * kGsRowBytes + (wave * kGsSteps + s) * 128 + gg * 32 + q * 16;
+      }
+      d[k] = *reinterpret_cast<const u32x4*>(w + off);
+    }
+  };
+  uint32_t acc = lds[threadIdx.x & 0] & 0u;
+  u32x4 ring[2][4];
+  if (S > 0) load(ring[0], 0);
+  if (S > 1) load(ring[1], 1);
+  for (int s0 = 0; s0 < S; s0 += 2) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (s0 + k < S) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc ^= ring[k][i].x ^ ring[k][i].y ^ ring[k][i].z ^ ring[k][i].w;
+        if (s0 + k + 2 < S) load(ring[k], s0 + k + 2);
+      }
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads; practically never taken
+  if (acc == 0x7F4A7C15u) lds[threadIdx.x] = acc;
+}
+
 // Two workgroups of 256 threads per CU (78 KB of LDS each, like the 16-row GEMM); thread 0 of each
 // records the HW_ID and XCC_ID registers, then the workgroup waits ~spin cycles so that all of
 // them are resident at once.
@@ -87,6 +146,22 @@ extern "C" int megamoe_probe_read(const void* buf, uint64_t bytes, int32_t order
   const u32x4* p = static_cast<const u32x4*>(buf);
   if (unroll == 1) hipLaunchKernelGGL(read_kernel<1>, dim3(grid), dim3(kThreads), 0, s, p, bytes / 16, order, sink);
   else hipLaunchKernelGGL(read_kernel<4>, dim3(grid), dim3(kThreads), 0, s, p, bytes / 16, order, sink);
+  return (int)hipGetLastError();
+}
+
+// experts >= 1 (groups = 128 per expert); bytes >= experts * 4096 * 3584; pattern 0 or 1.  Returns 0,
+// -1 for bad arguments, or the HIP error code.
+extern "C" int megamoe_probe_gemm_stream(const void* buf, uint64_t bytes, int32_t experts, int32_t pattern,
+                                         uint32_t* sink, void* stream) {
+  using namespace megamoe_probe;
+  if (!buf || !sink || experts < 1 || experts > 1024 || (pattern != 0 && pattern != 1) ||
+      bytes < (uint64_t)experts * kGsRowsPerExpert * kGsRowBytes)
+    return -1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* w = static_cast<const uint8_t*>(buf);
+  const int groups = experts * kGsGroupsPerExpert;
+  if (pattern == 0) hipLaunchKernelGGL(gemm_stream_kernel<0>, dim3(512), dim3(kThreads), 0, s, w, groups, sink);
+  else hipLaunchKernelGGL(gemm_stream_kernel<1>, dim3(512), dim3(kThreads), 0, s, w, groups, sink);
   return (int)hipGetLastError();
 }
 

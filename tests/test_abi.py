@@ -230,7 +230,7 @@ def test_dense_nvfp4_rejects_bad_args(lib):
 
 
 def test_probe_lib_exports_and_rejects_bad_args():
-    """bench.py's measurement kernels (csrc/probe.hip): the library loads, exports both entry points
+    """bench.py's measurement kernels (csrc/probe.hip): the library loads, exports its entry points
     and rejects bad arguments before any launch (no GPU is touched)."""
     from nvfp4_block_scaled_top_amd import build_lib
 
@@ -248,6 +248,13 @@ def test_probe_lib_exports_and_rejects_bad_args():
     assert h.megamoe_probe_read(fake, 1024, 0, 512, 2, fake, None) == -1        # unroll
     assert h.megamoe_probe_placement(fake, 513, None) == -1                     # grid > 512
     assert h.megamoe_probe_placement(None, 512, None) == -1
+    h.megamoe_probe_gemm_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    need = 9 * 4096 * 3584
+    assert h.megamoe_probe_gemm_stream(fake, need - 16, 9, 0, fake, None) == -1   # buffer too small
+    assert h.megamoe_probe_gemm_stream(fake, need, 9, 2, fake, None) == -1        # pattern
+    assert h.megamoe_probe_gemm_stream(fake, need, 0, 0, fake, None) == -1        # experts
+    assert h.megamoe_probe_gemm_stream(None, need, 9, 1, fake, None) == -1
 
 
 def test_build_spill_check_parses_remarks():
