@@ -292,16 +292,31 @@ __device__ __forceinline__ uint32_t add_dev(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Order of the handoff.  The producer's device-scope stores complete (s_waitcnt: vmcnt counts
+// stores on gfx9) before its counter increment is issued; the consumer issues its device-scope
+// loads only after its poll has seen the final count.  The hardware keeps both orders; a
+// compiler-only fence at each end keeps the compiler from moving the relaxed accesses across them
+// (no cache write-back or invalidate is emitted).
+__device__ __forceinline__ void publish_fence() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Waits until the device-scope counter *c reaches target (wave-uniform; every lane of the wave
 // calls it).  Bounded: after about a quarter of a second it sets *err and returns, so a broken
 // dependency shows as an error word instead of a hang.
 constexpr int kSpinLimit = 1 << 18;
 __device__ __forceinline__ void wait_count(const uint32_t* c, uint32_t target, uint32_t* err) {
   for (int it = 0; it < kSpinLimit; ++it) {
-    if (__builtin_amdgcn_readfirstlane(ld_dev(c)) >= target) return;
+    if (__builtin_amdgcn_readfirstlane(ld_dev(c)) >= target) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      return;
+    }
     __builtin_amdgcn_s_sleep(8);
   }
   st_dev(err, 1u);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // The part of one phase's group list that work item `part` of `nparts` takes.
@@ -989,7 +1004,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void ffn_small_kernel(FfnArgs 
       amax_bits = wave_max_u32(amax_bits);
       if (lane == 0) s_amax[wave] = amax_bits;
       amax_bits = 0;
-      __builtin_amdgcn_s_waitcnt(0);
+      publish_fence();
       __syncthreads();
       if (threadIdx.x == 0) {
         uint32_t m = s_amax[0];
@@ -1010,7 +1025,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void ffn_small_kernel(FfnArgs 
             }
           }
         } else {
-          __builtin_amdgcn_s_waitcnt(0);  // the amax slot before the count
+          publish_fence();  // the amax slot before the count
           add_dev(sync + kSyncL1, 1u);
         }
       }
@@ -1049,7 +1064,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void ffn_small_kernel(FfnArgs 
         st_dev(cd, (uint64_t)o[0] | ((uint64_t)o[1] << 32));
         st_dev(sd, (uint8_t)sc);
       }
-      __builtin_amdgcn_s_waitcnt(0);
+      publish_fence();
       __syncthreads();
       if (threadIdx.x == 0) add_dev(sync + kSyncQ, 1u);
     } else {
