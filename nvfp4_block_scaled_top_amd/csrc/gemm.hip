@@ -99,7 +99,9 @@ __device__ __forceinline__ float silu_f32(float g) {
 // weight byte small and every CU equally busy:
 //  * work unit = a group: kSNb (small_nb) 16-column MFMA blocks of one m-tile over the whole K
 //    (L1 block j: MFMA columns 0-7 are gate rows of h columns j0+8j.., columns 8-15 the matching
-//    up rows, paired after the reduction with a lane shuffle; L2 block j: weight rows j0+16j..).
+//    up rows, paired after the reduction with a lane shuffle; L2 block j: weight rows j0+16j..);
+//    L2 takes kSNbWide blocks per group when there are many groups per workgroup (see kSNbWide).
+//    The width changes neither the K split nor any summation order: both give the same bits.
 //    The groups of all small m-tiles are laid end to end and each workgroup takes an equal
 //    contiguous range of whole groups.  The two workgroups that share a CU take neighbouring
 //    ranges and the workgroups of one XCD a contiguous eighth (the A rows of an m-tile stay in
@@ -128,6 +130,9 @@ __device__ __forceinline__ float silu_f32(float g) {
 #ifndef MEGAMOE_SMALL_NB_L2
 #define MEGAMOE_SMALL_NB_L2 2
 #endif
+#ifndef MEGAMOE_SMALL_NB_L2_WIDE
+#define MEGAMOE_SMALL_NB_L2_WIDE 4
+#endif
 #ifndef MEGAMOE_SMALL_DEPTH
 #define MEGAMOE_SMALL_DEPTH 2
 #endif
@@ -139,6 +144,13 @@ __device__ __forceinline__ float silu_f32(float g) {
 #endif
 template <bool kL1>
 constexpr int small_nb() { return kL1 ? MEGAMOE_SMALL_NB_L1 : MEGAMOE_SMALL_NB_L2; }  // blocks per group
+// L2 with many groups per workgroup takes wider groups: the regular phase decodes each A row once
+// per MFMA step for all blocks of a group, so 4 blocks halve that cost per weight byte (the
+// 512-token prefill's L2: 757 -> 676 us), while with few groups per workgroup the coarser split
+// balances worse (decode T=8: 22.0 -> 23.1 us).  The kernel takes the wide width when the narrow
+// grouping gives every workgroup at least kWideMinGroups groups.
+constexpr int kSNbWide = MEGAMOE_SMALL_NB_L2_WIDE;
+constexpr int kWideMinGroups = 32;
 constexpr int kSDepth = MEGAMOE_SMALL_DEPTH;  // ring slots (chunks in flight per wave)
 constexpr int kSOcc = MEGAMOE_SMALL_OCC;      // workgroups (of 4 waves) per CU
 constexpr int kSWaves = kGemmThreads / kWave; // K split
@@ -146,16 +158,18 @@ constexpr int kLargeGrid = 256;               // large class: one workgroup per 
 constexpr int kSmallGrid = 256 * kSOcc;       // small class: resident workgroups
 constexpr int kAmaxSmallSlots = MEGAMOE_L1_AMAX_PARTS - kLargeGrid;  // slots [kLargeGrid, PARTS)
 // Dynamic LDS of the small class: the per-expert tables, then 3 staged scale buffers if kStaged.
-// With kSOcc = 2 a workgroup may use 80 KB; the static arrays take about 21 KB of it.
-constexpr size_t kSmallDynMaxLds = 160 * 1024 / kSOcc - 22 * 1024;
+// With kSOcc = 2 a workgroup may use 80 KB; the static arrays of a kernel whose groups have at
+// most nb blocks take 8 KB per block (the double-buffered group-end partials) plus about 5 KB.
+constexpr size_t small_dyn_max_lds(int nb) { return 160 * 1024 / kSOcc - (size_t)nb * 8 * 1024 - 6 * 1024; }
 static_assert(kSmallGrid <= kAmaxSmallSlots, "one amax slot per small workgroup");
 static_assert(kSmallGrid % kXcds == 0 && (kSmallGrid / kXcds) % kSOcc == 0, "grid split");
 
-template <bool kL1>
-constexpr int small_group_units() { return kL1 ? 8 * small_nb<kL1>() : 16 * small_nb<kL1>(); }
+template <bool kL1, int NB = small_nb<kL1>()>
+constexpr int small_group_units() { return kL1 ? 8 * NB : 16 * NB; }
 
 // Bytes of the per-expert tables at the start of the small class's dynamic LDS (16-aligned).
-__host__ __device__ inline size_t small_table_bytes(int E) { return (((size_t)5 * E + 1) * 4 + 15) / 16 * 16; }
+__host__ __device__ constexpr size_t small_table_bytes(int E) { return (((size_t)5 * E + 1) * 4 + 15) / 16 * 16; }
+static_assert(small_table_bytes(MEGAMOE_MAX_EXPERTS) <= small_dyn_max_lds(kSNbWide), "the tables fit beside wide groups");
 // Bytes of one staged scale buffer: kSNb x 16 weight rows of Ks scale bytes, each row padded to
 // (Ks/16 + 1) pieces of 16 bytes, rounded up to whole 1024-byte DMA instructions.
 __host__ __device__ inline size_t small_scale_buf_bytes(int nb, int K) {
@@ -393,12 +407,13 @@ struct SmallSync {
 
 // One pass of the small class over part `part` of `nparts` of its group lists (tiny m-tiles,
 // then regular ones), for one workgroup.  inv: the pass's 1 / (gs_a * gs_w[e]).
-template <bool kL1, int CH, bool kStaged, bool kQOut, bool kDev>
-__device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<small_nb<kL1>()>& L, const float* inv,
+template <bool kL1, int NB, int CH, bool kStaged, bool kQOut, bool kDev>
+__device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<NB>& L, const float* inv,
                                            int64_t part, int64_t nparts, uint32_t& amax_bits, int& parity,
                                            const SmallSync& sync) {
   static_assert(!kStaged || CH == 256, "staged scales copy whole 16-byte pieces: one per 256-element chunk");
-  constexpr int kSNb = small_nb<kL1>();
+  static_assert(!kL1 || NB % 2 == 0, "L1 NVFP4 h: a group holds whole 16-column blocks of h");
+  constexpr int kSNb = NB;
   constexpr int kQ = CH / 128;
   constexpr int kLaneBytes = CH / 8, kLaneScales = CH / 64;
   constexpr int kPieces = CH / 8;               // 8-element pieces per row and chunk
@@ -414,7 +429,7 @@ __device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<sma
   constexpr bool quant_out = kL1 && kQOut;  // L1: NVFP4 h (q_codes, q_scales) instead of bf16 h
   const float gs_q = quant_out ? *p.q_gs : 1.0f;
   const int NU = p.N;  // units per m-tile: L1 h columns (I), L2 output columns (H)
-  constexpr int GU = small_group_units<kL1>();
+  constexpr int GU = small_group_units<kL1, NB>();
   const int Gm = (NU + GU - 1) / GU;  // groups per m-tile
   const int K = p.K, Kh = K / 2, Ks = K / 16;
   const int Nw = kL1 ? 2 * p.N : p.N;  // weight rows per expert
@@ -816,11 +831,14 @@ __device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<sma
   run_phase(BoolTag<false>{});
 }
 
-template <bool kL1, int CH, bool kStaged, bool kQOut>
+// kNbMax: the widest group the kernel may take (L2: kSNbWide when the launch sized the staged
+// scale buffers for it, else the narrow width); the dynamic LDS holds scale buffers of that width.
+template <bool kL1, int CH, bool kStaged, bool kQOut, int kNbMax>
 __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArgs p) {
   constexpr int kSNb = small_nb<kL1>();
+  static_assert(kNbMax >= kSNb && (kL1 ? kNbMax == kSNb : kNbMax % kSNb == 0), "group widths");
   extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
-  __shared__ f32x4 s_red[2][kSWaves][kSNb][kWave];
+  __shared__ f32x4 s_red[2][kSWaves][kNbMax][kWave];
   __shared__ f16x8 s_afrag[kSWaves][kWave];  // tiny phase: this chunk's decoded A pieces
   __shared__ uint32_t s_amax[kSWaves];
   __shared__ int s_ntiny;
@@ -834,7 +852,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
   L.tiny = reinterpret_cast<int*>(s_inv + E);
   L.ntiny = &s_ntiny;
   L.scl = s_dyn + small_table_bytes(E);
-  L.red = s_red;
+  L.red = reinterpret_cast<f32x4 (*)[kSWaves][kSNb][kWave]>(&s_red[0][0][0][0]);
   L.afrag = s_afrag;
 
   // This workgroup's position: workgroup b runs on XCD b % 8; the kSOcc workgroups of a CU (XCD-
@@ -850,7 +868,19 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
   // step without a local token) the tables are not built and only the amax slots are written.
   if (sload(p.sched, 1) + (p.small_covers_large ? sload(p.sched, 2) : 0) > 0) {
     small_tables<CH>(p, L, s_inv, *p.a_gs);
-    small_pass<kL1, CH, kStaged, kQOut, false>(p, L, s_inv, lb, G, amax_bits, parity, SmallSync{});
+    bool wide = false;
+    if constexpr (kNbMax > kSNb) {  // every workgroup derives the same choice from the same tables
+      constexpr int GU = small_group_units<kL1>();
+      const int64_t narrow_groups = (int64_t)(s_ntiny + L.pref[E]) * ((p.N + GU - 1) / GU);
+      wide = narrow_groups >= (int64_t)kWideMinGroups * G;
+    }
+    if (wide) {
+      const SmallLds<kNbMax> W{L.pref, L.poff, L.cnt, L.tiny, L.ntiny, L.scl,
+                               reinterpret_cast<f32x4 (*)[kSWaves][kNbMax][kWave]>(&s_red[0][0][0][0]), s_afrag};
+      small_pass<kL1, kNbMax, CH, kStaged, kQOut, false>(p, W, s_inv, lb, G, amax_bits, parity, SmallSync{});
+    } else {
+      small_pass<kL1, kSNb, CH, kStaged, kQOut, false>(p, L, s_inv, lb, G, amax_bits, parity, SmallSync{});
+    }
   }
 
   if (kL1) {
@@ -999,7 +1029,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void ffn_small_kernel(FfnArgs 
     // the global item: L1 part t < n1, quantization part t - n1 < nq, L2 part t - n1 - nq
     const int64_t t = tx < c1 ? b1 + tx : tx < c1 + cq ? n1 + bq + (tx - c1) : n1 + nq + b2 + (tx - c1 - cq);
     if (t < n1) {
-      small_pass<true, CH, kStaged, kCal, true>(p1, L, inv1, t, n1, amax_bits, parity, SmallSync{});
+      small_pass<true, kSNb, CH, kStaged, kCal, true>(p1, L, inv1, t, n1, amax_bits, parity, SmallSync{});
       // Publish: this wave's h stores have completed (vmcnt counts stores), then the counts.
       amax_bits = wave_max_u32(amax_bits);
       if (lane == 0) s_amax[wave] = amax_bits;
@@ -1077,7 +1107,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void ffn_small_kernel(FfnArgs 
         __syncthreads();
         inv2_ready = true;
       }
-      small_pass<false, CH, kStaged, false, true>(p2, L, inv2, t - n1 - nq, n2, amax_bits, parity, l2sync);
+      small_pass<false, kSNb, CH, kStaged, false, true>(p2, L, inv2, t - n1 - nq, n2, amax_bits, parity, l2sync);
     }
     if (threadIdx.x == 0) t_next = add_dev(ticket, 1u);
   }
@@ -1525,19 +1555,25 @@ static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
     // Staged weight scales need whole 16-byte scale pieces per chunk (K a multiple of 256: a
     // staged row of K/16 bytes is K/256 whole pieces), at least 2 chunks of K for every wave (so
     // the loader never copies into the buffer of a group still being computed, see above) and 3
-    // buffers beside the tables.
+    // buffers beside the tables.  L2 sizes them for its wide groups; where those do not fit, the
+    // staged scales (worth more) are kept and the kernel runs narrow groups only.
+    constexpr int nb = small_nb<kL1>(), nbw = kL1 ? nb : kSNbWide;
     const int ch = a.K % 256 == 0 ? 256 : 128;
     const size_t tables = small_table_bytes(a.E);
-    const size_t bufs = 3 * small_scale_buf_bytes(small_nb<kL1>(), a.K);
-    const bool staged =
-        MEGAMOE_SMALL_STAGED && ch == 256 && a.K / ch >= 2 * kSWaves && tables + bufs <= kSmallDynMaxLds;
-    const size_t dyn = tables + (staged ? bufs : 0);
-    if (staged)
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true, kQ>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
-    else if (ch == 256)
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, false, kQ>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 128, false, kQ>), dim3(kSmallGrid), dim3(kGemmThreads), dyn, stream, a);
+    auto fits = [&](int w) { return tables + 3 * small_scale_buf_bytes(w, a.K) <= small_dyn_max_lds(w); };
+    const bool can_stage = MEGAMOE_SMALL_STAGED && ch == 256 && a.K / ch >= 2 * kSWaves;
+    const dim3 grid(kSmallGrid), block(kGemmThreads);
+    if (can_stage && fits(nbw)) {
+      const size_t dyn = tables + 3 * small_scale_buf_bytes(nbw, a.K);
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true, kQ, nbw>), grid, block, dyn, stream, a);
+    } else if (can_stage && fits(nb)) {
+      const size_t dyn = tables + 3 * small_scale_buf_bytes(nb, a.K);
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true, kQ, nb>), grid, block, dyn, stream, a);
+    } else if (ch == 256) {  // the tables (at most 20.5 KB) fit beside the wide kernel's static LDS
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, false, kQ, nbw>), grid, block, tables, stream, a);
+    } else {
+      hipLaunchKernelGGL((gemm_small_kernel<kL1, 128, false, kQ, nbw>), grid, block, tables, stream, a);
+    }
     return hipGetLastError();
   }
   return hipSuccess;
@@ -1572,7 +1608,7 @@ hipError_t launch_ffn_small(const FfnArgs& a0, hipStream_t stream) {
   const size_t b1 = small_scale_buf_bytes(small_nb<true>(), k1), b2 = small_scale_buf_bytes(small_nb<false>(), k2);
   const size_t bufs = 3 * (b1 > b2 ? b1 : b2);
   const bool staged = MEGAMOE_SMALL_STAGED && ch == 256 && k1 / ch >= 2 * kSWaves && k2 / ch >= 2 * kSWaves &&
-                      tables + bufs <= kSmallDynMaxLds;
+                      tables + bufs <= small_dyn_max_lds(small_nb<true>());
   const size_t dyn = tables + (staged ? bufs : 0);
   const dim3 grid(kSmallGrid), block(kGemmThreads);
   if (cal) {

@@ -4,7 +4,9 @@ bit for bit: h codes and scales, the global scale of h, the amax slots' maximum 
 amax-derived scale (the launch waits for every L1 group before quantizing h) and with a calibrated
 one (an expert's L2 waits for its own L1 groups only).  Workloads: decode at T = 1, 4 and 8 on
 the 48-expert share, the tiny and odd-K shapes (128-element chunks), padded rows,
-experts of up to 50 rows (several 16-row m-tiles each), a single expert and 1024 local experts.  The sync words are back
+experts of up to 50 rows (several 16-row m-tiles each), a single expert, 1024 local experts, and two
+routings with enough m-tiles that the separate L2 kernel takes 4-block groups (the fused launch
+keeps 2-block ones, so these compare the two group widths bit for bit).  The sync words are back
 at zero after every call, no wait expired, a second call right after the first gives the same bits,
 the layer's fused forward matches the oracle's layer, and replays of a captured graph equal the
 eager result."""
@@ -26,12 +28,18 @@ SINGLE = synth.Workload("single_expert_top1", 1, 1, 256, 128, (40,), 0, 1, 1)
 # the most local experts one call takes: 24.6 KB of per-expert tables in LDS, 1024 expert counters
 # in the sync buffer
 WIDE = synth.Workload("wide_e1024", 2048, 8, 512, 256, (24,), 512, 1024, 1)
+# The separate L2 kernel's 4-block groups (from 32 two-block groups per workgroup of the 512):
+# 1280 tokens top-1 over 4 experts at hidden 7168 (>= 80 regular m-tiles x 224 groups, staged weight
+# scales), and 1024 tokens top-2 over 1024 experts at hidden 1024 (mostly m-tiles of 1-2 rows, the
+# tiny phase, x 32 groups).
+WIDE_REG = synth.Workload("l2_4block_regular_e4", 4, 1, 7168, 2048, (1280,), 0, 4, 1)
+WIDE_TINY = synth.Workload("l2_4block_tiny_e1024", 1024, 2, 1024, 256, (1024,), 0, 1024, 1)
 DEC = synth.WORKLOADS[1]
 
 CASES = [(synth.WORKLOADS[0], 16), (DEC, 1), (DEC, 4), (DEC, 8), (MID, 300), (MID_PAD, 150), (ODD_K, 8),
-         (SINGLE, 40), (WIDE, 24)]
+         (SINGLE, 40), (WIDE, 24), (WIDE_REG, 1280), (WIDE_TINY, 1024)]
 IDS = ["tiny", "decode_t1", "decode_t4", "decode_t8", "mid", "mid_pad128", "odd_k640", "single_expert",
-       "wide_e1024"]
+       "wide_e1024", "l2_4block_regular", "l2_4block_tiny"]
 
 
 def make_layer(wl, T):
@@ -97,6 +105,8 @@ def test_fused_equals_separate(wl, T, calibrated):
     s, L, _ = make_layer(wl, T)
     w = s.gpu_w
     torch.cuda.synchronize()
+    if wl in (WIDE_REG, WIDE_TINY):  # enough 16-row m-tiles for the separate L2 kernel's 4-block groups
+        assert int(((L.counts + 15) // 16).sum().item()) * (wl.hidden // 32) >= 32 * 512
     gs_h = None
     if calibrated:
         separate(L, w)  # the amax scale, times 0.75 (a warm-up scale off by a factor)

@@ -38,6 +38,10 @@ MANY_MT = synth.Workload("many_mtiles_e4", 4, 1, 1024, 512, (4000,), 0, 4, 1, zi
 # put ~17 groups on every workgroup of the 16-row L2 kernel (the weight-scale copies of its loader
 # run ahead of the compute across group boundaries).
 SMALL_K1024 = synth.Workload("small_k1024_e4", 4, 2, 7168, 1024, (320,), 0, 4, 1)
+# Enough 16-row m-tiles for the 16-row L2 kernel's 4-block groups: top-1 over 4 experts, 1280 tokens
+# with block_m 16 forced, at least 80 m-tiles x 224 two-block groups of 7168 output columns, i.e.
+# at least 32 per workgroup of the 512 (reduction length 2048 with staged weight scales).
+SMALL_WIDE = synth.Workload("small_wide_l2_e4", 4, 1, 7168, 2048, (1280,), 0, 4, 1)
 # The degenerate routing: one expert, top-1 (every token's weight is 1), 40 tokens in one 256-row
 # tile whose rows 40..255 are padding, no tail tiles (intermediate 128, hidden 256).
 SINGLE = synth.Workload("single_expert_top1", 1, 1, 256, 128, (40,), 0, 1, 1)
@@ -266,15 +270,20 @@ def test_quantizer_hand_built_bytes():
     assert np_i32(scales).tolist() == [g["scales0"], g["scales1"]]
 
 
-def test_small_class_many_groups_short_k():
-    """16-row kernels only (block_m 16 forced), L2 with K = 1024 and ~17 groups per workgroup:
-    every stage against the oracle (h, y within 1e-3; end to end 1e-2 / 0.9999)."""
-    s = setup_for(SMALL_K1024, 320)
+@pytest.mark.parametrize("wl,T,wide", [(SMALL_K1024, 320, False), (SMALL_WIDE, 1280, True)],
+                         ids=["k1024_2block_groups", "k2048_4block_l2_groups"])
+def test_small_class_many_groups(wl, T, wide):
+    """16-row kernels only (block_m 16 forced): L2 with K = 1024 and ~17 two-block groups per
+    workgroup, and L2 with K = 2048 and enough m-tiles for 4-block groups; every stage against the
+    oracle (h, y within 1e-3; end to end 1e-2 / 0.9999)."""
+    s = setup_for(wl, T)
     ref = oracle_chain(s)
     L = run_gpu(s, block_m_override=16)
     check_tables(L, ref)
     sched = np_i32(L.sched)
     assert sched[1] >= 40 and sched[2] == 0  # >= 40 small m-tiles, no large ones
+    # the L2 kernel takes 4-block groups from 32 two-block groups (32 columns) per workgroup
+    assert (int(sched[1]) * (wl.hidden // 32) >= 32 * 512) == wide
     valid = ref["row_token"] >= 0
     err_h = rel_frob(bf16_t2np(L.h[:L.M_cap])[valid], ref["h"][valid])
     # L2 on the oracle's quantized h
@@ -289,7 +298,7 @@ def test_small_class_many_groups_short_k():
     err_y = rel_frob(bf16_t2np(y)[valid], ref["y"][valid])
     out = bf16_t2np(L.out[:L.T])
     err, cos = rel_frob(out, ref["out"]), cosine(out, ref["out"])
-    log(f"[small k1024] l1 {err_h:.2e} l2 {err_y:.2e} e2e {err:.2e} cos {cos:.7f}")
+    log(f"[small {wl.name}] l1 {err_h:.2e} l2 {err_y:.2e} e2e {err:.2e} cos {cos:.7f}")
     assert err_h <= STAGE_TOL and err_y <= STAGE_TOL and err <= E2E_TOL and cos >= E2E_COS
 
 
