@@ -616,7 +616,7 @@ GEMM_SRC = os.path.join(ROOT, "nvfp4_block_scaled_top_amd", "csrc", "gemm.hip")
 COPY_BYTES = 1 << 30  # the calibration kernel reads and writes this many bytes
 TRAFFIC_WORKLOADS = {"prefill": (3, 8192), "decode_t4": (1, 4), "decode_t8": (1, 8)}
 L1_LARGE = "gemm_large_kernel<true, false>"
-L1_SMALL = "gemm_small_kernel<true, 256, true, false>"
+L1_SMALL = "gemm_small_kernel<true, 256, true, false, 2>"
 
 
 def gemm_source_hash() -> str:
