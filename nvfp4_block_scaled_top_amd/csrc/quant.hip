@@ -153,7 +153,7 @@ hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int
   int nparts = amax_in_count;
   if (amax_in == nullptr && rows * cols <= kQuantSmallElems) {
     const int64_t nblk = rows * (cols / 16);
-    const int grid = (int)((nblk + kQuantSmallThreads - 1) / kQuantSmallThreads);
+    const int grid = (int)((nblk + kQuantSmallBlocks - 1) / kQuantSmallBlocks);
     hipLaunchKernelGGL(quant_small_kernel, dim3(grid > 0 ? grid : 1), dim3(kQuantSmallThreads), 0, stream, x, rows,
                        cols, row_valid, codes, scales, gs);
     return hipGetLastError();

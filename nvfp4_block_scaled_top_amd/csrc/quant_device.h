@@ -112,20 +112,51 @@ __device__ __forceinline__ float global_scale_of(float amax) {
   return amax > 0.0f ? 2688.0f / amax : 1.0f;  // IEEE division (correctly rounded)
 }
 
-// Small tensors (decode activations, up to 2^16 elements): one launch of ceil(blocks / 1024)
+// Small tensors (decode activations, up to 2^16 elements): one launch of ceil(blocks / 256)
 // workgroups of 1024 threads.  Every workgroup reduces the amax of the whole tensor itself (at most
 // 8 loads of 16 bytes per thread, all in flight, from L2 after the first workgroup), so no
-// workgroup waits for another; then each thread quantizes one 16-element block.
+// workgroup waits for another; then each quad of threads quantizes one 16-element block, 4
+// elements per thread (the per-element tests are most of the work, and a workgroup runs on one CU).
 constexpr int kQuantSmallThreads = 1024;
 constexpr int kQuantSmallLoads = 8;
 constexpr int64_t kQuantSmallElems = (int64_t)kQuantSmallThreads * kQuantSmallLoads * 8;
+constexpr int kQuantQuad = 4;                                          // threads per block
+constexpr int kQuantSmallBlocks = kQuantSmallThreads / kQuantQuad;    // blocks per workgroup
 
-// Workgroup `wg` of the single-launch form with a caller-given global scale: one block per thread.
+// Elements 4q..4q+3 of block b (q = lane % 4; the four lanes of a quad call it together with the
+// same b, so they share the block maximum through quad swaps): the block's scale (written by lane
+// q = 0) and its 4 codes (2 bytes).  !valid: zero codes and scale.  Same bits as quant_block.
+__device__ __forceinline__ void quant_block_quarter(const uint16_t* __restrict__ x, int64_t b, float gs, bool valid,
+                                                    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int q = (int)(threadIdx.x % kQuantQuad);
+  if (!valid) {
+    *reinterpret_cast<uint16_t*>(codes + b * 8 + 2 * q) = 0;
+    if (q == 0) scales[b] = 0;
+    return;
+  }
+  const u32x2 v = *reinterpret_cast<const u32x2*>(x + b * 16 + 4 * q);
+  uint32_t m = (v.x & 0x7FFFu) > ((v.x >> 16) & 0x7FFFu) ? (v.x & 0x7FFFu) : ((v.x >> 16) & 0x7FFFu);
+  const uint32_t m1 = (v.y & 0x7FFFu) > ((v.y >> 16) & 0x7FFFu) ? (v.y & 0x7FFFu) : ((v.y >> 16) & 0x7FFFu);
+  m = m > m1 ? m : m1;
+  uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+  m = m > o ? m : o;
+  o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+  m = m > o ? m : o;
+  float t[7];
+  const uint32_t sc = block_scale(m, gs, t);
+  const bool zs = sc == 0;
+  const uint32_t c = e2m1_code(v.x & 0xFFFFu, gs, t, zs) | (e2m1_code(v.x >> 16, gs, t, zs) << 4) |
+                     (e2m1_code(v.y & 0xFFFFu, gs, t, zs) << 8) | (e2m1_code(v.y >> 16, gs, t, zs) << 12);
+  *reinterpret_cast<uint16_t*>(codes + b * 8 + 2 * q) = (uint16_t)c;
+  if (q == 0) scales[b] = (uint8_t)sc;
+}
+
+// Workgroup `wg` of the single-launch form with a caller-given global scale: one block per quad.
 __device__ __forceinline__ void quant_gs_small_body(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                     float gs, uint8_t* __restrict__ codes,
                                                     uint8_t* __restrict__ scales, int wg) {
-  const int64_t b = (int64_t)wg * kQuantSmallThreads + threadIdx.x;
-  if (b < rows * (cols / 16)) quant_block(x, b, gs, codes, scales);
+  const int64_t b = (int64_t)wg * kQuantSmallBlocks + threadIdx.x / kQuantQuad;
+  if (b < rows * (cols / 16)) quant_block_quarter(x, b, gs, true, codes, scales);
 }
 
 // Workgroup `wg` of the small-tensor quantizer (1024 threads); red: [kQuantSmallThreads / kWave].
@@ -156,14 +187,9 @@ __device__ __forceinline__ void quant_small_body(const uint16_t* __restrict__ x,
   const float gs = global_scale_of(bf16_bits_to_f32(m));
   if (wg == 0 && threadIdx.x == 0) *gs_out = gs;
   const int64_t bpr = cols / 16;
-  const int64_t b = (int64_t)wg * kQuantSmallThreads + threadIdx.x;
-  if (b >= rows * bpr) return;
-  if (row_valid != nullptr && row_valid[b / bpr] < 0) {
-    *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{0u, 0u};
-    scales[b] = 0;
-    return;
-  }
-  quant_block(x, b, gs, codes, scales);
+  const int64_t b = (int64_t)wg * kQuantSmallBlocks + threadIdx.x / kQuantQuad;
+  if (b >= rows * bpr) return;  // whole quads leave together
+  quant_block_quarter(x, b, gs, row_valid == nullptr || row_valid[b / bpr] >= 0, codes, scales);
 }
 
 }  // namespace megamoe

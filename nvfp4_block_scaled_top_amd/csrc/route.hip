@@ -271,7 +271,7 @@ hipError_t launch_route_quant_small(const int32_t* topk_ids, int32_t T, int32_t 
                                     const float* gs_in, hipStream_t stream) {
   const size_t wcnt_bytes = (size_t)(kRouteChunk / kWave) * E * sizeof(int32_t);
   const int64_t nblk = (int64_t)T * (H / 16);
-  const int qgrid = (int)((nblk + kQuantSmallThreads - 1) / kQuantSmallThreads);
+  const int qgrid = (int)((nblk + kQuantSmallBlocks - 1) / kQuantSmallBlocks);
   hipLaunchKernelGGL(route_quant_small_kernel, dim3(1 + (qgrid > 0 ? qgrid : 1)), dim3(kRouteChunk), wcnt_bytes, stream,
                      topk_ids, T * k, k, e0, E, P, block_m_override, counts, eoff, poff, row_token, M_cap, token_rows,
                      sched, x, (int64_t)T, H, codes, scales, gs, gs_in);
