@@ -92,6 +92,45 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint16_t* __
   }
 }
 
+// The quantization pass for tensors of up to kQuadMaxBlocks blocks (e.g. decode's h, whose global
+// scale comes from the L1 amax slots): one block per quad of threads, as in the single-launch form,
+// so that the per-element tests of a few thousand blocks spread over four times the threads.
+// kGsIn: the caller's global scale; otherwise every workgroup reduces the amax partials.
+constexpr int64_t kQuadMaxBlocks = 1 << 16;
+template <bool kGsIn>
+__global__ __launch_bounds__(kQuantThreads) void quant_quad_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                   int64_t cols, const int32_t* __restrict__ row_valid,
+                                                                   const float* __restrict__ amax_src, int nparts,
+                                                                   const float* __restrict__ gs_in,
+                                                                   uint8_t* __restrict__ codes,
+                                                                   uint8_t* __restrict__ scales,
+                                                                   float* __restrict__ gs_out) {
+  float gs;
+  if (kGsIn) {
+    gs = *gs_in;
+  } else {
+    __shared__ uint32_t red[kQuantThreads / kWave];
+    uint32_t am = 0;
+    for (int j = threadIdx.x; j < nparts; j += blockDim.x) {
+      const uint32_t b = __float_as_uint(amax_src[j]);  // non-negative: uint order is float order
+      am = am > b ? am : b;
+    }
+    am = block_max_u32(am, red);
+    gs = global_scale_of(__uint_as_float(am));
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
+  }
+  const int64_t bpr = cols / 16, nblk = rows * bpr;
+  const int64_t stride = (int64_t)gridDim.x * (blockDim.x / kQuantQuad);
+  // the four threads of a quad hold the same b in every iteration
+  for (int64_t b = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kQuantQuad; b < nblk; b += stride)
+    quant_block_quarter(x, b, gs, row_valid == nullptr || row_valid[b / bpr] >= 0, codes, scales);
+}
+
+static unsigned quant_quad_grid(int64_t nblk) {
+  const int64_t g = (nblk * kQuantQuad + kQuantThreads - 1) / kQuantThreads;
+  return (unsigned)(g < 1 ? 1 : g > 2048 ? 2048 : g);
+}
+
 __global__ __launch_bounds__(kQuantSmallThreads) void quant_small_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                                          int64_t cols,
                                                                          const int32_t* __restrict__ row_valid,
@@ -127,6 +166,11 @@ hipError_t launch_quant_gs(const uint16_t* x, int64_t rows, int64_t cols, const 
                            uint8_t* codes, uint8_t* scales, hipStream_t stream) {
   const int64_t nblk = rows * (cols / 16);
   if (nblk == 0) return hipSuccess;
+  if (nblk <= kQuadMaxBlocks) {
+    hipLaunchKernelGGL(quant_quad_kernel<true>, dim3(quant_quad_grid(nblk)), dim3(kQuantThreads), 0, stream, x, rows,
+                       cols, row_valid, nullptr, 0, gs, codes, scales, nullptr);
+    return hipGetLastError();
+  }
   int64_t grid = (nblk + kQuantThreads - 1) / kQuantThreads;
   if (grid > 2048) grid = 2048;
   hipLaunchKernelGGL(quant_gs_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream, x, rows, cols, row_valid,
@@ -166,6 +210,11 @@ hipError_t launch_quant(const uint16_t* x, int64_t rows, int64_t cols, const int
     amax_src = ws;
   }
   const int64_t nblk = rows * (cols / 16);
+  if (nblk <= kQuadMaxBlocks) {
+    hipLaunchKernelGGL(quant_quad_kernel<false>, dim3(quant_quad_grid(nblk)), dim3(kQuantThreads), 0, stream, x, rows,
+                       cols, row_valid, amax_src, nparts, nullptr, codes, scales, gs);
+    return hipGetLastError();
+  }
   int64_t grid = (nblk + kQuantThreads - 1) / kQuantThreads;
   if (grid > 2048) grid = 2048;  // grid-stride beyond: every workgroup re-reduces the partial maxima
   if (grid < 1) grid = 1;
