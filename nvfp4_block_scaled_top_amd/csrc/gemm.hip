@@ -323,7 +323,7 @@ __device__ __forceinline__ void publish_fence() {
 constexpr int kSpinLimit = 1 << 18;
 __device__ __forceinline__ void wait_count(const uint32_t* c, uint32_t target, uint32_t* err) {
   for (int it = 0; it < kSpinLimit; ++it) {
-    if (__builtin_amdgcn_readfirstlane(ld_dev(c)) >= target) {
+    if ((uint32_t)__builtin_amdgcn_readfirstlane(ld_dev(c)) >= target) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       return;
     }
