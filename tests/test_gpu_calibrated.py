@@ -89,14 +89,16 @@ MID = synth.Workload("mid_zipf_e24", 32, 4, 512, 256, (300,), 0, 24, 1, zipf=Tru
 MANY_MT = synth.Workload("many_mtiles_e4", 4, 1, 1024, 512, (4000,), 0, 4, 1, zipf=True)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("wl,T", [(synth.WORKLOADS[0], 16), (synth.WORKLOADS[1], 8), (MID, 300),
-                                  (synth.WORKLOADS[2], 512), (MANY_MT, 4000)],
-                         ids=["tiny", "decode_t8", "mid", "t512_pad128", "many_mtiles"])
+                                  (synth.WORKLOADS[2], 512), (MANY_MT, 4000), (synth.WORKLOADS[3], 8192)],
+                         ids=["tiny", "decode_t8", "mid", "t512_pad128", "many_mtiles", "t8192_zipf"])
 def test_l1_nvfp4_equals_l1_then_quantizer(wl, T):
     """moe_grouped_gemm_l1_silu_nvfp4 (h quantized in the GEMM epilogue) gives, on every row that
     holds an assignment, the bits nvfp4_quantize_act_gs writes for the bf16 h of the plain L1; the
     other rows are left alone; the amax slots are those of the plain L1.  Scales: the amax-derived
-    one, and 4x it (saturating blocks)."""
+    one, and 4x it (saturating blocks).  The 8192-token Zipf routing runs the 256-row kernel's
+    epilogue over the full prefill tile list (53 experts, full and tail tiles)."""
     s = make_setup(wl, T)
     x, ids, _ = s.dev_inputs()
     L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
