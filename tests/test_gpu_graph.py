@@ -1,4 +1,4 @@
-"""HIP-graph capture of one layer forward: every replay equals the eager result bit for bit,
+"""HIP-graph capture of one layer forward (mid-size, decode T=8 and the 8192- and 512-token prefills): every replay equals the eager result bit for bit,
 with eager work and synchronizations between replays (the benchmark replays captured steps)."""
 import numpy as np
 import pytest
@@ -13,7 +13,15 @@ pytestmark = pytest.mark.gpu
 MID = synth.Workload("mid_zipf_e24", 32, 4, 512, 256, (300,), 0, 24, 1, zipf=True)
 
 
-@pytest.mark.parametrize("wl,T", [(MID, 300), (synth.WORKLOADS[1], 8)], ids=["mid", "decode_t8"])
+# the prefill launch sequences bench.py replays: three-kernel routing, the amax pass, both tile
+# classes (the 512-token one with 4-block L2 groups)
+PREFILL = [(synth.WORKLOADS[3], 8192), (synth.WORKLOADS[2], 512)]
+CASES = [(MID, 300), (synth.WORKLOADS[1], 8)] + PREFILL
+IDS = ["mid", "decode_t8", "t8192_zipf", "t512_pad128"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wl,T", CASES, ids=IDS)
 def test_graph_replays_match_eager(wl, T):
     s = make_setup(wl, T)
     x, ids, wts = s.dev_inputs()
@@ -37,7 +45,8 @@ def test_graph_replays_match_eager(wl, T):
         assert np.array_equal(np_i32(L.h[:L.M_cap].view(torch.int16))[valid], eager_h[valid]), r
 
 
-@pytest.mark.parametrize("wl,T", [(MID, 300), (synth.WORKLOADS[1], 8)], ids=["mid", "decode_t8"])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wl,T", CASES, ids=IDS)
 def test_graph_replays_calibrated(wl, T):
     """The calibrated forward (x quantized in the routing launch, h written as NVFP4 by L1)
     captured once: every replay equals the eager result, with h's codes poisoned in between."""
