@@ -1,5 +1,6 @@
-"""HIP-graph capture of one layer forward (mid-size, decode T=8 and the 8192- and 512-token prefills): every replay equals the eager result bit for bit,
-with eager work and synchronizations between replays (the benchmark replays captured steps)."""
+"""HIP-graph capture of one layer forward (mid-size, decode T=8, and the 8192- and 512-token
+prefills): every replay equals the eager result bit for bit, with eager work and synchronizations
+between replays (the benchmark replays captured steps)."""
 import numpy as np
 import pytest
 import torch
