@@ -6,8 +6,8 @@ one (an expert's L2 waits for its own L1 groups only).  Workloads: decode at T =
 the 48-expert share, the tiny and odd-K shapes (128-element chunks), padded rows,
 experts of up to 50 rows (several 16-row m-tiles each), a single expert, 1024 local experts, and two
 routings with enough m-tiles that the separate L2 kernel takes 4-block groups, with 256- and
-128-element chunks (the fused launch keeps 2-block ones, so these compare the two group widths bit
-for bit).  The sync words are back
+128-element chunks and at the layer's real shape with staged scales (the fused launch keeps 2-block
+ones, so these compare the two group widths bit for bit).  The sync words are back
 at zero after every call, no wait expired, a second call right after the first gives the same bits,
 the layer's fused forward matches the oracle's layer, and replays of a captured graph equal the
 eager result."""
@@ -38,12 +38,15 @@ WIDE_TINY = synth.Workload("l2_4block_tiny_e1024", 1024, 2, 1024, 256, (1024,), 
 # ... and with 128-element chunks (intermediate 640, an odd multiple of 128): 3072 tokens top-2
 # over 256 experts at hidden 2048 (about 24 rows per expert, two 16-row m-tiles, x 64 groups).
 WIDE_CH128 = synth.Workload("l2_4block_ch128_e256", 256, 2, 2048, 640, (3072,), 0, 256, 1)
+# ... and at the layer's real shape with staged weight scales: 32 tokens top-6 over all 384 experts
+# (about 160 m-tiles, mostly of one row: the tiny phase, x 224 groups).
+WIDE_TINY_REAL = synth.Workload("l2_4block_tiny_e384", 384, 6, 7168, 2048, (32,), 0, 384, 1)
 DEC = synth.WORKLOADS[1]
 
 CASES = [(synth.WORKLOADS[0], 16), (DEC, 1), (DEC, 4), (DEC, 8), (MID, 300), (MID_PAD, 150), (ODD_K, 8),
-         (SINGLE, 40), (WIDE, 24), (WIDE_REG, 1280), (WIDE_TINY, 1024), (WIDE_CH128, 3072)]
+         (SINGLE, 40), (WIDE, 24), (WIDE_REG, 1280), (WIDE_TINY, 1024), (WIDE_CH128, 3072), (WIDE_TINY_REAL, 32)]
 IDS = ["tiny", "decode_t1", "decode_t4", "decode_t8", "mid", "mid_pad128", "odd_k640", "single_expert",
-       "wide_e1024", "l2_4block_regular", "l2_4block_tiny", "l2_4block_ch128"]
+       "wide_e1024", "l2_4block_regular", "l2_4block_tiny", "l2_4block_ch128", "l2_4block_tiny_e384"]
 
 
 def make_layer(wl, T):
@@ -109,7 +112,7 @@ def test_fused_equals_separate(wl, T, calibrated):
     s, L, _ = make_layer(wl, T)
     w = s.gpu_w
     torch.cuda.synchronize()
-    if wl in (WIDE_REG, WIDE_TINY, WIDE_CH128):  # enough 16-row m-tiles for the separate L2 kernel's 4-block groups
+    if wl in (WIDE_REG, WIDE_TINY, WIDE_CH128, WIDE_TINY_REAL):  # enough 16-row m-tiles for 4-block L2 groups
         assert int(((L.counts + 15) // 16).sum().item()) * (wl.hidden // 32) >= 32 * 512
     gs_h = None
     if calibrated:
