@@ -78,8 +78,14 @@ def gpu_routing(wl, T, seed=0, dev="cuda:0"):
     return logits, ids, wts, np.bincount(loc, minlength=wl.num_experts)
 
 
+# The layer's weights carry the packed copy of their codes (MoEWeights.pack), which the 16-row
+# kernels read; --unpacked measures them on the row-major codes instead.
+PACKED = True
+
+
 def build_weights(wl, active, copies, dev):
-    """NVFP4 weights for the local experts, quantized on the GPU; experts with no token stay unset."""
+    """NVFP4 weights for the local experts, quantized on the GPU (and packed unless --unpacked);
+    experts with no token stay unset."""
     import torch
     from nvfp4_block_scaled_top_amd import layer, synth
 
@@ -88,6 +94,8 @@ def build_weights(wl, active, copies, dev):
         w13, w2 = synth.expert_weights(wl, wl.expert_begin + e, device=dev)
         layer.quantize_expert_into(W, e, w13, w2)
         del w13, w2
+    if PACKED:
+        W.pack()
     torch.cuda.synchronize()
     return [W] + [W.clone() for _ in range(copies - 1)]
 
@@ -616,7 +624,7 @@ GEMM_SRC = os.path.join(ROOT, "nvfp4_block_scaled_top_amd", "csrc", "gemm.hip")
 COPY_BYTES = 1 << 30  # the calibration kernel reads and writes this many bytes
 TRAFFIC_WORKLOADS = {"prefill": (3, 8192), "decode_t4": (1, 4), "decode_t8": (1, 8)}
 L1_LARGE = "gemm_large_kernel<true, false>"
-L1_SMALL = "gemm_small_kernel<true, 256, true, false, 2>"
+L1_SMALL = "gemm_small_kernel<true, 256, true, false, 2, true>"  # the packed-code instantiation
 
 
 def gemm_source_hash() -> str:
@@ -838,6 +846,8 @@ def main():
     ap.add_argument("--decode-seeds", type=int, default=64, help="routing seeds of the decode aggregate (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--unpacked", action="store_true",
+                    help="weights without the packed copy of their codes (the 16-row kernels read the row-major codes)")
     ap.add_argument("--quick", action="store_true", help="prefill only, no CPU baseline")
     ap.add_argument("--traffic-pass", choices=tuple(TRAFFIC_WORKLOADS),
                     help="launch sequence for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (no timing)")
@@ -852,6 +862,8 @@ def main():
     ap.add_argument("--ceilings-only", action="store_true",
                     help="print the measured ceilings (context of the bench line) as JSON and exit")
     args = ap.parse_args()
+    global PACKED
+    PACKED = not args.unpacked
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
         return

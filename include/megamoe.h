@@ -349,6 +349,55 @@ int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, con
                             int32_t max_rows_per_expert, void* y_bf16, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * nvfp4_pack_weight_codes - a second copy of NVFP4 weight codes in the layout the 16-row GEMM
+ * kernels stream fastest (the *_packed GEMMs below).
+ *
+ * Same codes, permuted; no arithmetic (the weights are those of CURRENT_BUG.md@2e65594, "Test
+ * Plan" Phase 1: E2M1 codes, two per byte).  codes [rows, K/2] row-major (e.g. W13 with rows =
+ * E * 2I and K = H, or W2 with rows = E * H and K = I) -> packed [rows * K/2] bytes: for 16-row
+ * block b (rows 16b .. 16b+15), 256-element chunk c of K and half q (0, 1) of the chunk's
+ * 2 KB, the 1 KB at byte ((b * (K/256) + c) * 2 + q) * 1024 holds, for L = 16g + r (r < 16,
+ * g < 4), the 16 code bytes 32g + 16q .. 32g + 16q + 15 of chunk c of row 16b + r at 16L.  The
+ * scales keep their row-major layout.  Caller-owned device buffers; the call only enqueues on
+ * `stream`.  Errors: rows not a positive multiple of 16 or K not a positive multiple of 256 ->
+ * -2; NULL pointer -> -1.
+ * ---------------------------------------------------------------------------------------- */
+int32_t nvfp4_pack_weight_codes(const uint8_t* codes, int64_t rows, int64_t K, uint8_t* packed, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_grouped_gemm_l1_silu_packed, moe_grouped_gemm_l1_silu_nvfp4_packed,
+ * moe_grouped_gemm_l2_packed - the three grouped GEMMs above, with one more argument after the
+ * weights' global scales: w13_packed / w2_packed, the same weight codes as packed by
+ * nvfp4_pack_weight_codes (W13 as [E * 2I] rows of K = H, W2 as [E * H] rows of K = I).
+ *
+ * Same operation and the same results, bit for bit.  The 16-row kernels read the packed copy
+ * (each load instruction 1 KB contiguous, non-temporal); the 256-row kernels read the row-major
+ * codes, which stay required.  Errors as for the unpacked calls, and: packed NULL -> -1;
+ * L2 with I not a multiple of 256 -> -2.
+ * ---------------------------------------------------------------------------------------- */
+int32_t moe_grouped_gemm_l1_silu_packed(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                        const int32_t* row_token, const int32_t* padded_offsets,
+                                        const int32_t* counts, const int32_t* sched, const uint8_t* w13_codes,
+                                        const uint8_t* w13_scales, const float* w13_gs, const uint8_t* w13_packed,
+                                        int32_t E, int32_t H, int32_t I, int64_t M_cap, int32_t block_m_override,
+                                        int32_t max_rows_per_expert, void* h_bf16, float* h_amax_parts,
+                                        void* stream);
+int32_t moe_grouped_gemm_l1_silu_nvfp4_packed(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                              const int32_t* row_token, const int32_t* padded_offsets,
+                                              const int32_t* counts, const int32_t* sched, const uint8_t* w13_codes,
+                                              const uint8_t* w13_scales, const float* w13_gs,
+                                              const uint8_t* w13_packed, int32_t E, int32_t H, int32_t I,
+                                              int64_t M_cap, int32_t block_m_override, int32_t max_rows_per_expert,
+                                              const float* h_gs, uint8_t* h_codes, uint8_t* h_scales,
+                                              float* h_amax_parts, void* stream);
+int32_t moe_grouped_gemm_l2_packed(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs,
+                                   const int32_t* padded_offsets, const int32_t* counts, const int32_t* sched,
+                                   const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
+                                   const uint8_t* w2_packed, int32_t E, int32_t H, int32_t I, int64_t M_cap,
+                                   int32_t block_m_override, int32_t max_rows_per_expert, void* y_bf16,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * moe_grouped_ffn_fused - L1 gate+up with SiLU(gate)*up, the requantization of h and L2 down in
  * one persistent launch (experts taken in 16-row m-tiles: decode sizes).
  *

@@ -251,12 +251,13 @@ int32_t nvfp4_quantize_act_gs(const void* x_bf16, int64_t rows, int64_t cols, co
                                        codes, scales, static_cast<hipStream_t>(stream)));
 }
 
-int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
-                                 const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
-                                 const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
-                                 const float* w13_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap,
-                                 int32_t block_m_override, int32_t max_rows_per_expert, void* h_bf16,
-                                 float* h_amax_parts, void* stream) {
+// The three grouped GEMMs, with the packed weight codes (nvfp4_pack_weight_codes) or without.
+static int32_t gemm_l1(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, const int32_t* row_token,
+                       const int32_t* padded_offsets, const int32_t* counts, const int32_t* sched,
+                       const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
+                       const uint8_t* w13_packed, int32_t E, int32_t H, int32_t I, int64_t M_cap,
+                       int32_t block_m_override, int32_t max_rows_per_expert, void* h_bf16, float* h_amax_parts,
+                       void* stream) {
   GemmClasses cls;
   if (!gemm_shape_ok(E, H, I, M_cap) || !classes_of(block_m_override, max_rows_per_expert, &cls))
     return MEGAMOE_ERR_SHAPE;
@@ -269,15 +270,16 @@ int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales
     return launch_status(launch_fill_f32(h_amax_parts, MEGAMOE_L1_AMAX_PARTS, 0.0f, static_cast<hipStream_t>(stream)));
   GemmArgs a{x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
              E, H, I, h_bf16, h_amax_parts, 0};
+  a.w_packed = w13_packed;
   return launch_status(launch_gemm_l1(a, cls, static_cast<hipStream_t>(stream)));
 }
 
-int32_t moe_grouped_gemm_l1_silu_nvfp4(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
-                                       const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
-                                       const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
-                                       const float* w13_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap,
-                                       int32_t block_m_override, int32_t max_rows_per_expert, const float* h_gs,
-                                       uint8_t* h_codes, uint8_t* h_scales, float* h_amax_parts, void* stream) {
+static int32_t gemm_l1_nvfp4(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                             const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
+                             const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                             const float* w13_gs, const uint8_t* w13_packed, int32_t E, int32_t H, int32_t I,
+                             int64_t M_cap, int32_t block_m_override, int32_t max_rows_per_expert, const float* h_gs,
+                             uint8_t* h_codes, uint8_t* h_scales, float* h_amax_parts, void* stream) {
   GemmClasses cls;
   if (!gemm_shape_ok(E, H, I, M_cap) || !classes_of(block_m_override, max_rows_per_expert, &cls))
     return MEGAMOE_ERR_SHAPE;
@@ -294,14 +296,15 @@ int32_t moe_grouped_gemm_l1_silu_nvfp4(const uint8_t* x_codes, const uint8_t* x_
   a.q_gs = h_gs;
   a.q_codes = h_codes;
   a.q_scales = h_scales;
+  a.w_packed = w13_packed;
   return launch_status(launch_gemm_l1(a, cls, static_cast<hipStream_t>(stream)));
 }
 
-int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs,
-                            const int32_t* padded_offsets, const int32_t* counts, const int32_t* sched,
-                            const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs, int32_t E, int32_t H,
-                            int32_t I, int64_t M_cap, int32_t block_m_override, int32_t max_rows_per_expert,
-                            void* y_bf16, void* stream) {
+static int32_t gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs,
+                       const int32_t* padded_offsets, const int32_t* counts, const int32_t* sched,
+                       const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs, const uint8_t* w2_packed,
+                       int32_t E, int32_t H, int32_t I, int64_t M_cap, int32_t block_m_override,
+                       int32_t max_rows_per_expert, void* y_bf16, void* stream) {
   GemmClasses cls;
   if (!gemm_shape_ok(E, H, I, M_cap) || !classes_of(block_m_override, max_rows_per_expert, &cls))
     return MEGAMOE_ERR_SHAPE;
@@ -312,7 +315,84 @@ int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, con
   if (M_cap == 0) return MEGAMOE_OK;  // no rows: nothing to compute or write
   GemmArgs a{h_codes, h_scales, h_gs, nullptr, padded_offsets, counts, sched, w2_codes, w2_scales, w2_gs,
              E, I, H, y_bf16, nullptr, 0};
+  a.w_packed = w2_packed;
   return launch_status(launch_gemm_l2(a, cls, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_grouped_gemm_l1_silu(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                 const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
+                                 const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                 const float* w13_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap,
+                                 int32_t block_m_override, int32_t max_rows_per_expert, void* h_bf16,
+                                 float* h_amax_parts, void* stream) {
+  return gemm_l1(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
+                 nullptr, E, H, I, M_cap, block_m_override, max_rows_per_expert, h_bf16, h_amax_parts, stream);
+}
+
+int32_t moe_grouped_gemm_l1_silu_packed(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                        const int32_t* row_token, const int32_t* padded_offsets,
+                                        const int32_t* counts, const int32_t* sched, const uint8_t* w13_codes,
+                                        const uint8_t* w13_scales, const float* w13_gs, const uint8_t* w13_packed,
+                                        int32_t E, int32_t H, int32_t I, int64_t M_cap, int32_t block_m_override,
+                                        int32_t max_rows_per_expert, void* h_bf16, float* h_amax_parts,
+                                        void* stream) {
+  if (!w13_packed) return MEGAMOE_ERR_NULL;  // K = H is a multiple of 256 for every accepted shape
+  return gemm_l1(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
+                 w13_packed, E, H, I, M_cap, block_m_override, max_rows_per_expert, h_bf16, h_amax_parts, stream);
+}
+
+int32_t moe_grouped_gemm_l1_silu_nvfp4(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                       const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
+                                       const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                       const float* w13_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap,
+                                       int32_t block_m_override, int32_t max_rows_per_expert, const float* h_gs,
+                                       uint8_t* h_codes, uint8_t* h_scales, float* h_amax_parts, void* stream) {
+  return gemm_l1_nvfp4(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales,
+                       w13_gs, nullptr, E, H, I, M_cap, block_m_override, max_rows_per_expert, h_gs, h_codes,
+                       h_scales, h_amax_parts, stream);
+}
+
+int32_t moe_grouped_gemm_l1_silu_nvfp4_packed(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                              const int32_t* row_token, const int32_t* padded_offsets,
+                                              const int32_t* counts, const int32_t* sched, const uint8_t* w13_codes,
+                                              const uint8_t* w13_scales, const float* w13_gs,
+                                              const uint8_t* w13_packed, int32_t E, int32_t H, int32_t I,
+                                              int64_t M_cap, int32_t block_m_override, int32_t max_rows_per_expert,
+                                              const float* h_gs, uint8_t* h_codes, uint8_t* h_scales,
+                                              float* h_amax_parts, void* stream) {
+  if (!w13_packed) return MEGAMOE_ERR_NULL;
+  return gemm_l1_nvfp4(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales,
+                       w13_gs, w13_packed, E, H, I, M_cap, block_m_override, max_rows_per_expert, h_gs, h_codes,
+                       h_scales, h_amax_parts, stream);
+}
+
+int32_t moe_grouped_gemm_l2(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs,
+                            const int32_t* padded_offsets, const int32_t* counts, const int32_t* sched,
+                            const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs, int32_t E, int32_t H,
+                            int32_t I, int64_t M_cap, int32_t block_m_override, int32_t max_rows_per_expert,
+                            void* y_bf16, void* stream) {
+  return gemm_l2(h_codes, h_scales, h_gs, padded_offsets, counts, sched, w2_codes, w2_scales, w2_gs, nullptr, E, H, I,
+                 M_cap, block_m_override, max_rows_per_expert, y_bf16, stream);
+}
+
+int32_t moe_grouped_gemm_l2_packed(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs,
+                                   const int32_t* padded_offsets, const int32_t* counts, const int32_t* sched,
+                                   const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
+                                   const uint8_t* w2_packed, int32_t E, int32_t H, int32_t I, int64_t M_cap,
+                                   int32_t block_m_override, int32_t max_rows_per_expert, void* y_bf16,
+                                   void* stream) {
+  if (I % 256 != 0) return MEGAMOE_ERR_SHAPE;  // the packed layout is in 256-element chunks of K = I
+  if (!w2_packed) return MEGAMOE_ERR_NULL;
+  return gemm_l2(h_codes, h_scales, h_gs, padded_offsets, counts, sched, w2_codes, w2_scales, w2_gs, w2_packed, E, H,
+                 I, M_cap, block_m_override, max_rows_per_expert, y_bf16, stream);
+}
+
+int32_t nvfp4_pack_weight_codes(const uint8_t* codes, int64_t rows, int64_t K, uint8_t* packed, void* stream) {
+  if (rows < 16 || rows % 16 != 0 || K < 256 || K % 256 != 0) return MEGAMOE_ERR_SHAPE;
+  if (!codes || !packed) return MEGAMOE_ERR_NULL;
+  const int32_t dev = check_device();
+  if (dev != MEGAMOE_OK) return dev;
+  return launch_status(launch_pack_codes16(codes, rows, K, packed, static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_combine(const void* y_bf16, const int32_t* token_rows, const float* topk_weights, int32_t T, int32_t k,

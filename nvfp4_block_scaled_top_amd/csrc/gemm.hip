@@ -98,8 +98,9 @@ __device__ __forceinline__ float silu_f32(float g) {
 // about 2 VALU instructions per weight byte and lane; the design keeps every other VALU cost per
 // weight byte small and every CU equally busy:
 //  * work unit = a group: kSNb (small_nb) 16-column MFMA blocks of one m-tile over the whole K
-//    (L1 block j: MFMA columns 0-7 are gate rows of h columns j0+8j.., columns 8-15 the matching
-//    up rows, paired after the reduction with a lane shuffle; L2 block j: weight rows j0+16j..);
+//    (L1 blocks 2i and 2i+1: the gate rows and the up rows of h columns j0+16i..+15, so that
+//    every weight load instruction reads 16 consecutive rows and gate and up of an h column meet
+//    in the same lane after the reduction; L2 block j: weight rows j0+16j..);
 //    L2 takes kSNbWide blocks per group when there are many groups per workgroup (see kSNbWide).
 //    The width changes neither the K split nor any summation order: both give the same bits.
 //    The groups of all small m-tiles are laid end to end and each workgroup takes an equal
@@ -407,11 +408,14 @@ struct SmallSync {
 
 // One pass of the small class over part `part` of `nparts` of its group lists (tiny m-tiles,
 // then regular ones), for one workgroup.  inv: the pass's 1 / (gs_a * gs_w[e]).
-template <bool kL1, int NB, int CH, bool kStaged, bool kQOut, bool kDev>
+// kPacked: the weight codes come from the packed copy (p.w_packed, see pack_codes16_kernel) with
+// non-temporal loads, 1 KB contiguous per load instruction, instead of from the row-major codes.
+template <bool kL1, int NB, int CH, bool kStaged, bool kQOut, bool kDev, bool kPacked = false>
 __device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<NB>& L, const float* inv,
                                            int64_t part, int64_t nparts, uint32_t& amax_bits, int& parity,
                                            const SmallSync& sync) {
   static_assert(!kStaged || CH == 256, "staged scales copy whole 16-byte pieces: one per 256-element chunk");
+  static_assert(!kPacked || CH == 256, "the packed codes are laid out in 256-element chunks");
   static_assert(!kL1 || NB % 2 == 0, "L1 NVFP4 h: a group holds whole 16-column blocks of h");
   constexpr int kSNb = NB;
   constexpr int kQ = CH / 128;
@@ -495,17 +499,23 @@ __device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<NB>
       const float* red = reinterpret_cast<const float*>(&L.red[parity][0][0][0]);
       uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
       const int row = 4 * g + wave;  // MFMA output row of accumulator element `wave`
-      uint32_t hq[kSNb];             // L1: bf16 h of column 8j + r16 (lanes r16 < 8)
-#pragma unroll
-      for (int j = 0; j < kSNb; ++j) {
+      // partial sums of block j, column `lane`, accumulator row `wave`, added in wave order
+      auto reduced = [&](int j) {
         float r = red[((0 * kSNb + j) * kWave + lane) * 4 + wave];
         for (int w = 1; w < ks; ++w) r += red[((w * kSNb + j) * kWave + lane) * 4 + wave];
-        if (kL1) {
-          const float up_raw = __shfl(r, lane + 8, kWave);  // column c+8 holds the up row of c
-          const int hc = 8 * j + r16;
-          const uint32_t hb = f32_to_bf16_bits(silu_f32(r * invg) * (up_raw * invg));
-          hq[j] = hb;
-          if (r16 < 8 && hc < cg.n && row < cg.rows_left) {
+        return r;
+      };
+      if constexpr (kL1) {
+        // block 2i holds the gate rows and block 2i+1 the up rows of h columns j0 + 16i + r16:
+        // gate and up of a column meet in the same lane
+        uint32_t hq[kSNb / 2];  // bf16 h of column 16i + r16
+#pragma unroll
+        for (int i = 0; i < kSNb / 2; ++i) {
+          const float rg = reduced(2 * i), ru = reduced(2 * i + 1);
+          const int hc = 16 * i + r16;
+          const uint32_t hb = f32_to_bf16_bits(silu_f32(rg * invg) * (ru * invg));
+          hq[i] = hb;
+          if (hc < cg.n && row < cg.rows_left) {
             if (!quant_out) {
               uint16_t* dst = out + (int64_t)(cg.row0 + row) * p.N + cg.j0 + hc;
               if (kDevOut) st_dev(dst, (uint16_t)hb);
@@ -514,50 +524,51 @@ __device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<NB>
             const uint32_t mag = hb & 0x7FFFu;
             amax_bits = amax_bits > mag ? amax_bits : mag;
           }
-        } else {
+        }
+        if constexpr (quant_out) {
+          // NVFP4 h: the 16 columns 16i.. of row `row` (one 16-element block) are the 16 lanes
+          // 16g + e, register i.  The 16 lanes reduce the block's amax, each derives the block
+          // scale and codes its own element (the quantizer's block_scale / e2m1_code), and the
+          // codes are gathered into lane 16g (element 2k in the low nibble of byte k), which stores
+          // the block.
+#pragma unroll
+          for (int i = 0; i < kSNb / 2; ++i) {
+            const uint32_t e0 = hq[i] & 0xFFFFu;
+            uint32_t m = e0 & 0x7FFFu;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+              const uint32_t t = __shfl_xor(m, o, kWave);
+              m = m > t ? m : t;
+            }
+            float th[7];
+            const uint32_t sc = block_scale(m, gs_q, th);
+            const uint32_t c = e2m1_code(e0, gs_q, th, sc == 0);
+            const uint32_t b1 = c | (__shfl_xor(c, 1, kWave) << 4);     // lane 2k: byte k
+            const uint32_t b2 = b1 | (__shfl_xor(b1, 2, kWave) << 8);   // lane 4k: bytes 2k, 2k+1
+            const uint32_t b4 = b2 | (__shfl_xor(b2, 4, kWave) << 16);  // lane 8k: bytes 4k..4k+3
+            const uint32_t hi = __shfl_xor(b4, 8, kWave);               // lane 16g: bytes 4..7
+            if (r16 == 0 && 16 * i < cg.n && row < cg.rows_left) {
+              const int64_t orow = cg.row0 + row;
+              const int col = cg.j0 + 16 * i;
+              uint8_t* cdst = p.q_codes + orow * (p.N / 2) + col / 2;
+              uint8_t* sdst = p.q_scales + orow * (p.N / 16) + col / 16;
+              if (kDevOut) {
+                st_dev(reinterpret_cast<uint64_t*>(cdst), (uint64_t)b4 | ((uint64_t)hi << 32));
+                st_dev(sdst, (uint8_t)sc);
+              } else {
+                *reinterpret_cast<u32x2*>(cdst) = u32x2{b4, hi};
+                *sdst = (uint8_t)sc;
+              }
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kSNb; ++j) {
+          const float r = reduced(j);
           const int rc = 16 * j + r16;
           if (rc < cg.n && row < cg.rows_left)
             out[(int64_t)(cg.row0 + row) * p.N + cg.j0 + rc] = (uint16_t)f32_to_bf16_bits(r * invg);
-        }
-      }
-      if constexpr (quant_out) {
-        // NVFP4 h: the 16 columns 16b.. of row `row` are blocks j = 2b, 2b+1, element e in lane
-        // 16g + e % 8, register 2b + e / 8 (groups hold whole blocks: I % 16 == 0).  The 8 lanes
-        // reduce the block's amax, each derives the block scale and codes its own 2 elements
-        // (the quantizer's block_scale / e2m1_code), and lane 16g assembles and stores the block.
-#pragma unroll
-        for (int b = 0; b < kSNb / 2; ++b) {
-          const uint32_t e0 = hq[2 * b] & 0xFFFFu, e1 = hq[2 * b + 1] & 0xFFFFu;  // elements r16, 8 + r16
-          uint32_t m = (e0 & 0x7FFFu) > (e1 & 0x7FFFu) ? (e0 & 0x7FFFu) : (e1 & 0x7FFFu);
-#pragma unroll
-          for (int o = 1; o < 8; o <<= 1) {
-            const uint32_t t = __shfl_xor(m, o, kWave);
-            m = m > t ? m : t;
-          }
-          float th[7];
-          const uint32_t sc = block_scale(m, gs_q, th);
-          const uint32_t cc = e2m1_code(e0, gs_q, th, sc == 0) | (e2m1_code(e1, gs_q, th, sc == 0) << 8);
-          // even lane 2i: byte i (elements 2i, 2i+1) in bits 0-7, byte i + 4 in bits 8-15
-          const uint32_t pr = cc | (__shfl_xor(cc, 1, kWave) << 4);
-          const int base = lane & ~15;
-          const uint32_t p1 = __shfl(pr, base + 2, kWave), p2 = __shfl(pr, base + 4, kWave),
-                         p3 = __shfl(pr, base + 6, kWave);
-          if (r16 == 0 && row < cg.rows_left) {
-            const uint32_t lo = (pr & 0xFFu) | ((p1 & 0xFFu) << 8) | ((p2 & 0xFFu) << 16) | ((p3 & 0xFFu) << 24);
-            const uint32_t hi = ((pr >> 8) & 0xFFu) | (((p1 >> 8) & 0xFFu) << 8) | (((p2 >> 8) & 0xFFu) << 16) |
-                                (((p3 >> 8) & 0xFFu) << 24);
-            const int64_t orow = cg.row0 + row;
-            const int col = cg.j0 + 16 * b;
-            uint8_t* cdst = p.q_codes + orow * (p.N / 2) + col / 2;
-            uint8_t* sdst = p.q_scales + orow * (p.N / 16) + col / 16;
-            if (kDevOut) {
-              st_dev(reinterpret_cast<uint64_t*>(cdst), (uint64_t)lo | ((uint64_t)hi << 32));
-              st_dev(sdst, (uint8_t)sc);
-            } else {
-              *reinterpret_cast<u32x2*>(cdst) = u32x2{lo, hi};
-              *sdst = (uint8_t)sc;
-            }
-          }
         }
       }
       parity ^= 1;
@@ -593,9 +604,9 @@ __device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<NB>
     auto weight_row = [&](const SmallGroup& q, int col) -> int64_t {  // MFMA column -> weight row
       if (kL1) {
         const int j = col / 16, c = col % 16;
-        const int hc = 8 * j + (c & 7);
+        const int hc = 16 * (j / 2) + c;
         const int hcol = q.j0 + (hc < q.n ? hc : 0);
-        return (int64_t)q.e * Nw + (c < 8 ? hcol : p.N + hcol);
+        return (int64_t)q.e * Nw + ((j & 1) ? p.N + hcol : hcol);
       }
       return (int64_t)q.e * Nw + q.j0 + (col < q.n ? col : 0);
     };
@@ -661,14 +672,22 @@ __device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<NB>
       for (int j = 0; j < kSNb; ++j) {
         int64_t brow;
         if (kL1) {
-          const int hc = 8 * j + (r16 & 7);
+          const int hc = 16 * (j / 2) + r16;
           const int col = q.j0 + (hc < q.n ? hc : 0);
-          brow = (int64_t)q.e * Nw + (r16 < 8 ? col : p.N + col);
+          brow = (int64_t)q.e * Nw + ((j & 1) ? p.N + col : col);
         } else {
           const int rc = 16 * j + r16;
           brow = (int64_t)q.e * Nw + q.j0 + (rc < q.n ? rc : 0);
         }
-        lb_c[j] = p.w_codes + brow * Kh + g * kLaneBytes;
+        if constexpr (kPacked) {
+          // the block's 16 consecutive weight rows (whole: N % 16 == 0); a block past the
+          // group's units re-reads the group's first block
+          const int u0 = kL1 ? 16 * (j / 2) : 16 * j;
+          const int64_t r0 = (int64_t)q.e * Nw + ((kL1 && (j & 1)) ? p.N : 0) + q.j0 + (u0 < q.n ? u0 : 0);
+          lb_c[j] = p.w_packed + r0 * Kh + 16 * lane;
+        } else {
+          lb_c[j] = p.w_codes + brow * Kh + g * kLaneBytes;
+        }
         lb_s[j] = p.w_scales + brow * Ks + g * kLaneScales;
       }
     };
@@ -697,7 +716,13 @@ __device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<NB>
 #pragma unroll
       for (int j = 0; j < kSNb; ++j) {
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) d.b[j][q] = *reinterpret_cast<const u32x4*>(lb_c[j] + off + 16 * q);
+        for (int q = 0; q < kQ; ++q) {
+          // packed: chunk lc of a block is 2 KB, instruction q its q-th KB
+          if constexpr (kPacked)
+            d.b[j][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(lb_c[j] + 16 * off + 1024 * q));
+          else
+            d.b[j][q] = *reinterpret_cast<const u32x4*>(lb_c[j] + off + 16 * q);
+        }
         if (!kStaged) d.bs[j] = load_scale(lb_s[j] + soff);
       }
       if (++lc == c1) {
@@ -833,7 +858,7 @@ __device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<NB>
 
 // kNbMax: the widest group the kernel may take (L2: kSNbWide when the launch sized the staged
 // scale buffers for it, else the narrow width); the dynamic LDS holds scale buffers of that width.
-template <bool kL1, int CH, bool kStaged, bool kQOut, int kNbMax>
+template <bool kL1, int CH, bool kStaged, bool kQOut, int kNbMax, bool kPacked = false>
 __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArgs p) {
   constexpr int kSNb = small_nb<kL1>();
   static_assert(kNbMax >= kSNb && (kL1 ? kNbMax == kSNb : kNbMax % kSNb == 0), "group widths");
@@ -877,9 +902,9 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void gemm_small_kernel(GemmArg
     if (wide) {
       const SmallLds<kNbMax> W{L.pref, L.poff, L.cnt, L.tiny, L.ntiny, L.scl,
                                reinterpret_cast<f32x4 (*)[kSWaves][kNbMax][kWave]>(&s_red[0][0][0][0]), s_afrag};
-      small_pass<kL1, kNbMax, CH, kStaged, kQOut, false>(p, W, s_inv, lb, G, amax_bits, parity, SmallSync{});
+      small_pass<kL1, kNbMax, CH, kStaged, kQOut, false, kPacked>(p, W, s_inv, lb, G, amax_bits, parity, SmallSync{});
     } else {
-      small_pass<kL1, kSNb, CH, kStaged, kQOut, false>(p, L, s_inv, lb, G, amax_bits, parity, SmallSync{});
+      small_pass<kL1, kSNb, CH, kStaged, kQOut, false, kPacked>(p, L, s_inv, lb, G, amax_bits, parity, SmallSync{});
     }
   }
 
@@ -1563,12 +1588,16 @@ static hipError_t launch_gemm(GemmArgs a, GemmClasses c, hipStream_t stream) {
     auto fits = [&](int w) { return tables + 3 * small_scale_buf_bytes(w, a.K) <= small_dyn_max_lds(w); };
     const bool can_stage = MEGAMOE_SMALL_STAGED && ch == 256 && a.K / ch >= 2 * kSWaves;
     const dim3 grid(kSmallGrid), block(kGemmThreads);
+    // the packed codes are read by the staged configurations (a.w_packed is checked at the boundary)
+    const bool packed = a.w_packed != nullptr;
     if (can_stage && fits(nbw)) {
       const size_t dyn = tables + 3 * small_scale_buf_bytes(nbw, a.K);
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true, kQ, nbw>), grid, block, dyn, stream, a);
+      if (packed) hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true, kQ, nbw, true>), grid, block, dyn, stream, a);
+      else hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true, kQ, nbw>), grid, block, dyn, stream, a);
     } else if (can_stage && fits(nb)) {
       const size_t dyn = tables + 3 * small_scale_buf_bytes(nb, a.K);
-      hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true, kQ, nb>), grid, block, dyn, stream, a);
+      if (packed) hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true, kQ, nb, true>), grid, block, dyn, stream, a);
+      else hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, true, kQ, nb>), grid, block, dyn, stream, a);
     } else if (ch == 256) {  // the tables (at most 20.5 KB) fit beside the wide kernel's static LDS
       hipLaunchKernelGGL((gemm_small_kernel<kL1, 256, false, kQ, nbw>), grid, block, tables, stream, a);
     } else {
@@ -1620,6 +1649,39 @@ hipError_t launch_ffn_small(const FfnArgs& a0, hipStream_t stream) {
     else if (ch == 256) hipLaunchKernelGGL((ffn_small_kernel<256, false, false>), grid, block, dyn, stream, a);
     else hipLaunchKernelGGL((ffn_small_kernel<128, false, false>), grid, block, dyn, stream, a);
   }
+  return hipGetLastError();
+}
+
+// Packed weight codes for the 16-row kernels.  In the row-major layout a load instruction of the
+// 16-row kernels reads 64 bytes from each of 16 weight rows; in the packed layout it reads 1 KB
+// contiguous, which lets those loads be non-temporal (every weight byte is read once per call)
+// without fetching a 128-byte line twice.  For 16-row block rb (weight rows 16 rb .. 16 rb + 15),
+// 256-element chunk c and load instruction q (0, 1), lane L = 16 g + r holds the 16 code bytes
+// 32 g + 16 q .. of chunk c of row 16 rb + r -- the bytes that lane loads from the row-major
+// codes -- at byte ((rb * (K / 256) + c) * 2 + q) * 1024 + 16 L.  The same bytes, permuted: the
+// products do not change.
+__global__ __launch_bounds__(256) void pack_codes16_kernel(const u32x4* __restrict__ src, int64_t rows,
+                                                           int64_t pieces_per_row, u32x4* __restrict__ dst) {
+  const int64_t n = rows * pieces_per_row;  // 16-byte pieces
+  const int64_t per_block = 16 * pieces_per_row;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t rb = i / per_block;
+    const int64_t in_block = i - rb * per_block;
+    const int64_t c = in_block / 128;  // 2 KB = 128 pieces per chunk of a block
+    const int w = (int)(in_block - c * 128);
+    const int q = w / kWave, L = w % kWave;
+    const int r = L % 16, g = L / 16;
+    dst[i] = src[(rb * 16 + r) * pieces_per_row + c * 8 + 2 * g + q];
+  }
+}
+
+hipError_t launch_pack_codes16(const uint8_t* codes, int64_t rows, int64_t K, uint8_t* packed, hipStream_t stream) {
+  const int64_t pieces = rows * (K / 32);
+  int64_t grid = (pieces + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(pack_codes16_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(codes), rows, K / 32, reinterpret_cast<u32x4*>(packed));
   return hipGetLastError();
 }
 

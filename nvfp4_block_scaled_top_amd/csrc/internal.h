@@ -88,6 +88,9 @@ struct GemmArgs {
   const float* q_gs = nullptr;
   uint8_t* q_codes = nullptr;
   uint8_t* q_scales = nullptr;
+  // Optional: the weight codes also in the packed layout of nvfp4_pack_weight_codes, read by the
+  // 16-row kernels instead of w_codes (the 256-row kernels read w_codes).
+  const uint8_t* w_packed = nullptr;
 };
 // Which tile classes a call may contain, from the routing override and the caller's row bound.
 struct GemmClasses {
@@ -95,6 +98,9 @@ struct GemmClasses {
 };
 hipError_t launch_gemm_l1(const GemmArgs& a, GemmClasses c, hipStream_t stream);
 hipError_t launch_gemm_l2(const GemmArgs& a, GemmClasses c, hipStream_t stream);
+// Weight codes [rows, K/2] (rows % 16 == 0, K % 256 == 0) into the packed layout of the 16-row
+// kernels (nvfp4_pack_weight_codes).
+hipError_t launch_pack_codes16(const uint8_t* codes, int64_t rows, int64_t K, uint8_t* packed, hipStream_t stream);
 // L1, the requantization of h and L2 of the small class in one launch (moe_grouped_ffn_fused).
 // Sync words: per-XCD tickets, three counters and the error word in the first 384, then one
 // 32-word line per expert.

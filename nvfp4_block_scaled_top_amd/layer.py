@@ -28,6 +28,10 @@ class MoEWeights:
     w2_codes: torch.Tensor    # uint8 [E, H, I/2]
     w2_scales: torch.Tensor   # uint8 [E, H, I/16]
     w2_gs: torch.Tensor       # float32 [E]
+    # Optional second copies of the codes in the 16-row kernels' packed layout (pack()); when
+    # present the layer's GEMMs read them in the 16-row kernels (same results, bit for bit).
+    w13_packed: Optional[torch.Tensor] = None  # uint8 [E * 2I * H/2]
+    w2_packed: Optional[torch.Tensor] = None   # uint8 [E * H * I/2]
 
     @property
     def num_experts(self) -> int:
@@ -55,7 +59,19 @@ class MoEWeights:
                           torch.empty(E, dtype=torch.float32, device=device))
 
     def clone(self) -> "MoEWeights":
-        return MoEWeights(*(t.clone() for t in dataclasses.astuple(self)))
+        return MoEWeights(*(None if t is None else t.clone() for t in dataclasses.astuple(self)))
+
+    def pack(self, stream=None) -> "MoEWeights":
+        """(Re)build the packed copies of the codes (nvfp4_pack_weight_codes); call again after the
+        codes change.  W2 is packed only when I is a multiple of 256 (the packed layout's chunk)."""
+        self.w13_packed = torch.empty(self.w13_codes.numel(), dtype=torch.uint8, device=self.w13_codes.device)
+        mm.nvfp4_pack_weight_codes(self.w13_codes, self.w13_packed, stream=stream)
+        if self.intermediate % 256 == 0:
+            self.w2_packed = torch.empty(self.w2_codes.numel(), dtype=torch.uint8, device=self.w2_codes.device)
+            mm.nvfp4_pack_weight_codes(self.w2_codes, self.w2_packed, stream=stream)
+        else:
+            self.w2_packed = None
+        return self
 
 
 def quantize_matrix(w_bf16: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, gs: torch.Tensor,
@@ -180,7 +196,7 @@ class MoELayer:
         mm.moe_grouped_gemm_l1_silu(self.x_codes, self.x_scales, self._gs_x, self.row_token, self.padded_offsets,
                                     self.counts, self.sched, w.w13_codes, w.w13_scales, w.w13_gs,
                                     self._rows(self.h, self.M_cap), self.h_amax, self.block_m_override,
-                                    self.T, stream=stream)
+                                    self.T, stream=stream, w13_packed=w.w13_packed)
 
     def l1_nvfp4(self, w: MoEWeights, gs: torch.Tensor, stream=None) -> None:
         """L1 writing h as NVFP4 with the calibrated global scale gs (no bf16 h, no quantize_h)."""
@@ -189,7 +205,7 @@ class MoELayer:
                                           self.padded_offsets, self.counts, self.sched, w.w13_codes, w.w13_scales,
                                           w.w13_gs, gs, self._rows(self.h_codes, self.M_cap),
                                           self._rows(self.h_scales, self.M_cap), self.h_amax, self.block_m_override,
-                                          self.T, stream=stream)
+                                          self.T, stream=stream, w13_packed=w.w13_packed)
 
     def quantize_h(self, stream=None, gs: Optional[torch.Tensor] = None) -> None:
         """gs given (float32 [1] on the device): the calibrated quantizer with that global scale."""
@@ -206,7 +222,7 @@ class MoELayer:
     def l2(self, w: MoEWeights, stream=None) -> None:
         mm.moe_grouped_gemm_l2(self.h_codes, self.h_scales, self._gs_h, self.padded_offsets, self.counts, self.sched,
                                w.w2_codes, w.w2_scales, w.w2_gs, self._rows(self.y, self.M_cap),
-                               self.block_m_override, self.T, stream=stream)
+                               self.block_m_override, self.T, stream=stream, w2_packed=w.w2_packed)
 
     def ffn_fused(self, w: MoEWeights, stream=None, h_gs: Optional[torch.Tensor] = None) -> None:
         """L1, the requantization of h and L2 in one launch (every expert in 16-row m-tiles: for

@@ -55,6 +55,13 @@ SIGNATURES = {
     "moe_grouped_gemm_l1_silu": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
                                         _P, _P, _P]),
     "moe_grouped_gemm_l2": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _P, _P]),
+    "nvfp4_pack_weight_codes": (_I32, [_P, _I64, _I64, _P, _P]),
+    "moe_grouped_gemm_l1_silu_packed": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64,
+                                               _I32, _I32, _P, _P, _P]),
+    "moe_grouped_gemm_l1_silu_nvfp4_packed": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                                     _I64, _I32, _I32, _P, _P, _P, _P, _P]),
+    "moe_grouped_gemm_l2_packed": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
+                                          _P, _P]),
     "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
     "moe_combine_shared": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P]),
     "megamoe_dense_workspace_bytes": (_SZ, [_I64]),
@@ -201,40 +208,62 @@ def nvfp4_quantize_act_gs(x_bf16, global_scale_in, codes, scales, row_valid=None
         _ptr(x_bf16), rows, cols, _ptr(row_valid), _ptr(global_scale_in), _ptr(codes), _ptr(scales), _stream(stream)))
 
 
+def nvfp4_pack_weight_codes(codes, packed, stream=None):
+    """codes: uint8 [..., rows, K/2] (leading dimensions folded into rows); packed: as many bytes."""
+    K = 2 * codes.shape[-1]
+    rows = codes.numel() // codes.shape[-1]
+    if packed.numel() != codes.numel():
+        raise MegaMoEError("packed must hold as many bytes as codes")
+    _check("nvfp4_pack_weight_codes", lib().nvfp4_pack_weight_codes(_ptr(codes), rows, K, _ptr(packed), _stream(stream)))
+
+
 def moe_grouped_gemm_l1_silu(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes,
                              w13_scales, w13_gs, h_bf16, h_amax_parts, block_m_override=0, max_rows_per_expert=0,
-                             stream=None):
+                             stream=None, w13_packed=None):
+    """w13_packed: optional, the codes packed by nvfp4_pack_weight_codes (moe_grouped_gemm_l1_silu_packed)."""
     E, I2, Hh = w13_codes.shape
     M_cap = h_bf16.shape[0]
     if h_amax_parts.numel() < L1_AMAX_PARTS:
         raise MegaMoEError(f"h_amax_parts needs {L1_AMAX_PARTS} floats")
-    _check("moe_grouped_gemm_l1_silu", lib().moe_grouped_gemm_l1_silu(
-        _ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts), _ptr(sched),
-        _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), E, 2 * Hh, I2 // 2, M_cap, block_m_override,
-        max_rows_per_expert, _ptr(h_bf16), _ptr(h_amax_parts), _stream(stream)))
+    head = (_ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts),
+            _ptr(sched), _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs))
+    tail = (E, 2 * Hh, I2 // 2, M_cap, block_m_override, max_rows_per_expert, _ptr(h_bf16), _ptr(h_amax_parts),
+            _stream(stream))
+    if w13_packed is None:
+        _check("moe_grouped_gemm_l1_silu", lib().moe_grouped_gemm_l1_silu(*head, *tail))
+    else:
+        _check("moe_grouped_gemm_l1_silu_packed", lib().moe_grouped_gemm_l1_silu_packed(*head, _ptr(w13_packed), *tail))
 
 
 def moe_grouped_gemm_l1_silu_nvfp4(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes,
                                    w13_scales, w13_gs, h_gs, h_codes, h_scales, h_amax_parts, block_m_override=0,
-                                   max_rows_per_expert=0, stream=None):
+                                   max_rows_per_expert=0, stream=None, w13_packed=None):
     E, I2, Hh = w13_codes.shape
     M_cap = h_codes.shape[0]
     if h_amax_parts.numel() < L1_AMAX_PARTS:
         raise MegaMoEError(f"h_amax_parts needs {L1_AMAX_PARTS} floats")
-    _check("moe_grouped_gemm_l1_silu_nvfp4", lib().moe_grouped_gemm_l1_silu_nvfp4(
-        _ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts), _ptr(sched),
-        _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), E, 2 * Hh, I2 // 2, M_cap, block_m_override,
-        max_rows_per_expert, _ptr(h_gs), _ptr(h_codes), _ptr(h_scales), _ptr(h_amax_parts), _stream(stream)))
+    head = (_ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts),
+            _ptr(sched), _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs))
+    tail = (E, 2 * Hh, I2 // 2, M_cap, block_m_override, max_rows_per_expert, _ptr(h_gs), _ptr(h_codes),
+            _ptr(h_scales), _ptr(h_amax_parts), _stream(stream))
+    if w13_packed is None:
+        _check("moe_grouped_gemm_l1_silu_nvfp4", lib().moe_grouped_gemm_l1_silu_nvfp4(*head, *tail))
+    else:
+        _check("moe_grouped_gemm_l1_silu_nvfp4_packed",
+               lib().moe_grouped_gemm_l1_silu_nvfp4_packed(*head, _ptr(w13_packed), *tail))
 
 
 def moe_grouped_gemm_l2(h_codes, h_scales, h_gs, padded_offsets, counts, sched, w2_codes, w2_scales, w2_gs, y_bf16,
-                        block_m_override=0, max_rows_per_expert=0, stream=None):
+                        block_m_override=0, max_rows_per_expert=0, stream=None, w2_packed=None):
     E, H, Ih = w2_codes.shape
     M_cap = y_bf16.shape[0]
-    _check("moe_grouped_gemm_l2", lib().moe_grouped_gemm_l2(
-        _ptr(h_codes), _ptr(h_scales), _ptr(h_gs), _ptr(padded_offsets), _ptr(counts), _ptr(sched), _ptr(w2_codes),
-        _ptr(w2_scales), _ptr(w2_gs), E, H, 2 * Ih, M_cap, block_m_override, max_rows_per_expert, _ptr(y_bf16),
-        _stream(stream)))
+    head = (_ptr(h_codes), _ptr(h_scales), _ptr(h_gs), _ptr(padded_offsets), _ptr(counts), _ptr(sched),
+            _ptr(w2_codes), _ptr(w2_scales), _ptr(w2_gs))
+    tail = (E, H, 2 * Ih, M_cap, block_m_override, max_rows_per_expert, _ptr(y_bf16), _stream(stream))
+    if w2_packed is None:
+        _check("moe_grouped_gemm_l2", lib().moe_grouped_gemm_l2(*head, *tail))
+    else:
+        _check("moe_grouped_gemm_l2_packed", lib().moe_grouped_gemm_l2_packed(*head, _ptr(w2_packed), *tail))
 
 
 def megamoe_ffn_sync_bytes(num_experts: int) -> int:

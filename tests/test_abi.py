@@ -175,6 +175,29 @@ def test_gemm_rejects_bad_args(lib):
     assert l2(*pl2, 8, 256, 128, 0, 0, 0, None, None) == -1
 
 
+def test_packed_entry_points_reject_bad_args(lib):
+    """nvfp4_pack_weight_codes and the *_packed GEMMs: shape and NULL checks, before any HIP call."""
+    pk = lib.nvfp4_pack_weight_codes
+    assert pk(FAKE, 24, 256, FAKE, None) == -2    # rows not a multiple of 16
+    assert pk(FAKE, 0, 256, FAKE, None) == -2
+    assert pk(FAKE, 16, 384, FAKE, None) == -2    # K not a multiple of 256
+    assert pk(None, 16, 256, FAKE, None) == -1
+    assert pk(FAKE, 16, 256, None, None) == -1
+    p10 = [FAKE] * 10
+    l1p = lib.moe_grouped_gemm_l1_silu_packed
+    assert l1p(*p10, None, 8, 256, 128, 64, 0, 0, FAKE, FAKE, None) == -1    # packed codes NULL
+    assert l1p(*p10, FAKE, 8, 384, 128, 64, 0, 0, FAKE, FAKE, None) == -2    # H not a multiple of 256
+    assert l1p(*p10, FAKE, 8, 256, 128, 64, 0, 0, FAKE, None, None) == -1    # h_amax NULL
+    qp = lib.moe_grouped_gemm_l1_silu_nvfp4_packed
+    assert qp(*p10, None, 8, 256, 128, 64, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert qp(*p10, FAKE, 8, 256, 128, 64, 0, 0, None, FAKE, FAKE, FAKE, None) == -1   # h_gs NULL
+    p9 = [FAKE] * 9
+    l2p = lib.moe_grouped_gemm_l2_packed
+    assert l2p(*p9, FAKE, 8, 256, 128, 64, 0, 0, FAKE, None) == -2    # I not a multiple of 256
+    assert l2p(*p9, None, 8, 256, 256, 64, 0, 0, FAKE, None) == -1
+    assert l2p(*p9, FAKE, 8, 256, 256, 64, 0, 0, None, None) == -1    # y NULL
+
+
 def test_ffn_fused_rejects_bad_args(lib):
     """moe_grouped_ffn_fused: shape, NULL and sync-size checks, all before any HIP call."""
     f = lib.moe_grouped_ffn_fused
