@@ -452,8 +452,9 @@ def probe_lib():
 def gemm_stream_ceilings(experts=9, copies=4, reps=100):
     """Read rate (GB/s) of the 16-row L1 GEMM's weight-code stream at decode T=8 (9 active experts'
     W13 codes, 132 MB) with the kernel's launch shape and load structure but no arithmetic
-    (csrc/probe.hip, megamoe_probe_gemm_stream): in the kernel's own addressing and in a
-    workgroup-contiguous order; `copies` rotated buffers keep it out of the last-level cache."""
+    (csrc/probe.hip, megamoe_probe_gemm_stream): in the kernel's addressing of the row-major codes, in
+    a workgroup-contiguous order, and in its addressing of the packed codes with non-temporal loads;
+    `copies` rotated buffers keep it out of the last-level cache."""
     import torch
 
     lib = probe_lib()
@@ -462,7 +463,8 @@ def gemm_stream_ceilings(experts=9, copies=4, reps=100):
     bufs = [torch.full((nbytes,), 0x35 + i, dtype=torch.uint8, device="cuda") for i in range(copies)]
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     res = {"bytes": nbytes}
-    for name, pattern in (("gemm_addressing_GBps", 0), ("workgroup_contiguous_GBps", 1)):
+    for name, pattern in (("gemm_addressing_GBps", 0), ("workgroup_contiguous_GBps", 1),
+                          ("packed_codes_nontemporal_GBps", 2)):
         def run(i):
             rc = lib.megamoe_probe_gemm_stream(bufs[i % copies].data_ptr(), nbytes, experts, pattern,
                                                sink.data_ptr(), ctypes_stream(stream))

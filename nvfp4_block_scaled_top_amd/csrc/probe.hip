@@ -65,11 +65,13 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
 // LDS each), groups of 2 x 16 weight rows over the whole K cut into equal contiguous ranges, the 4
 // waves splitting the 28 K-chunks of 128 code bytes (7 steps per group), a 2-step register ring of
 // 4 x 16-byte loads per lane refilled after each step is consumed (XOR-ed into a sink).
-//   pattern 0: the GEMM's addressing: lane (r = lane % 16, g = lane / 16) of block j reads 32 bytes
-//              of row r at K offset 32 g; rows 0-7 of a block are gate rows, 8-15 the matching up
-//              rows 2048 rows later;
+//   pattern 0: the GEMM's addressing in the row-major codes: lane (r = lane % 16, g = lane / 16)
+//              of block j reads 32 bytes of row r at K offset 32 g; block 0 holds the group's 16
+//              gate rows, block 1 the matching 16 up rows 2048 rows later;
 //   pattern 1: workgroup-contiguous: the 4 KB a wave takes at step s of group G lie at
-//              ((G * 7 + s) * 4 + wave) * 4 KB (a layout permuted for the stream).
+//              ((G * 7 + s) * 4 + wave) * 4 KB (a layout permuted for the stream);
+//   pattern 2: the GEMM's addressing in the packed codes (nvfp4_pack_weight_codes), non-temporal:
+//              each load instruction reads the 1 KB of its block's chunk and half.
 constexpr int kGsRowBytes = 3584, kGsRowsPerExpert = 4096, kGsGroupsPerExpert = 128, kGsSteps = 7;
 constexpr int kGsLdsWords = 80 * 1024 / 4;
 
@@ -87,15 +89,18 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_stream_kernel(const uint8_t*
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       int64_t off;
+      const int j = k >> 1, q = k & 1, e = g / kGsGroupsPerExpert, gi = g % kGsGroupsPerExpert;
+      const int row0 = e * kGsRowsPerExpert + (j ? kGsRowsPerExpert / 2 : 0) + gi * 16;  // block's first row
+      const int chunk = wave * kGsSteps + s;
       if (PATTERN == 1) {
         off = ((int64_t)(g * kGsSteps + s) * 4 + wave) * 4096 + k * 1024 + lane * 16;
+      } else if (PATTERN == 2) {
+        off = (int64_t)row0 * kGsRowBytes + (int64_t)chunk * 2048 + q * 1024 + lane * 16;
       } else {
-        const int j = k >> 1, q = k & 1, e = g / kGsGroupsPerExpert, gi = g % kGsGroupsPerExpert;
-        const int hc = gi * 16 + 8 * j + (r16 & 7);
-        const int row = e * kGsRowsPerExpert + (r16 < 8 ? hc : kGsRowsPerExpert / 2 + hc);
-        off = (int64_t)row * kGsRowBytes + (wave * kGsSteps + s) * 128 + gg * 32 + q * 16;
+        off = (int64_t)(row0 + r16) * kGsRowBytes + chunk * 128 + gg * 32 + q * 16;
       }
-      d[k] = *reinterpret_cast<const u32x4*>(w + off);
+      if (PATTERN == 2) d[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w + off));
+      else d[k] = *reinterpret_cast<const u32x4*>(w + off);
     }
   };
   uint32_t acc = lds[threadIdx.x & 0] & 0u;
@@ -149,19 +154,20 @@ extern "C" int megamoe_probe_read(const void* buf, uint64_t bytes, int32_t order
   return (int)hipGetLastError();
 }
 
-// experts >= 1 (groups = 128 per expert); bytes >= experts * 4096 * 3584; pattern 0 or 1.  Returns 0,
+// experts >= 1 (groups = 128 per expert); bytes >= experts * 4096 * 3584; pattern 0, 1 or 2.  Returns 0,
 // -1 for bad arguments, or the HIP error code.
 extern "C" int megamoe_probe_gemm_stream(const void* buf, uint64_t bytes, int32_t experts, int32_t pattern,
                                          uint32_t* sink, void* stream) {
   using namespace megamoe_probe;
-  if (!buf || !sink || experts < 1 || experts > 1024 || (pattern != 0 && pattern != 1) ||
+  if (!buf || !sink || experts < 1 || experts > 1024 || pattern < 0 || pattern > 2 ||
       bytes < (uint64_t)experts * kGsRowsPerExpert * kGsRowBytes)
     return -1;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* w = static_cast<const uint8_t*>(buf);
   const int groups = experts * kGsGroupsPerExpert;
   if (pattern == 0) hipLaunchKernelGGL(gemm_stream_kernel<0>, dim3(512), dim3(kThreads), 0, s, w, groups, sink);
-  else hipLaunchKernelGGL(gemm_stream_kernel<1>, dim3(512), dim3(kThreads), 0, s, w, groups, sink);
+  else if (pattern == 1) hipLaunchKernelGGL(gemm_stream_kernel<1>, dim3(512), dim3(kThreads), 0, s, w, groups, sink);
+  else hipLaunchKernelGGL(gemm_stream_kernel<2>, dim3(512), dim3(kThreads), 0, s, w, groups, sink);
   return (int)hipGetLastError();
 }
 

@@ -275,7 +275,7 @@ def test_probe_lib_exports_and_rejects_bad_args():
                                             ctypes.c_void_p, ctypes.c_void_p]
     need = 9 * 4096 * 3584
     assert h.megamoe_probe_gemm_stream(fake, need - 16, 9, 0, fake, None) == -1   # buffer too small
-    assert h.megamoe_probe_gemm_stream(fake, need, 9, 2, fake, None) == -1        # pattern
+    assert h.megamoe_probe_gemm_stream(fake, need, 9, 3, fake, None) == -1        # pattern
     assert h.megamoe_probe_gemm_stream(fake, need, 0, 0, fake, None) == -1        # experts
     assert h.megamoe_probe_gemm_stream(None, need, 9, 1, fake, None) == -1
 
