@@ -447,6 +447,19 @@ int32_t moe_grouped_ffn_fused(const uint8_t* x_codes, const uint8_t* x_scales, c
                               float* h_gs_out, void* y_bf16, void* sync, size_t sync_bytes,
                               void* stream);
 
+/* moe_grouped_ffn_fused_packed - moe_grouped_ffn_fused with the packed copies of both weights'
+ * codes (nvfp4_pack_weight_codes; w13_packed, w2_packed after w2_gs), read by its 16-row passes.
+ * Same results, bit for bit.  Errors as for moe_grouped_ffn_fused, and: a packed copy NULL -> -1;
+ * I not a multiple of 256 -> -2.  (For the callers of the *_packed grouped GEMMs above.) */
+int32_t moe_grouped_ffn_fused_packed(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                     const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
+                                     const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                     const float* w13_gs, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                     const float* w2_gs, const uint8_t* w13_packed, const uint8_t* w2_packed,
+                                     int32_t E, int32_t H, int32_t I, int64_t M_cap, const float* h_gs_in,
+                                     void* h_bf16, float* h_amax_parts, uint8_t* h_codes, uint8_t* h_scales,
+                                     float* h_gs_out, void* y_bf16, void* sync, size_t sync_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * nvfp4_linear - dense NVFP4 linear layer: the L2 GEMM with one group holding every row.
  *

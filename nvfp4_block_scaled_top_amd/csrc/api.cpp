@@ -421,14 +421,14 @@ size_t megamoe_ffn_sync_bytes(int32_t num_experts) {
   return (size_t)(kFfnSyncHeader + (int64_t)num_experts * kFfnSyncStride) * sizeof(uint32_t);
 }
 
-int32_t moe_grouped_ffn_fused(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
-                              const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
-                              const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
-                              const float* w13_gs, const uint8_t* w2_codes, const uint8_t* w2_scales,
-                              const float* w2_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap,
-                              const float* h_gs_in, void* h_bf16, float* h_amax_parts, uint8_t* h_codes,
-                              uint8_t* h_scales, float* h_gs_out, void* y_bf16, void* sync, size_t sync_bytes,
-                              void* stream) {
+static int32_t ffn_fused(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                         const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
+                         const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                         const float* w13_gs, const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
+                         const uint8_t* w13_packed, const uint8_t* w2_packed, int32_t E, int32_t H, int32_t I,
+                         int64_t M_cap, const float* h_gs_in, void* h_bf16, float* h_amax_parts, uint8_t* h_codes,
+                         uint8_t* h_scales, float* h_gs_out, void* y_bf16, void* sync, size_t sync_bytes,
+                         void* stream) {
   if (!gemm_shape_ok(E, H, I, M_cap)) return MEGAMOE_ERR_SHAPE;
   if (!x_gs || !padded_offsets || !counts || !sched || !w13_codes || !w13_scales || !w13_gs || !w2_codes ||
       !w2_scales || !w2_gs || !h_amax_parts || !sync)
@@ -455,6 +455,8 @@ int32_t moe_grouped_ffn_fused(const uint8_t* x_codes, const uint8_t* x_scales, c
   }
   a.l2 = GemmArgs{h_codes, h_scales, h_gs_in ? h_gs_in : h_gs_out, nullptr, padded_offsets, counts, sched, w2_codes,
                   w2_scales, w2_gs, E, I, H, y_bf16, nullptr, 0};
+  a.l1.w_packed = w13_packed;
+  a.l2.w_packed = w2_packed;
   a.sync = static_cast<uint32_t*>(sync);
   a.row_valid = row_token;
   a.M_cap = M_cap;
@@ -462,6 +464,34 @@ int32_t moe_grouped_ffn_fused(const uint8_t* x_codes, const uint8_t* x_scales, c
   a.hq_scales = h_scales;
   a.h_gs = h_gs_out;
   return launch_status(launch_ffn_small(a, s));
+}
+
+int32_t moe_grouped_ffn_fused(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                              const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
+                              const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                              const float* w13_gs, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                              const float* w2_gs, int32_t E, int32_t H, int32_t I, int64_t M_cap,
+                              const float* h_gs_in, void* h_bf16, float* h_amax_parts, uint8_t* h_codes,
+                              uint8_t* h_scales, float* h_gs_out, void* y_bf16, void* sync, size_t sync_bytes,
+                              void* stream) {
+  return ffn_fused(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
+                   w2_codes, w2_scales, w2_gs, nullptr, nullptr, E, H, I, M_cap, h_gs_in, h_bf16, h_amax_parts,
+                   h_codes, h_scales, h_gs_out, y_bf16, sync, sync_bytes, stream);
+}
+
+int32_t moe_grouped_ffn_fused_packed(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                     const int32_t* row_token, const int32_t* padded_offsets, const int32_t* counts,
+                                     const int32_t* sched, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                     const float* w13_gs, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                     const float* w2_gs, const uint8_t* w13_packed, const uint8_t* w2_packed,
+                                     int32_t E, int32_t H, int32_t I, int64_t M_cap, const float* h_gs_in,
+                                     void* h_bf16, float* h_amax_parts, uint8_t* h_codes, uint8_t* h_scales,
+                                     float* h_gs_out, void* y_bf16, void* sync, size_t sync_bytes, void* stream) {
+  if (I % 256 != 0) return MEGAMOE_ERR_SHAPE;  // the packed layout is in 256-element chunks of K
+  if (!w13_packed || !w2_packed) return MEGAMOE_ERR_NULL;
+  return ffn_fused(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales, w13_gs,
+                   w2_codes, w2_scales, w2_gs, w13_packed, w2_packed, E, H, I, M_cap, h_gs_in, h_bf16, h_amax_parts,
+                   h_codes, h_scales, h_gs_out, y_bf16, sync, sync_bytes, stream);
 }
 
 size_t megamoe_dense_workspace_bytes(int64_t M) {

@@ -961,7 +961,7 @@ static_assert(MEGAMOE_FFN_SYNC_ERROR_WORD == 352 && kSyncHeader >= 384, "sync wo
 // Bytes of the fused kernel's per-expert tables: those of the small class plus the L2 inv.
 __host__ __device__ inline size_t ffn_table_bytes(int E) { return (((size_t)6 * E + 1) * 4 + 15) / 16 * 16; }
 
-template <int CH, bool kStaged, bool kCal>
+template <int CH, bool kStaged, bool kCal, bool kPacked = false>
 __global__ __launch_bounds__(kGemmThreads, kSOcc) void ffn_small_kernel(FfnArgs a) {
   constexpr int kSNb = small_nb<true>();
   static_assert(small_nb<false>() == kSNb, "the two passes share the reduction buffers");
@@ -1054,7 +1054,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void ffn_small_kernel(FfnArgs 
     // the global item: L1 part t < n1, quantization part t - n1 < nq, L2 part t - n1 - nq
     const int64_t t = tx < c1 ? b1 + tx : tx < c1 + cq ? n1 + bq + (tx - c1) : n1 + nq + b2 + (tx - c1 - cq);
     if (t < n1) {
-      small_pass<true, kSNb, CH, kStaged, kCal, true>(p1, L, inv1, t, n1, amax_bits, parity, SmallSync{});
+      small_pass<true, kSNb, CH, kStaged, kCal, true, kPacked>(p1, L, inv1, t, n1, amax_bits, parity, SmallSync{});
       // Publish: this wave's h stores have completed (vmcnt counts stores), then the counts.
       amax_bits = wave_max_u32(amax_bits);
       if (lane == 0) s_amax[wave] = amax_bits;
@@ -1132,7 +1132,7 @@ __global__ __launch_bounds__(kGemmThreads, kSOcc) void ffn_small_kernel(FfnArgs 
         __syncthreads();
         inv2_ready = true;
       }
-      small_pass<false, kSNb, CH, kStaged, false, true>(p2, L, inv2, t - n1 - nq, n2, amax_bits, parity, l2sync);
+      small_pass<false, kSNb, CH, kStaged, false, true, kPacked>(p2, L, inv2, t - n1 - nq, n2, amax_bits, parity, l2sync);
     }
     if (threadIdx.x == 0) t_next = add_dev(ticket, 1u);
   }
@@ -1640,6 +1640,13 @@ hipError_t launch_ffn_small(const FfnArgs& a0, hipStream_t stream) {
                       tables + bufs <= small_dyn_max_lds(small_nb<true>());
   const size_t dyn = tables + (staged ? bufs : 0);
   const dim3 grid(kSmallGrid), block(kGemmThreads);
+  // the packed codes of both GEMMs (checked at the boundary) are read by the staged configurations
+  const bool packed = a.l1.w_packed != nullptr && a.l2.w_packed != nullptr;
+  if (staged && packed) {
+    if (cal) hipLaunchKernelGGL((ffn_small_kernel<256, true, true, true>), grid, block, dyn, stream, a);
+    else hipLaunchKernelGGL((ffn_small_kernel<256, true, false, true>), grid, block, dyn, stream, a);
+    return hipGetLastError();
+  }
   if (cal) {
     if (staged) hipLaunchKernelGGL((ffn_small_kernel<256, true, true>), grid, block, dyn, stream, a);
     else if (ch == 256) hipLaunchKernelGGL((ffn_small_kernel<256, false, true>), grid, block, dyn, stream, a);

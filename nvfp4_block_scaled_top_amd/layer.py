@@ -239,7 +239,8 @@ class MoELayer:
                                  w.w2_scales, w.w2_gs, self.h_amax, self._rows(self.h_codes, M),
                                  self._rows(self.h_scales, M), self._rows(self.y, M), self.ffn_sync,
                                  h_gs_in=h_gs, h_bf16=None if h_gs is not None else self._rows(self.h, M),
-                                 h_gs_out=None if h_gs is not None else self.h_gs, stream=stream)
+                                 h_gs_out=None if h_gs is not None else self.h_gs, stream=stream,
+                                 w13_packed=w.w13_packed, w2_packed=w.w2_packed)
 
     def ffn_sync_error(self) -> int:
         """The fused launch's error word (non-zero once a wait inside it ever expired)."""

@@ -56,6 +56,8 @@ SIGNATURES = {
                                         _P, _P, _P]),
     "moe_grouped_gemm_l2": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _P, _P]),
     "nvfp4_pack_weight_codes": (_I32, [_P, _I64, _I64, _P, _P]),
+    "moe_grouped_ffn_fused_packed": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32,
+                                            _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_l1_silu_packed": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64,
                                                _I32, _I32, _P, _P, _P]),
     "moe_grouped_gemm_l1_silu_nvfp4_packed": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
@@ -272,16 +274,22 @@ def megamoe_ffn_sync_bytes(num_experts: int) -> int:
 
 def moe_grouped_ffn_fused(x_codes, x_scales, x_gs, row_token, padded_offsets, counts, sched, w13_codes, w13_scales,
                           w13_gs, w2_codes, w2_scales, w2_gs, h_amax_parts, h_codes, h_scales, y_bf16, sync,
-                          h_gs_in=None, h_bf16=None, h_gs_out=None, stream=None):
+                          h_gs_in=None, h_bf16=None, h_gs_out=None, stream=None, w13_packed=None, w2_packed=None):
+    """w13_packed, w2_packed: optional, both weights' packed codes (moe_grouped_ffn_fused_packed)."""
     E, I2, Hh = w13_codes.shape
     M_cap = y_bf16.shape[0]
     if h_amax_parts.numel() < L1_AMAX_PARTS:
         raise MegaMoEError(f"h_amax_parts needs {L1_AMAX_PARTS} floats")
-    _check("moe_grouped_ffn_fused", lib().moe_grouped_ffn_fused(
-        _ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts), _ptr(sched),
-        _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), _ptr(w2_codes), _ptr(w2_scales), _ptr(w2_gs), E, 2 * Hh,
-        I2 // 2, M_cap, _ptr(h_gs_in), _ptr(h_bf16), _ptr(h_amax_parts), _ptr(h_codes), _ptr(h_scales),
-        _ptr(h_gs_out), _ptr(y_bf16), _ptr(sync), _nbytes(sync), _stream(stream)))
+    head = (_ptr(x_codes), _ptr(x_scales), _ptr(x_gs), _ptr(row_token), _ptr(padded_offsets), _ptr(counts),
+            _ptr(sched), _ptr(w13_codes), _ptr(w13_scales), _ptr(w13_gs), _ptr(w2_codes), _ptr(w2_scales),
+            _ptr(w2_gs))
+    tail = (E, 2 * Hh, I2 // 2, M_cap, _ptr(h_gs_in), _ptr(h_bf16), _ptr(h_amax_parts), _ptr(h_codes),
+            _ptr(h_scales), _ptr(h_gs_out), _ptr(y_bf16), _ptr(sync), _nbytes(sync), _stream(stream))
+    if w13_packed is None or w2_packed is None:
+        _check("moe_grouped_ffn_fused", lib().moe_grouped_ffn_fused(*head, *tail))
+    else:
+        _check("moe_grouped_ffn_fused_packed",
+               lib().moe_grouped_ffn_fused_packed(*head, _ptr(w13_packed), _ptr(w2_packed), *tail))
 
 
 def moe_combine(y_bf16, token_rows, topk_weights, out_bf16, stream=None):

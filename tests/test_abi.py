@@ -196,6 +196,13 @@ def test_packed_entry_points_reject_bad_args(lib):
     assert l2p(*p9, FAKE, 8, 256, 128, 64, 0, 0, FAKE, None) == -2    # I not a multiple of 256
     assert l2p(*p9, None, 8, 256, 256, 64, 0, 0, FAKE, None) == -1
     assert l2p(*p9, FAKE, 8, 256, 256, 64, 0, 0, None, None) == -1    # y NULL
+    fp = lib.moe_grouped_ffn_fused_packed
+    need = mm.megamoe_ffn_sync_bytes(8)
+    p13 = [FAKE] * 13
+    tail = (FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, need, None)
+    assert fp(*p13, FAKE, FAKE, 8, 256, 128, 64, *tail) == -2     # I not a multiple of 256
+    assert fp(*p13, None, FAKE, 8, 256, 256, 64, *tail) == -1     # w13 packed NULL
+    assert fp(*p13, FAKE, None, 8, 256, 256, 64, *tail) == -1     # w2 packed NULL
 
 
 def test_ffn_fused_rejects_bad_args(lib):

@@ -112,3 +112,34 @@ def test_layer_packed_equals_unpacked_calibrated(wl, T):
     assert a["h_codes"].shape[0] > 0
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def _fused_bits(s, packed: bool, h_gs=None) -> dict:
+    from nvfp4_block_scaled_top_amd import layer
+    w = s.gpu_w.clone()
+    if packed:
+        w.pack()
+    wl = s.wl
+    L = layer.MoELayer(s.T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
+                       expert_begin=wl.expert_begin, device=DEV)
+    x, ids, wts = s.dev_inputs()
+    L.forward(x, ids, wts, w, h_gs=h_gs, fused=True)
+    torch.cuda.synchronize()
+    assert L.ffn_sync_error() == 0
+    return {"out": L.out[:L.T].contiguous().view(torch.uint8).cpu().numpy(), "y": _valid_rows(L, L.y),
+            "h_codes": _valid_rows(L, L.h_codes), "h_scales": _valid_rows(L, L.h_scales)}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("calibrated", [False, True], ids=["amax_scale", "calibrated_scale"])
+def test_fused_packed_equals_unpacked(calibrated):
+    """moe_grouped_ffn_fused_packed against moe_grouped_ffn_fused on the decode share (T=8)."""
+    wl, T = synth.WORKLOADS[1], 8
+    log(f"[packed] fused {wl.name} T={T} calibrated={calibrated}")
+    s = make_setup(wl, T)
+    gs = torch.from_numpy(_forward_bits(s, packed=False)["h_gs"]).to(DEV) if calibrated else None
+    a = _fused_bits(s, packed=False, h_gs=gs)
+    b = _fused_bits(s, packed=True, h_gs=gs)
+    assert a["y"].shape[0] > 0
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
