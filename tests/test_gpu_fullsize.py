@@ -17,7 +17,9 @@ by the oracle's C quantizer and decoded exactly, the GEMMs as float64 matrix pro
   * combine: every token of out against the oracle's combine of the GPU's y, within one bf16 step
     plus the fp32 accumulation error of k terms;
   * end to end: out against the oracle's own chain (its own h, requantization, y, combine),
-    relative Frobenius <= 1e-2 and cosine >= 0.9999.
+    relative Frobenius <= 1e-2 and cosine >= 0.9999;
+  * the same forward with the packed copy of the weight codes (how bench.py runs it) gives the same
+    bits at every stage.
 """
 import time
 
@@ -86,6 +88,22 @@ def test_prefill_full_size_end_to_end(cfg):
     y_gpu = _host_bf16(L.y[:M])
     out_gpu = _host_bf16(L.out[:T]).astype(np.float64)
     valid = row_token >= 0
+
+    # the same forward on weights that carry the packed copy of their codes (the benchmark's
+    # configuration: the 16-row kernels read it): the same bits at every stage
+    W.pack()
+    Lp = layer.MoELayer(T, k, E, H, I, P, expert_begin=wl.expert_begin, device=DEV)
+    Lp.forward(torch.from_numpy(x_bits.view(np.int16)).to(DEV), torch.from_numpy(ids).to(DEV),
+               torch.from_numpy(wts).to(DEV), W)
+    torch.cuda.synchronize()
+    for name, a, b in (("h", L.h, Lp.h), ("h_codes", L.h_codes, Lp.h_codes), ("h_scales", L.h_scales, Lp.h_scales),
+                       ("y", L.y, Lp.y)):
+        assert np.array_equal(np_i32(a[:M])[valid], np_i32(b[:M])[valid]), name
+    assert Lp.h_gs.item() == gsh_gpu
+    assert np.array_equal(bf16_bits_of(L.out[:T]), bf16_bits_of(Lp.out[:T]))
+    W.w13_packed = W.w2_packed = None
+    del Lp
+    log("[fullsize] packed weight codes: h, h codes / scales / gs, y and out bit-identical")
 
     # ---- oracle L1 per expert (weights regenerated, quantized by the oracle, checked bit-exact) ----
     h_ref = np.zeros((M, I), np.float64)
