@@ -47,6 +47,30 @@ def test_graph_replays_match_eager(wl, T):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("wl,T", CASES[1:], ids=IDS[1:])
+def test_graph_replays_packed_weights(wl, T):
+    """The benchmark's configuration: weights with the packed copy of their codes.  Every replay
+    equals the eager forward on the row-major codes alone, bit for bit."""
+    s = make_setup(wl, T)
+    x, ids, wts = s.dev_inputs()
+    L = layer.MoELayer(T, wl.top_k, wl.num_experts, wl.hidden, wl.intermediate, wl.pad_multiple,
+                       expert_begin=wl.expert_begin, device=DEV)
+    L.forward(x, ids, wts, s.gpu_w)
+    torch.cuda.synchronize()
+    eager = np_i32(L.out[:T].view(torch.int16)).copy()
+    w = s.gpu_w.clone().pack()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.forward(x, ids, wts, w)
+    for r in range(3):
+        L.out.fill_(0x7FC0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np_i32(L.out[:T].view(torch.int16)), eager), r
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("wl,T", CASES, ids=IDS)
 def test_graph_replays_calibrated(wl, T):
     """The calibrated forward (x quantized in the routing launch, h written as NVFP4 by L1)
