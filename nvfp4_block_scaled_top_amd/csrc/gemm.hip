@@ -202,6 +202,12 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
   lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform; must live in an SGPR for M0
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
 }
+// The same with the non-temporal hint: for bytes read once per call (the 16-row kernels' weight
+// scales when they stream the packed codes).
+__device__ __forceinline__ void dma16nt(const uint8_t* src, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds), "v"(src) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const uint8_t* src, uint32_t lds) {
   lds = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
@@ -618,7 +624,8 @@ __device__ __forceinline__ void small_pass(const GemmArgs& p, const SmallLds<NB>
         const int pi = pc - cr * P;
         const bool real = cr < kSNb * 16 && pi < P - 1;
         const uint8_t* src = p.w_scales + weight_row(q, real ? cr : 0) * Ks + (real ? 16 * pi : 0);
-        dma16(src, base + 1024 * i);
+        if constexpr (kPacked) dma16nt(src, base + 1024 * i);  // read once, like the packed codes
+        else dma16(src, base + 1024 * i);
       }
     };
     auto loader_enter = [&]() {
