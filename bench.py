@@ -8,7 +8,9 @@ experts (hidden 7168, intermediate 2048, top-6).  Useful FLOPs are 6*H*I per (to
 expert) assignment.  The same JSON line carries the decode workload (the 48-expert
 expert-parallel share of 384 experts at T = 1, 4, 8, with 4 rotated weight copies so weights
 come from HBM, not from the 256 MB last-level cache), reported as weight GB/s, where weight
-bytes are the NVFP4 bytes of the experts that received at least one token.
+bytes are the NVFP4 bytes of the experts that received at least one token.  The weights carry the
+packed copy of their codes (MoEWeights.pack, nvfp4_pack_weight_codes), which the 16-row kernels read
+(``--unpacked``: the row-major codes only).
 
 ``roofline`` is for the dominant kernel.  Prefill: the L1 large-tile kernel
 (gemm_large_kernel<true, false>, experts with more than 16 tokens; 60% of the step), whose launch
@@ -38,6 +40,7 @@ two-per-CU launch, and the dense NVFP4 GEMM on random versus zero codes (the clo
 the operand data).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-seeds N] [--no-cpu-baseline] [--quick]
+       [--unpacked]
 """
 from __future__ import annotations
 
