@@ -879,7 +879,7 @@ def main():
         summarize_traffic(args.summarize_traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py runs on exactly one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 
